@@ -1,0 +1,239 @@
+"""ctypes wrapper of the CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg use it; the product library never does. Arrays are numpy;
+bf16 values travel as uint16 bit patterns.
+"""
+import ctypes as C
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+GATE, UP, DOWN = 0, 1, 2
+ACC_F64, ACC_F32 = 0, 1
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = C.CDLL(_build.LIB)
+        u8p, u16p, u32p = C.POINTER(C.c_uint8), C.POINTER(C.c_uint16), C.POINTER(C.c_uint32)
+        i32p, f32p, u64p = C.POINTER(C.c_int32), C.POINTER(C.c_float), C.POINTER(C.c_uint64)
+        L.orc_e2m1_value.restype = C.c_double
+        L.orc_e2m1_value.argtypes = [C.c_uint]
+        L.orc_e4m3_value.restype = C.c_double
+        L.orc_e4m3_value.argtypes = [C.c_uint]
+        L.orc_bf16_to_f32.restype = C.c_float
+        L.orc_bf16_to_f32.argtypes = [C.c_uint16]
+        L.orc_f64_to_bf16.restype = C.c_uint16
+        L.orc_f64_to_bf16.argtypes = [C.c_double]
+        L.orc_global_factor.restype = C.c_float
+        L.orc_global_factor.argtypes = [C.c_float]
+        L.orc_block_scale.restype = C.c_float
+        L.orc_block_scale.argtypes = [C.c_uint, C.c_float]
+        L.orc_weight.restype = C.c_float
+        L.orc_weight.argtypes = [C.c_uint, C.c_uint, C.c_float]
+        L.orc_record_layout.restype = C.c_int
+        L.orc_record_layout.argtypes = [C.c_int, C.c_int, u64p, u64p, u64p]
+        L.orc_pack_record.restype = None
+        L.orc_pack_record.argtypes = [C.c_int, C.c_int, C.POINTER(u32p), C.POINTER(u8p), f32p, u8p]
+        L.orc_dequant_projection.restype = None
+        L.orc_dequant_projection.argtypes = [u8p, C.c_int, C.c_int, C.c_int, f32p, u16p]
+        L.orc_router_logits.restype = None
+        L.orc_router_logits.argtypes = [u16p, f32p, C.c_int, C.c_int, C.c_int, f32p]
+        L.orc_route_topk.restype = C.c_int
+        L.orc_route_topk.argtypes = [f32p, C.c_int, C.c_int, C.c_int, i32p, f32p]
+        L.orc_sort_pairs.restype = C.c_int
+        L.orc_sort_pairs.argtypes = [i32p, C.c_int, C.c_int, i32p, i32p]
+        L.orc_moe_forward.restype = C.c_int
+        L.orc_moe_forward.argtypes = [C.POINTER(u8p), C.c_int, C.c_int, C.c_int, u16p, C.c_int,
+                                      i32p, f32p, C.c_int, u16p, C.c_int, f32p, u16p, u16p]
+        L.orc_q8_quantize.restype = C.c_int
+        L.orc_q8_quantize.argtypes = [u16p, C.c_int, C.c_int, u32p, u16p, u16p]
+        L.orc_affine8_linear.restype = C.c_int
+        L.orc_affine8_linear.argtypes = [u16p, u32p, u16p, u16p, C.c_int, C.c_int, C.c_int, f32p, u16p]
+        L.orc_rmsnorm.restype = None
+        L.orc_rmsnorm.argtypes = [u16p, C.c_int, C.c_int, C.c_double, u16p]
+        _lib = L
+    return _lib
+
+
+def _p(a, ct):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(C.POINTER(ct))
+
+
+# ---- number formats ------------------------------------------------------
+def e2m1_value(code):
+    return lib().orc_e2m1_value(int(code))
+
+
+def e4m3_value(byte):
+    return lib().orc_e4m3_value(int(byte))
+
+
+def global_factor(g):
+    return lib().orc_global_factor(float(g))
+
+
+def block_scale(s_byte, g):
+    return lib().orc_block_scale(int(s_byte), float(g))
+
+
+def weight(code, s_byte, g):
+    return lib().orc_weight(int(code), int(s_byte), float(g))
+
+
+def f64_to_bf16(values):
+    v = np.asarray(values, dtype=np.float64).ravel()
+    f = lib().orc_f64_to_bf16
+    return np.array([f(float(a)) for a in v], dtype=np.uint16).reshape(np.shape(values))
+
+
+def bf16_to_f32(bits):
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+# ---- record --------------------------------------------------------------
+def record_layout(H, I):
+    off = (C.c_uint64 * 9)()
+    nb, st = C.c_uint64(), C.c_uint64()
+    rc = lib().orc_record_layout(H, I, off, C.byref(nb), C.byref(st))
+    if rc != 0:
+        raise ValueError("bad shape")
+    return [int(o) for o in off], int(nb.value), int(st.value)
+
+
+def pack_record(H, I, codes, scales, g):
+    """codes[p]: uint32 [out][in/8]; scales[p]: uint8 [out][in/16]; g: 3 floats."""
+    _, _, stride = record_layout(H, I)
+    codes = [np.ascontiguousarray(c, dtype=np.uint32) for c in codes]
+    scales = [np.ascontiguousarray(s, dtype=np.uint8) for s in scales]
+    cp = (C.POINTER(C.c_uint32) * 3)(*[_p(c, C.c_uint32) for c in codes])
+    sp = (C.POINTER(C.c_uint8) * 3)(*[_p(s, C.c_uint8) for s in scales])
+    gp = np.ascontiguousarray(g, dtype=np.float32)
+    out = np.empty(stride, dtype=np.uint8)
+    lib().orc_pack_record(H, I, cp, sp, _p(gp, C.c_float), _p(out, C.c_uint8))
+    return out
+
+
+def proj_shape(H, I, proj):
+    return (H, I) if proj == DOWN else (I, H)
+
+
+def dequant_projection(record, H, I, proj, want_unit=True):
+    rows, cols = proj_shape(H, I, proj)
+    rec = np.ascontiguousarray(record, dtype=np.uint8)
+    w = np.empty((rows, cols), dtype=np.float32)
+    u = np.empty((rows, cols), dtype=np.uint16) if want_unit else None
+    lib().orc_dequant_projection(_p(rec, C.c_uint8), H, I, proj, _p(w, C.c_float), _p(u, C.c_uint16))
+    return w, u
+
+
+# ---- routing -------------------------------------------------------------
+def router_logits(x_bf16, Wr):
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    W = np.ascontiguousarray(Wr, dtype=np.float32)
+    T, H = x.shape
+    E = W.shape[1]
+    out = np.empty((T, E), dtype=np.float32)
+    lib().orc_router_logits(_p(x, C.c_uint16), _p(W, C.c_float), T, H, E, _p(out, C.c_float))
+    return out
+
+
+def route_topk(logits, k):
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = lg.shape
+    idx = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float32)
+    rc = lib().orc_route_topk(_p(lg, C.c_float), T, E, k, _p(idx, C.c_int32), _p(w, C.c_float))
+    if rc != 0:
+        raise ValueError("route_topk: bad k or NaN logit")
+    return idx, w
+
+
+def sort_pairs(idx, E):
+    ix = np.ascontiguousarray(idx, dtype=np.int32).ravel()
+    P = ix.size
+    off = np.empty(E + 1, dtype=np.int32)
+    srt = np.empty(max(P, 1), dtype=np.int32)
+    rc = lib().orc_sort_pairs(_p(ix, C.c_int32), P, E, _p(off, C.c_int32), _p(srt, C.c_int32))
+    if rc != 0:
+        raise ValueError("sort_pairs: index out of range")
+    return off, srt[:P]
+
+
+# ---- the layer -----------------------------------------------------------
+def moe_forward(records, E, H, I, x_bf16, idx, w, residual=None, acc=ACC_F64, want_mid=False):
+    """records: dict or list mapping expert id -> uint8 record array (stride bytes)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    T = x.shape[0]
+    ix = np.ascontiguousarray(idx, dtype=np.int32)
+    wv = np.ascontiguousarray(w, dtype=np.float32)
+    k = ix.shape[1]
+    keep = []
+    ptrs = (C.POINTER(C.c_uint8) * E)()
+    items = records.items() if isinstance(records, dict) else enumerate(records)
+    for e, r in items:
+        if r is None:
+            continue
+        r = np.ascontiguousarray(r, dtype=np.uint8)
+        keep.append(r)
+        ptrs[int(e)] = _p(r, C.c_uint8)
+    res = None if residual is None else np.ascontiguousarray(residual, dtype=np.uint16)
+    yf = np.empty((T, H), dtype=np.float32)
+    yb = np.empty((T, H), dtype=np.uint16)
+    mid = np.empty((T * k, I), dtype=np.uint16) if want_mid else None
+    rc = lib().orc_moe_forward(ptrs, E, H, I, _p(x, C.c_uint16), T, _p(ix, C.c_int32),
+                               _p(wv, C.c_float), k, _p(res, C.c_uint16), acc,
+                               _p(yf, C.c_float), _p(yb, C.c_uint16), _p(mid, C.c_uint16))
+    if rc != 0:
+        raise ValueError("moe_forward: bad argument or missing record")
+    return (yf, yb, mid) if want_mid else (yf, yb)
+
+
+# ---- residents -----------------------------------------------------------
+def q8_quantize(v_bf16):
+    v = np.ascontiguousarray(v_bf16, dtype=np.uint16)
+    N, K = v.shape
+    codes = np.zeros((N, K // 4), dtype=np.uint32)
+    scales = np.empty((N, K // 64), dtype=np.uint16)
+    biases = np.empty((N, K // 64), dtype=np.uint16)
+    rc = lib().orc_q8_quantize(_p(v, C.c_uint16), N, K, _p(codes, C.c_uint32),
+                               _p(scales, C.c_uint16), _p(biases, C.c_uint16))
+    if rc != 0:
+        raise ValueError("q8_quantize: bad shape")
+    return codes, scales, biases
+
+
+def affine8_linear(x_bf16, codes, scales, biases):
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    T, K = x.shape
+    cd = np.ascontiguousarray(codes, dtype=np.uint32)
+    N = cd.shape[0]
+    sc = np.ascontiguousarray(scales, dtype=np.uint16)
+    bi = np.ascontiguousarray(biases, dtype=np.uint16)
+    yf = np.empty((T, N), dtype=np.float32)
+    yb = np.empty((T, N), dtype=np.uint16)
+    rc = lib().orc_affine8_linear(_p(x, C.c_uint16), _p(cd, C.c_uint32), _p(sc, C.c_uint16),
+                                  _p(bi, C.c_uint16), T, K, N, _p(yf, C.c_float), _p(yb, C.c_uint16))
+    if rc != 0:
+        raise ValueError("affine8_linear: bad shape")
+    return yf, yb
+
+
+def rmsnorm(x_bf16, eps=1e-6):
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    T, H = x.shape
+    y = np.empty_like(x)
+    lib().orc_rmsnorm(_p(x, C.c_uint16), T, H, float(eps), _p(y, C.c_uint16))
+    return y
