@@ -1,0 +1,262 @@
+"""Benchmark of the NVFP4 MoE layer on one MI355X.
+
+One step = the whole hot path on one batch: router logits + top-k (S1, S2),
+pair sort (S3), gate/up + SwiGLU (S4, S5), down (S6) and the weighted combine
+(S7), all through the C ABI, inputs resident in HBM.
+
+Headline (value): decode, T=1, H=5120, I=2560, 256 experts, top-8, as HBM
+GB/s of algorithmic bytes (the 8 selected records of 22,118,412 B + the f32
+router 5,242,880 B + x and y). Consecutive steps rotate over 64 different
+activations, so the routed records change every step and the 256 MB
+Infinity Cache cannot serve them.
+Second leg (prefill): T=8192 with Zipf(1.1)-skewed logits given, as TFLOP/s of
+2 * 65,536 * 3 * 5120 * 2560 flop.
+roofline: the dominant kernel of each leg, its algorithmic bytes (flop) per
+launch over its mean launch time from HIP events recorded around each launch
+on the stream it runs on.
+cpu_baseline: the CPU oracle (as is) on a bounded sample of the decode
+workload, on this host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--prefill-steps P]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+import weight_quantized_moe_amd as wq  # noqa: E402
+from synth import workloads as W  # noqa: E402
+
+METRIC = "NVFP4 MoE layer: decode HBM GB/s (T=1) + prefill TFLOP/s (T=8192), 1 GPU"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+ROTATE = 64
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+
+
+def kernel_avg_ms(name):
+    ms, n = wq.moe_profile_read(name)
+    return (ms / n if n else float("nan")), n
+
+
+class DecodeLeg:
+    def __init__(self, bank):
+        c = W.CONFIGS["decode"]
+        self.c, self.bank = c, bank
+        H, I, E, k, T = c["H"], c["I"], c["E"], c["k"], c["T"]
+        xs = [W.inputs("decode", v)[0] for v in range(ROTATE)]
+        _, Wr, _ = W.inputs("decode")
+        self.x = bf16_dev(np.stack(xs))  # [ROTATE][T][H]
+        self.Wr = torch.from_numpy(Wr).cuda()
+        self.logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+        self.idx = torch.empty((ROTATE, T, k), dtype=torch.int32, device="cuda")
+        self.w = torch.empty((ROTATE, T, k), dtype=torch.float32, device="cuda")
+        self.y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+        self.rws = wq.workspace(wq.moe_route_workspace_bytes(T, H, E))
+        self.ws = wq.workspace(wq.moe_nvfp4_workspace_bytes(T, k, H, I, E))
+        self.i = 0
+
+    def step(self):
+        c, r = self.c, self.i % ROTATE
+        self.i += 1
+        wq.moe_route_topk(self.x[r], self.Wr, self.logits, c["T"], c["H"], c["E"], c["k"], self.idx[r],
+                          self.w[r], self.rws)
+        wq.moe_nvfp4_forward(self.bank, self.x[r], c["T"], self.idx[r], self.w[r], c["k"], None, self.y, 0,
+                             self.ws)
+
+    def step_bytes(self, r):
+        """algorithmic HBM bytes of the step that used activation r"""
+        c = self.c
+        n_unique = len(np.unique(self.idx_host[r]))
+        rec = wq.moe_nvfp4_record_bytes(c["H"], c["I"])
+        return n_unique * rec + c["H"] * c["E"] * 4 + 2 * c["T"] * c["H"] * 2
+
+    def gateup_bytes(self, r):
+        c = self.c
+        n_unique = len(np.unique(self.idx_host[r]))
+        per_proj = c["H"] * c["I"] // 2 + c["H"] * c["I"] // 16
+        return n_unique * 2 * per_proj + c["T"] * c["H"] * 2 + len(self.idx_host[r].ravel()) * c["I"] * 2
+
+
+class PrefillLeg:
+    def __init__(self, bank):
+        c = W.CONFIGS["prefill"]
+        self.c, self.bank = c, bank
+        H, I, E, k, T = c["H"], c["I"], c["E"], c["k"], c["T"]
+        x, _, logits = W.inputs("prefill")
+        self.x = bf16_dev(x)
+        self.logits = torch.from_numpy(logits).cuda()
+        self.idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        self.w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        self.y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+        self.ws = wq.workspace(wq.moe_nvfp4_workspace_bytes(T, k, H, I, E))
+        self.flop = 2 * T * k * 3 * H * I
+
+    def step(self):
+        c = self.c
+        wq.moe_route_topk(None, None, self.logits, c["T"], c["H"], c["E"], c["k"], self.idx, self.w)
+        wq.moe_nvfp4_forward(self.bank, self.x, c["T"], self.idx, self.w, c["k"], None, self.y, 0, self.ws)
+
+
+def timed(fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1), (time.perf_counter() - t0) * 1e3
+
+
+def cpu_baseline(c, budget_s=20.0):
+    """The oracle, as it stands, on decode steps (router + top-k + layer), on
+    this host; as many steps as fit the time budget (at least one, at most 8)."""
+    import oracle
+
+    H, I, E, k = c["H"], c["I"], c["E"], c["k"]
+    _, Wr, _ = W.inputs("decode")
+    t_total, n, nbytes = 0.0, 0, 0
+    cache = {}
+    while n == 0 or t_total < budget_s:
+        x, _, _ = W.inputs("decode", n % ROTATE)
+        idx_probe, _ = oracle.route_topk(oracle.router_logits(x, Wr), k)
+        recs = {}
+        for e in np.unique(idx_probe):
+            if int(e) not in cache:
+                cc, ss, gg = W.host_parts(c["bank_seed"], int(e), H, I)
+                cache[int(e)] = oracle.pack_record(H, I, cc, ss, gg)
+            recs[int(e)] = cache[int(e)]
+        t0 = time.perf_counter()
+        lg = oracle.router_logits(x, Wr)
+        idx, w = oracle.route_topk(lg, k)
+        oracle.moe_forward(recs, E, H, I, x, idx, w)
+        t_total += time.perf_counter() - t0
+        nbytes += len(np.unique(idx)) * wq.moe_nvfp4_record_bytes(H, I) + H * E * 4 + 2 * H * 2
+        n += 1
+        if n >= 8:
+            break
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} decode steps (T=1, router + top-8 + layer), {t_total:.1f} s, f64-accumulating C oracle"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the layer runs on one MI355X; --gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wq.lib()
+    torch.cuda.set_device(0)
+    c = W.CONFIGS["decode"]
+    log(f"building the bank: {c['E']} records of {wq.moe_nvfp4_record_bytes(c['H'], c['I'])} B")
+    t0 = time.time()
+    bank, base = W.build_bank(c["bank_seed"], c["H"], c["I"], c["E"])
+    log(f"bank ready in {time.time() - t0:.1f} s")
+
+    # ---- decode leg
+    dec = DecodeLeg(bank)
+    K, Wm = args.steps, args.warmup
+    ms_total, wall_ms = timed(dec.step, K, Wm)
+    dec.idx_host = dec.idx.cpu().numpy()
+    first = (Wm) % ROTATE
+    rs = [(first + i) % ROTATE for i in range(K)]
+    step_bytes = np.array([dec.step_bytes(r) for r in rs], dtype=np.float64)
+    ms_per_step = ms_total / K
+    value = step_bytes.sum() / (ms_total * 1e-3) / 1e9
+    log(f"decode: {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s (wall {wall_ms / K * 1e3:.1f} us/step)")
+
+    # per-kernel times from events around each launch (a separate pass: the
+    # events add a little launch overhead)
+    wq.moe_profile_enable(True)
+    dec.i = Wm
+    for _ in range(K):
+        dec.step()
+    torch.cuda.synchronize()
+    kern = {}
+    for name in ["router", "topk", "sort", "decode_gateup", "decode_down", "combine"]:
+        kern[name] = kernel_avg_ms(name)
+    wq.moe_profile_enable(False)
+    for n_, (avg, cnt) in kern.items():
+        log(f"  {n_:15s} {avg * 1e3:8.2f} us x {cnt}")
+    gu_bytes = np.mean([dec.gateup_bytes(r) for r in rs])
+    gu_ms = kern["decode_gateup"][0]
+    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    roofline = {"kernel": "decode_gateup", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(gu_ms * 1e3, 2)}
+
+    out = {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": Wm,
+           "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "decode: one NVFP4 MoE layer, T=1, H=5120, I=2560, 256 experts, top-8, "
+                                  "router f32 5120x256; 64 rotating activations",
+                      "global_batch": 1, "H": 5120, "I": 2560, "E": 256, "top_k": 8,
+                      "bytes_per_step": int(step_bytes.mean())},
+           "roofline": roofline,
+           "kernels_us": {n_: round(v[0] * 1e3, 2) for n_, v in kern.items()}}
+
+    # ---- prefill leg
+    if not args.no_prefill:
+        del dec
+        torch.cuda.empty_cache()
+        pre = PrefillLeg(bank)
+        P = args.prefill_steps
+        pms, _ = timed(pre.step, P, 2)
+        tflops = pre.flop / (pms / P * 1e-3) / 1e12
+        wq.moe_profile_enable(True)
+        for _ in range(P):
+            pre.step()
+        torch.cuda.synchronize()
+        pk = {n_: kernel_avg_ms(n_) for n_ in ["topk", "sort", "prefill_gateup", "prefill_down", "combine"]}
+        wq.moe_profile_enable(False)
+        for n_, (avg, cnt) in pk.items():
+            log(f"  {n_:15s} {avg * 1e3:8.2f} us x {cnt}")
+        gu_flop = 2 * pre.c["T"] * pre.c["k"] * 2 * pre.c["H"] * pre.c["I"]
+        gu_tf = gu_flop / (pk["prefill_gateup"][0] * 1e-3) / 1e12
+        out["prefill"] = {"value": round(tflops, 2), "unit": "TFLOP/s", "steps": P, "ms_per_step": round(pms / P, 4),
+                          "workload": "prefill: T=8192, top-8 of 256 on Zipf(1.1)-skewed logits (given), "
+                                      "65,536 pairs, 5.154 TFLOP per step",
+                          "roofline": {"kernel": "prefill_gateup", "bound": "mfma", "achieved": round(gu_tf, 2),
+                                       "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": round(gu_tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                                       "flop_per_launch": gu_flop,
+                                       "avg_launch_ms": round(pk["prefill_gateup"][0], 4)},
+                          "kernels_us": {n_: round(v[0] * 1e3, 2) for n_, v in pk.items()}}
+        log(f"prefill: {pms / P:.3f} ms/step, {tflops:.1f} TFLOP/s")
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(c)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+/*
+ * moe_mi355x.h -- C ABI of libmoe_mi355x.so: the routed-expert MoE layer over
+ * weight-only NVFP4 experts (BF16 activations) on AMD Instinct MI355X (gfx950).
+ *
+ * Sources, by page title and section:
+ *   [PACK] "Beam 1.0 501B-A23B, streaming pack, NVFP4 experts / MLX 8-bit
+ *          residents": "What this pack holds" (routed-experts, global-scales,
+ *          residents and q8-rule bullets) and the intro (49 routed layers of
+ *          256 experts, 8 active per token).
+ *   [VQ]   "Beam-1.0-501B-A23B VQ GGUF": "What stays native" (router logits and
+ *          SwiGLU in FP32) and "Kernel budget on GB10" (BF16 mids, 5,120 and
+ *          2,560 row widths).
+ *
+ * Conventions (every entry point):
+ *   - Returns MOE_OK (0) or a negative MOE_E* code; moe_last_error() then gives
+ *     a message (thread-local). No C++ exception crosses this boundary.
+ *   - Tensor pointers are caller-owned DEVICE memory unless stated otherwise;
+ *     the library keeps no pointer after a call returns.
+ *   - Arguments are validated before anything is enqueued: on an error return
+ *     nothing has been launched.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*, NULL = the
+ *     null stream) and the call returns without waiting. Launch failures are
+ *     reported as MOE_EHIP from hipGetLastError at enqueue time.
+ *   - bf16 values travel as uint16_t bit patterns; f32 is IEEE binary32.
+ *   - Results are deterministic: no floating-point atomics on any path.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_EINVAL (-1)     /* null pointer or value out of range */
+#define MOE_ESHAPE (-2)     /* a size breaks a shape rule */
+#define MOE_EALIGN (-3)     /* a pointer or offset is not aligned as required */
+#define MOE_EWORKSPACE (-4) /* workspace too small */
+#define MOE_EHIP (-5)       /* the HIP runtime reported an error */
+
+/* forward flags */
+#define MOE_F32_OUT 1u      /* y is f32 [T][H] instead of bf16 */
+#define MOE_FORCE_DECODE 2u /* always use the expert-streaming (GEMV) kernels */
+#define MOE_FORCE_PREFILL 4u /* always use the grouped-GEMM (MFMA) kernels */
+
+enum { MOE_GATE = 0, MOE_UP = 1, MOE_DOWN = 2 };
+
+/* Message for the last error on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* ---- the expert record, [PACK] routed-experts bullet ----------------------
+ * One record per expert: gate, up and down, each with E2M1 codes (U32 words,
+ * 8 codes per word, element 8q+j in bits 4j..4j+3 of word q), E4M3 block
+ * scales (one byte per 16 inputs) and an f32 global g. Gate and up are
+ * [I rows][H inputs], down is [H rows][I inputs], row-major. Default part
+ * order: gate.codes, gate.scales, up.codes, up.scales, down.codes,
+ * down.scales, g_gate, g_up, g_down; records start every `stride` bytes, the
+ * record size rounded up to 4 KiB. At H = 5120, I = 2560: 22,118,412 B per
+ * record at a 22,122,496 B stride. */
+size_t moe_nvfp4_record_bytes(int H, int I);  /* 3*(H*I/2 + H*I/16) + 12; 0 on bad shape */
+size_t moe_nvfp4_record_stride(int H, int I); /* record bytes rounded up to 4096 */
+
+typedef struct moe_nvfp4_bank {
+  int32_t H, I, E, reserved;
+  uint64_t record_bytes, stride;
+  /* part_off[2p] codes, part_off[2p+1] scales, part_off[6+p] global of
+   * projection p (gate, up, down), bytes from the record start */
+  uint64_t part_off[9];
+  void* base; /* device, E * stride bytes, 4096-byte aligned */
+} moe_nvfp4_bank;
+
+/* Fills *b for E records of shape (H, I) at `base` with the default layout.
+ * Shape rules: H, I positive multiples of 16, 1 <= E <= 1024.
+ * Errors: MOE_EINVAL (null b/base), MOE_ESHAPE, MOE_EALIGN (base not
+ * 4096-aligned). */
+int moe_nvfp4_bank_init(moe_nvfp4_bank* b, void* base, int H, int I, int E);
+
+/* S0, pack: copies the 9 parts of each of the b->E experts into their records
+ * and zeroes each record's tail pad. Per projection p:
+ *   codes[p]  U32 [E][out_p][in_p/8], scales[p] u8 [E][out_p][in_p/16],
+ *   g[p]      f32 [E],
+ * host or device memory (the runtime picks the copy direction). Host sources
+ * must stay valid until the stream reaches the copies. */
+int moe_pack_nvfp4_bank(const moe_nvfp4_bank* b, const uint32_t* const codes[3],
+                        const uint8_t* const scales[3], const float* const g[3], void* stream);
+
+/* S1 + S2, routing ([PACK] intro: 8 of 256 experts per token; [VQ] "What
+ * stays native": FP32 router logits).
+ *   If x and w_router are both non-null: logits[t][e] = sum_h x[t][h]*Wr[h][e]
+ *   (f32 accumulation, partial sums over 64-row chunks of H added in chunk
+ *   order) is computed into `logits` first; the chunk sums need `workspace`
+ *   (device, 256-byte aligned, >= moe_route_workspace_bytes(T, H, E) bytes).
+ *   Otherwise `logits` is the input and workspace may be NULL. Then per token:
+ *   the k largest logits (ties: lower expert index; -0 == +0; a NaN ranks
+ *   below every number), idx i32 [T][k] in descending order, and w f32 [T][k]
+ *   = softmax over the k selected logits (f32, summed in slot order).
+ *   x bf16 [T][H]; w_router f32 [H][E]; logits f32 [T][E].
+ *   Rules: T >= 0, 1 <= k <= min(E, 64), 1 <= E <= 1024, H % 16 == 0. */
+size_t moe_route_workspace_bytes(int T, int H, int E);
+int moe_route_topk(const uint16_t* x, const float* w_router, float* logits, int T, int H,
+                   int E, int k, int32_t* idx, float* w, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* S3, token -> expert counting sort of the P = T*k pairs (pair p = t*k + j):
+ * offsets i32 [E+1] (offsets[e] = first sorted slot of expert e, offsets[E] = P)
+ * and sorted i32 [P] (pair ids, ascending within one expert: a stable sort).
+ * idx values outside [0, E) are a caller error; they are dropped and
+ * offsets[E] then counts only the valid pairs. */
+int moe_sort_pairs(const int32_t* idx, int T, int k, int E, int32_t* offsets, int32_t* sorted,
+                   void* stream);
+
+/* S3..S7, the layer (shape rules: H and I multiples of 64, T >= 0,
+ * 1 <= k <= min(E, 64)):
+ *   y[t] = residual[t] + sum_j w[t][j] * down_e( bf16( silu(gate_e x[t]) * up_e x[t] ) )
+ * with e = idx[t][j], each projection dequantized by the [PACK] global-scales
+ * rule (weight = e2m1 * f32(e4m3 * f32(g / 2688))), f32 accumulation, FP32
+ * SwiGLU and BF16 mids ([VQ]). x, residual (nullable): bf16 [T][H]; idx i32
+ * [T][k]; w f32 [T][k]; y bf16 [T][H], or f32 with MOE_F32_OUT.
+ * Expert-streaming (GEMV) kernels are used for small T*k, grouped-GEMM (bf16
+ * MFMA) kernels for large T*k; flags can force either.
+ * workspace: device, >= moe_nvfp4_workspace_bytes(T, k, H, I, E) bytes,
+ * 256-byte aligned, not shared with a concurrent call. idx values outside
+ * [0, E) are a caller error (those pairs contribute nothing). */
+size_t moe_nvfp4_workspace_bytes(int T, int k, int H, int I, int E);
+int moe_nvfp4_forward(const moe_nvfp4_bank* b, const uint16_t* x, int T, const int32_t* idx,
+                      const float* w, int k, const uint16_t* residual, void* y, unsigned flags,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* S8, resident linear in MLX affine 8-bit, group 64 ([PACK] residents and
+ * q8-rule bullets): y[t][n] = sum_k x[t][k] * (scale[n][k/64]*q[n][k] +
+ * bias[n][k/64]), f32 accumulation, bf16 out.
+ * x bf16 [T][K]; codes U32 [N][K/4] (4 codes per word, first in the low
+ * byte); scales, biases bf16 [N][K/64]; y bf16 [T][N].
+ * Rules: K % 64 == 0, N >= 1, T >= 0; codes 16-byte aligned. */
+int affine8_g64_linear(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
+                       const uint16_t* biases, int T, int K, int N, uint16_t* y, void* stream);
+
+/* S9, weightless RMS norm used between stacked layers:
+ * y = bf16( x / sqrt(mean(x^2) + eps) ), f32 math. x, y bf16 [T][H]. */
+int moe_rmsnorm(const uint16_t* x, int T, int H, float eps, uint16_t* y, void* stream);
+
+/* Test export of the dequant rule ([PACK] global-scales bullet) for one
+ * projection of one record: out_f32 [out][in] (nullable) = e2m1 * f32(e4m3 *
+ * f32(g/2688)); out_unit (nullable) bf16 [out][in] = e2m1 * e4m3, exact. */
+int moe_nvfp4_dequant(const moe_nvfp4_bank* b, int expert, int proj, float* out_f32,
+                      uint16_t* out_unit, void* stream);
+
+/* Kernel timing with HIP events recorded around each launch on its stream.
+ * moe_profile_enable(1) clears and starts collection (it adds a little launch
+ * overhead); moe_profile_read(name, ...) synchronizes the recorded events and
+ * returns the summed duration and count of the kernel family `name` since the
+ * last enable. Names: "router", "topk", "sort", "decode_gateup", "decode_down",
+ * "combine", "prefill_gateup", "prefill_down", "affine8", "rmsnorm". */
+int moe_profile_enable(int on);
+int moe_profile_read(const char* name, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -127,10 +127,12 @@ def zipf_ranks(seed, E, s=1.1):
     return rank.astype(np.float64) ** (-s)
 
 
-def skewed_logits(seed, T, E, s=1.1):
-    """f32 router logits N(0,1) + Zipf-rank bias [T][E]"""
+def skewed_logits(seed, T, E, s=1.1, rank_seed=None):
+    """f32 router logits N(0,1) + Zipf-rank bias [T][E]; the expert ranks come
+    from rank_seed (default: seed), the noise from seed"""
     z = normal_np(seed, S_LOGIT, T * E).reshape(T, E)
-    return (z + zipf_ranks(seed, E, s)[None, :]).astype(np.float32)
+    r = zipf_ranks(seed if rank_seed is None else rank_seed, E, s)
+    return (z + r[None, :]).astype(np.float32)
 
 
 def global_scales(seed, n_records):

@@ -1,0 +1,369 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Every oracle input comes from the seeded generators or from the oracle itself
+(never from the HIP path). Comparison classes:
+  bit-exact:  pack bytes, dequantized f32 weights and bf16 unit values, top-k
+              indices on identical logits, the pair sort;
+  bounded:    router logits (f32 sums in another order: 1e-5 rms), softmax
+              weights (f32 evaluation, bound derived in check_weights), bf16
+              outputs (one bf16 ulp + 1e-4 rms, see check_bf16);
+  tolerance:  f32 layer outputs, relative L2 <= 5e-3 and per-element
+              |err| <= 1e-2 * rms(reference).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import workloads as W
+
+wq = pytest.importorskip("weight_quantized_moe_amd")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def bf16_tensor(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV)
+
+
+def to_np_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check_f32(got, ref, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref**2))
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    mx = np.max(np.abs(got - ref)) / rms
+    say(f"{what}: rel L2 {rel:.3e}, max |err|/rms {mx:.3e}")
+    assert rel <= 5e-3 and mx <= 1e-2, (what, rel, mx)
+
+
+def check_bf16(got_bits, ref_f32, what):
+    """A bf16 output is the device's f32 value rounded once (half a bf16 ulp);
+    the f32 value itself carries the f32 path's absolute error, which near a
+    cancellation exceeds the bf16 ulp of the tiny result. Bound: one bf16 ulp of
+    |ref| plus 1e-4 * rms(ref), a hundredth of the per-element layer bound."""
+    got = oracle.bf16_to_f32(got_bits).astype(np.float64)
+    ref = np.asarray(ref_f32, np.float64)
+    a = np.maximum(np.abs(ref), 2.0**-126)
+    ulp = 2.0 ** (np.floor(np.log2(a)) - 7)
+    rms = np.sqrt(np.mean(ref**2))
+    err = np.abs(got - ref)
+    bad = err > ulp + 1e-4 * rms
+    say(f"{what}: max |err| - ulp = {np.max(err - ulp) / rms:.2e} rms")
+    assert not bad.any(), (what, int(bad.sum()), got[bad][:5], ref[bad][:5])
+
+
+def host_records(seed, experts, H, I):
+    recs = {}
+    for e in experts:
+        c, s, g = W.host_parts(seed, int(e), H, I)
+        recs[int(e)] = oracle.pack_record(H, I, c, s, g)
+    return recs
+
+
+def oracle_routing(name, x, Wr, logits, k):
+    if logits is None:
+        logits = oracle.router_logits(x, Wr)
+    idx, w = oracle.route_topk(logits, k)
+    return logits, idx, w
+
+
+def gpu_forward(bank, x_bits, idx, w, k, flags=0, residual=None):
+    T, H = x_bits.shape
+    ws = wq.workspace(wq.moe_nvfp4_workspace_bytes(T, k, bank.H, bank.I, bank.E))
+    xd = bf16_tensor(x_bits)
+    idd = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).to(DEV)
+    wd = torch.from_numpy(np.ascontiguousarray(w, np.float32)).to(DEV)
+    rd = None if residual is None else bf16_tensor(residual)
+    yf = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    yb = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    wq.moe_nvfp4_forward(bank, xd, T, idd, wd, k, rd, yf, flags | wq.MOE_F32_OUT, ws)
+    wq.moe_nvfp4_forward(bank, xd, T, idd, wd, k, rd, yb, flags, ws)
+    torch.cuda.synchronize()
+    return yf.cpu().numpy(), to_np_bits(yb)
+
+
+# ---- banks ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def tiny_bank():
+    c = W.CONFIGS["tiny"]
+    say("building tiny bank")
+    return W.build_bank(c["bank_seed"], c["H"], c["I"], c["E"])
+
+
+@pytest.fixture(scope="module")
+def big_bank():
+    c = W.CONFIGS["decode"]
+    say("building the 256-record bank (5.66 GB)")
+    return W.build_bank(c["bank_seed"], c["H"], c["I"], c["E"])
+
+
+# ---- S0 pack and the dequant rule --------------------------------------------------
+def test_pack_bytes_match_oracle_tiny(tiny_bank):
+    bank, base = tiny_bank
+    c = W.CONFIGS["tiny"]
+    recs = host_records(c["bank_seed"], range(c["E"]), c["H"], c["I"])
+    dev = base.cpu().numpy()
+    for e in range(c["E"]):
+        assert np.array_equal(dev[e * bank.stride:(e + 1) * bank.stride], recs[e]), e
+
+
+def test_pack_bytes_match_oracle_sampled_full_shape(big_bank):
+    bank, base = big_bank
+    c = W.CONFIGS["decode"]
+    for e in [0, 1, 97, 255]:
+        rec = host_records(c["bank_seed"], [e], c["H"], c["I"])[e]
+        dev = base[e * bank.stride:(e + 1) * bank.stride].cpu().numpy()
+        assert np.array_equal(dev, rec), e
+
+
+@pytest.mark.parametrize("proj", [0, 1, 2])
+def test_dequant_bit_exact_tiny(tiny_bank, proj):
+    bank, base = tiny_bank
+    c = W.CONFIGS["tiny"]
+    rows, cols = (c["H"], c["I"]) if proj == 2 else (c["I"], c["H"])
+    recs = host_records(c["bank_seed"], range(c["E"]), c["H"], c["I"])
+    for e in range(c["E"]):
+        wf = torch.empty((rows, cols), dtype=torch.float32, device=DEV)
+        wu = torch.empty((rows, cols), dtype=torch.int16, device=DEV)
+        wq.moe_nvfp4_dequant(bank, e, proj, wf, wu)
+        torch.cuda.synchronize()
+        rw, ru = oracle.dequant_projection(recs[e], c["H"], c["I"], proj)
+        assert np.array_equal(wf.cpu().numpy().view(np.uint32), rw.view(np.uint32)), (e, proj)
+        assert np.array_equal(to_np_bits(wu), ru), (e, proj)
+
+
+def test_dequant_bit_exact_full_shape(big_bank):
+    bank, base = big_bank
+    c = W.CONFIGS["decode"]
+    for e, proj in [(3, 0), (128, 1), (254, 2)]:
+        rows, cols = (c["H"], c["I"]) if proj == 2 else (c["I"], c["H"])
+        rec = host_records(c["bank_seed"], [e], c["H"], c["I"])[e]
+        wf = torch.empty((rows, cols), dtype=torch.float32, device=DEV)
+        wu = torch.empty((rows, cols), dtype=torch.int16, device=DEV)
+        wq.moe_nvfp4_dequant(bank, e, proj, wf, wu)
+        torch.cuda.synchronize()
+        rw, ru = oracle.dequant_projection(rec, c["H"], c["I"], proj)
+        assert np.array_equal(wf.cpu().numpy().view(np.uint32), rw.view(np.uint32)), (e, proj)
+        assert np.array_equal(to_np_bits(wu), ru), (e, proj)
+
+
+# ---- S1 + S2 routing -----------------------------------------------------------------
+def gpu_route(x_bits, Wr, logits_in, E, k):
+    T, H = x_bits.shape
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    if logits_in is None:
+        lg = torch.empty((T, E), dtype=torch.float32, device=DEV)
+        ws = wq.workspace(wq.moe_route_workspace_bytes(T, H, E))
+        wq.moe_route_topk(bf16_tensor(x_bits), torch.from_numpy(Wr).to(DEV), lg, T, H, E, k, idx, w, ws)
+    else:
+        lg = torch.from_numpy(np.ascontiguousarray(logits_in)).to(DEV)
+        wq.moe_route_topk(None, None, lg, T, H, E, k, idx, w)
+    torch.cuda.synchronize()
+    return lg.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+
+
+def check_weights(w_gpu, w_ref, logits_sel):
+    """Softmax weights: the device evaluates w_j = expf(l_j - l_0) / sum in f32.
+    With unit roundoff u = 2^-24: the difference costs |l_j - l_0| u, expf
+    about 2u, the k-term sum (k - 1)u, the division u, relative to w_j. The
+    bound doubles that: (|l_j - l_0| + k + 3) * 2u * w_j."""
+    k = w_ref.shape[1]
+    d = np.abs(logits_sel.astype(np.float64) - logits_sel[:, :1].astype(np.float64))
+    tol = (d + k + 3) * 2.0**-23 * np.abs(w_ref.astype(np.float64))
+    err = np.abs(w_gpu.astype(np.float64) - w_ref.astype(np.float64))
+    assert np.all(err <= tol), float(np.max(err / np.maximum(tol, 1e-300)))
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "stacked"])
+def test_router_logits_and_topk(name):
+    c = W.CONFIGS[name]
+    for variant in range(3):
+        x, Wr, _ = W.inputs(name, variant)
+        ref_lg = oracle.router_logits(x, Wr)
+        lg, _, _ = gpu_route(x, Wr, None, c["E"], c["k"])
+        rms = np.sqrt(np.mean(ref_lg.astype(np.float64) ** 2))
+        assert np.max(np.abs(lg - ref_lg)) <= 1e-5 * rms, name
+        # top-k on identical logits (the oracle's): bit-exact indices
+        _, idx, w = gpu_route(x, None, ref_lg, c["E"], c["k"])
+        ridx, rw = oracle.route_topk(ref_lg, c["k"])
+        assert np.array_equal(idx, ridx)
+        check_weights(w, rw, np.take_along_axis(ref_lg, ridx, axis=1))
+
+
+@pytest.mark.parametrize("name", ["batched", "prefill"])
+def test_topk_on_given_logits(name):
+    c = W.CONFIGS[name]
+    x, _, logits = W.inputs(name)
+    _, idx, w = gpu_route(x, None, logits, c["E"], c["k"])
+    ridx, rw = oracle.route_topk(logits, c["k"])
+    assert np.array_equal(idx, ridx)
+    check_weights(w, rw, np.take_along_axis(logits, ridx, axis=1))
+
+
+def test_topk_ties_zeros_and_k_edges():
+    rng = np.random.default_rng(0)
+    for E, k in [(256, 8), (1024, 64), (16, 16), (5, 1), (64, 3)]:
+        lg = rng.normal(size=(37, E)).astype(np.float32)
+        lg[0] = 0.0
+        lg[1, ::2] = -0.0
+        lg[2] = np.round(lg[2])
+        lg[3, :] = 7.0
+        x = np.zeros((37, 16), np.uint16)
+        _, idx, w = gpu_route(x, None, lg, E, k)
+        ridx, rw = oracle.route_topk(lg, k)
+        assert np.array_equal(idx, ridx), (E, k)
+        check_weights(w, rw, np.take_along_axis(lg, ridx, axis=1))
+
+
+# ---- S3 sort -------------------------------------------------------------------------
+@pytest.mark.parametrize("T,k,E", [(1, 8, 256), (32, 8, 256), (8192, 8, 256), (4, 2, 16), (3, 64, 1024), (1, 1, 1)])
+def test_sort_bit_exact(T, k, E):
+    rng = np.random.default_rng(T * 7 + k)
+    idx = rng.integers(0, E, (T, k)).astype(np.int32)
+    offs = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    srt = torch.empty(T * k, dtype=torch.int32, device=DEV)
+    wq.moe_sort_pairs(torch.from_numpy(idx).to(DEV), T, k, E, offs, srt)
+    torch.cuda.synchronize()
+    roff, rsrt = oracle.sort_pairs(idx, E)
+    assert np.array_equal(offs.cpu().numpy(), roff)
+    assert np.array_equal(srt.cpu().numpy(), rsrt)
+
+
+def test_sort_drops_invalid_indices():
+    idx = np.array([[3, -1], [7, 3], [16, 0]], np.int32)
+    offs = torch.empty(17, dtype=torch.int32, device=DEV)
+    srt = torch.full((6,), -5, dtype=torch.int32, device=DEV)
+    wq.moe_sort_pairs(torch.from_numpy(idx).to(DEV), 3, 2, 16, offs, srt)
+    torch.cuda.synchronize()
+    valid = idx.ravel()[(idx.ravel() >= 0) & (idx.ravel() < 16)]
+    roff, _ = oracle.sort_pairs(valid, 16)
+    assert np.array_equal(offs.cpu().numpy(), roff)
+    assert srt.cpu().numpy()[:4].tolist() == [5, 0, 3, 2]
+
+
+# ---- the layer -------------------------------------------------------------------------
+@pytest.mark.parametrize("flags", [0, 2, 4])  # auto, forced GEMV, forced grouped GEMM
+def test_forward_tiny(tiny_bank, flags):
+    bank, _ = tiny_bank
+    c = W.CONFIGS["tiny"]
+    recs = host_records(c["bank_seed"], range(c["E"]), c["H"], c["I"])
+    for variant in range(3):
+        x, Wr, _ = W.inputs("tiny", variant)
+        _, idx, w = oracle_routing("tiny", x, Wr, None, c["k"])
+        ref_f, _ = oracle.moe_forward(recs, c["E"], c["H"], c["I"], x, idx, w)
+        yf, yb = gpu_forward(bank, x, idx, w, c["k"], flags)
+        check_f32(yf, ref_f, f"tiny flags={flags} v{variant}")
+        check_bf16(yb, ref_f, "tiny bf16")
+
+
+def test_forward_tiny_ragged_and_residual(tiny_bank):
+    # T not a multiple of any tile, duplicated experts across tokens, an
+    # expert with many tokens (grouped-GEMM tail), a residual input
+    bank, _ = tiny_bank
+    c = W.CONFIGS["tiny"]
+    recs = host_records(c["bank_seed"], range(c["E"]), c["H"], c["I"])
+    T, k = 203, 2
+    x = synth.activations(77, T, c["H"])
+    res = synth.activations(78, T, c["H"])
+    lg = np.random.default_rng(5).normal(size=(T, c["E"])).astype(np.float32)
+    lg[:, 3] += 3.0  # expert 3 in nearly every token
+    idx, w = oracle.route_topk(lg, k)
+    ref_f, _ = oracle.moe_forward(recs, c["E"], c["H"], c["I"], x, idx, w, residual=res)
+    for flags in (2, 4):
+        yf, yb = gpu_forward(bank, x, idx, w, k, flags, residual=res)
+        check_f32(yf, ref_f, f"tiny ragged flags={flags}")
+        check_bf16(yb, ref_f, "tiny ragged bf16")
+
+
+def test_forward_decode_full_shape(big_bank):
+    bank, _ = big_bank
+    c = W.CONFIGS["decode"]
+    for variant in range(2):
+        x, Wr, _ = W.inputs("decode", variant)
+        _, idx, w = oracle_routing("decode", x, Wr, None, c["k"])
+        say(f"decode v{variant}: experts {idx.ravel().tolist()}")
+        recs = host_records(c["bank_seed"], np.unique(idx), c["H"], c["I"])
+        ref_f, _ = oracle.moe_forward(recs, c["E"], c["H"], c["I"], x, idx, w)
+        for flags in (0, 4):
+            yf, yb = gpu_forward(bank, x, idx, w, c["k"], flags)
+            check_f32(yf, ref_f, f"decode v{variant} flags={flags}")
+            check_bf16(yb, ref_f, "decode bf16")
+
+
+def test_forward_batched_full_shape_sampled(big_bank):
+    bank, _ = big_bank
+    c = W.CONFIGS["batched"]
+    x, _, logits = W.inputs("batched")
+    idx, w = oracle.route_topk(logits, c["k"])
+    yf, yb = gpu_forward(bank, x, idx, w, c["k"])
+    sample = [0, 13, 31]
+    recs = host_records(c["bank_seed"], np.unique(idx[sample]), c["H"], c["I"])
+    ref_f, _ = oracle.moe_forward(recs, c["E"], c["H"], c["I"], x[sample], idx[sample], w[sample])
+    check_f32(yf[sample], ref_f, "batched sampled")
+    check_bf16(yb[sample], ref_f, "batched bf16")
+
+
+def test_forward_prefill_full_shape_sampled(big_bank):
+    bank, _ = big_bank
+    c = W.CONFIGS["prefill"]
+    x, _, logits = W.inputs("prefill")
+    idx, w = oracle.route_topk(logits, c["k"])
+    say("prefill forward on the GPU")
+    yf, yb = gpu_forward(bank, x, idx, w, c["k"])
+    assert np.isfinite(yf).all()
+    # sampled tokens: the first, the last, and tokens routed to the largest and
+    # the smallest expert groups (tile tails)
+    counts = np.bincount(idx.ravel(), minlength=c["E"])
+    big_e, small_e = int(np.argmax(counts)), int(np.argmin(counts))
+    t_big = int(np.nonzero((idx == big_e).any(axis=1))[0][-1])
+    t_small = int(np.nonzero((idx == small_e).any(axis=1))[0][-1])
+    sample = sorted(set([0, c["T"] - 1, t_big, t_small]))
+    say(f"prefill sample tokens {sample}")
+    recs = host_records(c["bank_seed"], np.unique(idx[sample]), c["H"], c["I"])
+    ref_f, _ = oracle.moe_forward(recs, c["E"], c["H"], c["I"], x[sample], idx[sample], w[sample])
+    check_f32(yf[sample], ref_f, "prefill sampled")
+    check_bf16(yb[sample], ref_f, "prefill bf16")
+
+
+def test_forward_deterministic(big_bank):
+    bank, _ = big_bank
+    c = W.CONFIGS["batched"]
+    x, _, logits = W.inputs("batched", 1)
+    idx, w = oracle.route_topk(logits, c["k"])
+    a, _ = gpu_forward(bank, x, idx, w, c["k"], 2)
+    b, _ = gpu_forward(bank, x, idx, w, c["k"], 2)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    p, _ = gpu_forward(bank, x, idx, w, c["k"], 4)
+    q, _ = gpu_forward(bank, x, idx, w, c["k"], 4)
+    assert np.array_equal(p.view(np.uint32), q.view(np.uint32))
+
+
+# ---- S8 / S9 -------------------------------------------------------------------------------
+def test_affine8_and_rmsnorm():
+    for T, K, N in [(8, 5120, 5120), (3, 256, 192), (1, 64, 64), (13, 512, 100)]:
+        v = synth.resident_weights(11, N, K)
+        codes, scales, biases = oracle.q8_quantize(v)
+        x = synth.activations(12, T, K)
+        ref_f, ref_b = oracle.affine8_linear(x, codes, scales, biases)
+        y = torch.empty((T, N), dtype=torch.int16, device=DEV)
+        wq.affine8_g64_linear(bf16_tensor(x), torch.from_numpy(codes.view(np.int32)).to(DEV),
+                              bf16_tensor(scales), bf16_tensor(biases), T, K, N, y)
+        torch.cuda.synchronize()
+        check_bf16(to_np_bits(y), ref_f, f"affine8 {T}x{K}x{N}")
+    x = synth.activations(13, 8, 5120)
+    y = torch.empty((8, 5120), dtype=torch.int16, device=DEV)
+    wq.moe_rmsnorm(bf16_tensor(x), 8, 5120, 1e-6, y)
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm(x, 1e-6)
+    check_bf16(to_np_bits(y), oracle.bf16_to_f32(ref), "rmsnorm")

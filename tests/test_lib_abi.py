@@ -1,0 +1,121 @@
+"""The C-ABI library loads, exports every function include/moe_mi355x.h
+declares, and rejects bad arguments before it touches a GPU (these calls run
+on a machine without one)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import oracle
+import weight_quantized_moe_amd as wq
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe_mi355x.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z][a-z0-9_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 15, names
+    assert sorted(names) == sorted(wq.EXPORTS)
+    L = C.CDLL(wq.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_record_sizes_match_oracle():
+    for H, I in [(5120, 2560), (256, 128), (64, 64), (16, 32)]:
+        _, nbytes, stride = oracle.record_layout(H, I)
+        assert wq.moe_nvfp4_record_bytes(H, I) == nbytes
+        assert wq.moe_nvfp4_record_stride(H, I) == stride
+    assert wq.moe_nvfp4_record_bytes(24, 16) == 0
+
+
+def test_bank_init_layout_and_errors():
+    L = wq.lib()
+    b = wq.moe_nvfp4_bank()
+    assert L.moe_nvfp4_bank_init(C.byref(b), C.c_void_p(1 << 20), 5120, 2560, 256) == wq.MOE_OK
+    off, nbytes, stride = oracle.record_layout(5120, 2560)
+    assert list(b.part_off) == off and b.record_bytes == nbytes and b.stride == stride
+    assert L.moe_nvfp4_bank_init(C.byref(b), C.c_void_p((1 << 20) + 256), 5120, 2560, 256) == wq.MOE_EALIGN
+    assert L.moe_nvfp4_bank_init(C.byref(b), C.c_void_p(1 << 20), 5120, 2568, 256) == wq.MOE_ESHAPE
+    assert L.moe_nvfp4_bank_init(C.byref(b), C.c_void_p(1 << 20), 5120, 2560, 0) == wq.MOE_ESHAPE
+    assert L.moe_nvfp4_bank_init(C.byref(b), None, 5120, 2560, 16) == wq.MOE_EINVAL
+    assert b"bank_init" in L.moe_last_error()
+
+
+def _bank(H=256, I=128, E=16):
+    b = wq.moe_nvfp4_bank()
+    assert wq.lib().moe_nvfp4_bank_init(C.byref(b), C.c_void_p(1 << 24), H, I, E) == 0
+    return b
+
+
+def test_forward_validation_before_launch():
+    L = wq.lib()
+    b = _bank()
+    fake = C.c_void_p(1 << 26)
+    ws_need = L.moe_nvfp4_workspace_bytes(4, 2, 256, 128, 16)
+    assert ws_need > 0
+    args = lambda **kw: dict(dict(x=fake, T=4, idx=fake, w=fake, k=2, res=None, y=fake, flags=0, ws=fake,
+                                  wsb=ws_need), **kw)
+
+    def call(a, bank=b):
+        return L.moe_nvfp4_forward(C.byref(bank), a["x"], a["T"], a["idx"], a["w"], a["k"], a["res"], a["y"],
+                                   a["flags"], a["ws"], a["wsb"], None)
+
+    assert call(args(k=0)) == wq.MOE_ESHAPE
+    assert call(args(k=17)) == wq.MOE_ESHAPE
+    assert call(args(T=-1)) == wq.MOE_ESHAPE
+    assert call(args(x=None)) == wq.MOE_EINVAL
+    assert call(args(wsb=ws_need - 1)) == wq.MOE_EWORKSPACE
+    assert call(args(ws=C.c_void_p((1 << 26) + 16))) == wq.MOE_EALIGN
+    assert call(args(x=C.c_void_p((1 << 26) + 2))) == wq.MOE_EALIGN
+    assert call(args(flags=wq.MOE_FORCE_DECODE | wq.MOE_FORCE_PREFILL)) == wq.MOE_EINVAL
+    assert call(args(flags=64)) == wq.MOE_EINVAL
+    assert call(args(T=0)) == wq.MOE_OK  # nothing to do, nothing launched
+    bad = _bank(H=256, I=96)  # I not a multiple of 64
+    assert call(args(), bank=bad) == wq.MOE_ESHAPE
+    broken = _bank()
+    broken.part_off[2] += 4  # up.codes no longer 16-byte aligned
+    assert call(args(), bank=broken) == wq.MOE_EALIGN
+    broken = _bank()
+    broken.stride = 4096
+    assert call(args(), bank=broken) == wq.MOE_EINVAL
+
+
+def test_route_sort_affine_rmsnorm_validation():
+    L = wq.lib()
+    fake = C.c_void_p(1 << 26)
+    assert L.moe_route_topk(None, None, fake, 4, 256, 16, 0, fake, fake, None, 0, None) == wq.MOE_ESHAPE
+    assert L.moe_route_topk(None, None, fake, 4, 256, 16, 17, fake, fake, None, 0, None) == wq.MOE_ESHAPE
+    assert L.moe_route_topk(None, None, fake, 4, 256, 2048, 8, fake, fake, None, 0, None) == wq.MOE_ESHAPE
+    assert L.moe_route_topk(fake, None, fake, 4, 256, 16, 2, fake, fake, None, 0, None) == wq.MOE_EINVAL
+    need = L.moe_route_workspace_bytes(4, 256, 16)
+    assert L.moe_route_topk(fake, fake, fake, 4, 256, 16, 2, fake, fake, fake, need - 1, None) == wq.MOE_EWORKSPACE
+    assert L.moe_route_topk(fake, fake, fake, 4, 250, 16, 2, fake, fake, fake, need, None) == wq.MOE_ESHAPE
+    assert L.moe_route_topk(None, None, fake, 0, 256, 16, 2, fake, fake, None, 0, None) == wq.MOE_OK
+    assert L.moe_sort_pairs(fake, 4, 0, 16, fake, fake, None) == wq.MOE_ESHAPE
+    assert L.moe_sort_pairs(None, 4, 2, 16, fake, fake, None) == wq.MOE_EINVAL
+    assert L.affine8_g64_linear(fake, fake, fake, fake, 2, 100, 64, fake, None) == wq.MOE_ESHAPE
+    assert L.affine8_g64_linear(fake, C.c_void_p((1 << 26) + 4), fake, fake, 2, 128, 64, fake, None) == wq.MOE_EALIGN
+    assert L.moe_rmsnorm(fake, 2, 0, C.c_float(1e-6), fake, None) == wq.MOE_ESHAPE
+    assert L.moe_rmsnorm(fake, 2, 16, C.c_float(-1.0), fake, None) == wq.MOE_EINVAL
+    b = _bank()
+    assert L.moe_nvfp4_dequant(C.byref(b), 16, 0, fake, None, None) == wq.MOE_EINVAL
+    assert L.moe_nvfp4_dequant(C.byref(b), 0, 3, fake, None, None) == wq.MOE_EINVAL
+    assert L.moe_nvfp4_dequant(C.byref(b), 0, 0, None, None, None) == wq.MOE_EINVAL
+
+
+def test_workspace_sizes_grow_with_pairs():
+    L = wq.lib()
+    a = L.moe_nvfp4_workspace_bytes(1, 8, 5120, 2560, 256)
+    b = L.moe_nvfp4_workspace_bytes(8192, 8, 5120, 2560, 256)
+    assert 0 < a < b
+    # mids (bf16) and per-pair f32 rows dominate: P*(2I + 4H) bytes
+    assert b >= 65536 * (2 * 2560 + 4 * 5120)

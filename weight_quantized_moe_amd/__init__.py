@@ -1,0 +1,194 @@
+"""Python binding of libmoe_mi355x.so (see include/moe_mi355x.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. PyTorch supplies device memory and the stream. The functions carry the
+C entry points' names and take torch tensors (bf16 as torch.bfloat16 or
+int16/uint16 bit patterns); outputs are caller-allocated unless a helper says
+otherwise. A missing or unloadable library raises at import-time use; there is
+no fallback path.
+"""
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4, -5
+MOE_F32_OUT, MOE_FORCE_DECODE, MOE_FORCE_PREFILL = 1, 2, 4
+GATE, UP, DOWN = 0, 1, 2
+
+EXPORTS = [
+    "moe_last_error", "moe_nvfp4_record_bytes", "moe_nvfp4_record_stride", "moe_nvfp4_bank_init",
+    "moe_pack_nvfp4_bank", "moe_route_workspace_bytes", "moe_route_topk", "moe_sort_pairs",
+    "moe_nvfp4_workspace_bytes", "moe_nvfp4_forward", "affine8_g64_linear", "moe_rmsnorm",
+    "moe_nvfp4_dequant", "moe_profile_enable", "moe_profile_read",
+]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class moe_nvfp4_bank(C.Structure):
+    _fields_ = [("H", C.c_int32), ("I", C.c_int32), ("E", C.c_int32), ("reserved", C.c_int32),
+                ("record_bytes", C.c_uint64), ("stride", C.c_uint64),
+                ("part_off", C.c_uint64 * 9), ("base", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MoeError(MOE_EINVAL, f"{LIB_PATH} is not built (run __graft_entry__.build())")
+        L = C.CDLL(LIB_PATH)
+        vp, sz, i32 = C.c_void_p, C.c_size_t, C.c_int
+        bankp = C.POINTER(moe_nvfp4_bank)
+        L.moe_last_error.restype = C.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_nvfp4_record_bytes.restype = sz
+        L.moe_nvfp4_record_bytes.argtypes = [i32, i32]
+        L.moe_nvfp4_record_stride.restype = sz
+        L.moe_nvfp4_record_stride.argtypes = [i32, i32]
+        L.moe_nvfp4_bank_init.restype = i32
+        L.moe_nvfp4_bank_init.argtypes = [bankp, vp, i32, i32, i32]
+        L.moe_pack_nvfp4_bank.restype = i32
+        L.moe_pack_nvfp4_bank.argtypes = [bankp, C.POINTER(vp), C.POINTER(vp), C.POINTER(vp), vp]
+        L.moe_route_workspace_bytes.restype = sz
+        L.moe_route_workspace_bytes.argtypes = [i32, i32, i32]
+        L.moe_route_topk.restype = i32
+        L.moe_route_topk.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+        L.moe_sort_pairs.restype = i32
+        L.moe_sort_pairs.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+        L.moe_nvfp4_workspace_bytes.restype = sz
+        L.moe_nvfp4_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.moe_nvfp4_forward.restype = i32
+        L.moe_nvfp4_forward.argtypes = [bankp, vp, i32, vp, vp, i32, vp, vp, C.c_uint, vp, sz, vp]
+        L.affine8_g64_linear.restype = i32
+        L.affine8_g64_linear.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp]
+        L.moe_rmsnorm.restype = i32
+        L.moe_rmsnorm.argtypes = [vp, i32, i32, C.c_float, vp, vp]
+        L.moe_nvfp4_dequant.restype = i32
+        L.moe_nvfp4_dequant.argtypes = [bankp, i32, i32, vp, vp, vp]
+        L.moe_profile_enable.restype = i32
+        L.moe_profile_enable.argtypes = [i32]
+        L.moe_profile_read.restype = i32
+        L.moe_profile_read.argtypes = [C.c_char_p, C.POINTER(C.c_double), C.POINTER(C.c_int64)]
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != MOE_OK:
+        raise MoeError(rc, lib().moe_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+# ---- sizes and the bank ----------------------------------------------------------
+def moe_nvfp4_record_bytes(H, I):
+    return lib().moe_nvfp4_record_bytes(H, I)
+
+
+def moe_nvfp4_record_stride(H, I):
+    return lib().moe_nvfp4_record_stride(H, I)
+
+
+def moe_nvfp4_bank_init(base, H, I, E):
+    """Descriptor for E records at the device tensor `base` (uint8, E*stride bytes)."""
+    b = moe_nvfp4_bank()
+    _check(lib().moe_nvfp4_bank_init(C.byref(b), C.c_void_p(base.data_ptr()), H, I, E))
+    b._keep = base
+    return b
+
+
+def alloc_bank(H, I, E, device="cuda"):
+    """Allocates a 4 KiB-aligned bank of E records on `device` and its descriptor."""
+    stride = moe_nvfp4_record_stride(H, I)
+    raw = torch.empty(E * stride + 4096, dtype=torch.uint8, device=device)
+    off = (-raw.data_ptr()) % 4096
+    base = raw[off:off + E * stride]
+    b = moe_nvfp4_bank_init(base, H, I, E)
+    b._raw = raw
+    return b, base
+
+
+def moe_pack_nvfp4_bank(bank, codes, scales, g, stream=None):
+    """codes[p]: int32/uint32 [E][out][in/8]; scales[p]: uint8 [E][out][in/16]; g[p]: f32 [E]."""
+    for t in list(codes) + list(scales) + list(g):
+        assert t.is_contiguous()
+    cp = (C.c_void_p * 3)(*[t.data_ptr() for t in codes])
+    sp = (C.c_void_p * 3)(*[t.data_ptr() for t in scales])
+    gp = (C.c_void_p * 3)(*[t.data_ptr() for t in g])
+    _check(lib().moe_pack_nvfp4_bank(C.byref(bank), cp, sp, gp, _stream(stream)))
+
+
+# ---- routing ------------------------------------------------------------------------
+def moe_route_workspace_bytes(T, H, E):
+    return lib().moe_route_workspace_bytes(T, H, E)
+
+
+def moe_route_topk(x, w_router, logits, T, H, E, k, idx, w, workspace=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().moe_route_topk(_ptr(x), _ptr(w_router), _ptr(logits), T, H, E, k, _ptr(idx), _ptr(w),
+                                _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def moe_sort_pairs(idx, T, k, E, offsets, sorted_, stream=None):
+    _check(lib().moe_sort_pairs(_ptr(idx), T, k, E, _ptr(offsets), _ptr(sorted_), _stream(stream)))
+
+
+# ---- the layer ----------------------------------------------------------------------
+def moe_nvfp4_workspace_bytes(T, k, H, I, E):
+    return lib().moe_nvfp4_workspace_bytes(T, k, H, I, E)
+
+
+def moe_nvfp4_forward(bank, x, T, idx, w, k, residual, y, flags, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().moe_nvfp4_forward(C.byref(bank), _ptr(x), T, _ptr(idx), _ptr(w), k, _ptr(residual), _ptr(y),
+                                   flags, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def affine8_g64_linear(x, codes, scales, biases, T, K, N, y, stream=None):
+    _check(lib().affine8_g64_linear(_ptr(x), _ptr(codes), _ptr(scales), _ptr(biases), T, K, N, _ptr(y),
+                                    _stream(stream)))
+
+
+def moe_rmsnorm(x, T, H, eps, y, stream=None):
+    _check(lib().moe_rmsnorm(_ptr(x), T, H, float(eps), _ptr(y), _stream(stream)))
+
+
+def moe_nvfp4_dequant(bank, expert, proj, out_f32, out_unit, stream=None):
+    _check(lib().moe_nvfp4_dequant(C.byref(bank), expert, proj, _ptr(out_f32), _ptr(out_unit), _stream(stream)))
+
+
+def moe_profile_enable(on):
+    _check(lib().moe_profile_enable(1 if on else 0))
+
+
+def moe_profile_read(name):
+    ms, n = C.c_double(), C.c_int64()
+    _check(lib().moe_profile_read(name.encode(), C.byref(ms), C.byref(n)))
+    return ms.value, n.value
+
+
+def workspace(nbytes, device="cuda"):
+    """A 256-byte aligned device workspace of at least nbytes (torch allocations are)."""
+    t = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    assert t.data_ptr() % 256 == 0
+    return t

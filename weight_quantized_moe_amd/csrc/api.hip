@@ -1,0 +1,420 @@
+// C ABI of libmoe_mi355x.so: argument validation, workspace layout, dispatch
+// and kernel timing. Every check happens before the first enqueue, so an
+// error return means nothing was launched. See include/moe_mi355x.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/moe_mi355x.h"
+#include "internal.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t up256(size_t n) { return (n + 255) / 256 * 256; }
+
+// ---- kernel timing -------------------------------------------------------------
+struct ProfEntry {
+  hipEvent_t start, end;
+};
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::map<std::string, std::vector<ProfEntry>> done;
+  std::map<std::string, hipEvent_t> open;
+  void clear() {
+    for (auto& kv : done)
+      for (auto& pe : kv.second) {
+        hipEventDestroy(pe.start);
+        hipEventDestroy(pe.end);
+      }
+    done.clear();
+    for (auto& kv : open) hipEventDestroy(kv.second);
+    open.clear();
+  }
+};
+Profiler& prof() {
+  static Profiler p;
+  return p;
+}
+
+}  // namespace
+
+namespace moe {
+
+void prof_begin(const char* name, hipStream_t s) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> lk(p.mu);
+  if (!p.on) return;
+  hipEvent_t ev;
+  if (hipEventCreate(&ev) != hipSuccess) return;
+  hipEventRecord(ev, s);
+  p.open[name] = ev;
+}
+
+void prof_end(const char* name, hipStream_t s) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> lk(p.mu);
+  if (!p.on) return;
+  auto it = p.open.find(name);
+  if (it == p.open.end()) return;
+  hipEvent_t ev;
+  if (hipEventCreate(&ev) != hipSuccess) return;
+  hipEventRecord(ev, s);
+  p.done[name].push_back({it->second, ev});
+  p.open.erase(it);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+// ---- sizes and the bank descriptor ---------------------------------------------
+static bool record_shape_ok(int H, int I) { return H > 0 && I > 0 && H % 16 == 0 && I % 16 == 0; }
+
+MOE_API const char* moe_last_error(void) { return g_err; }
+
+MOE_API size_t moe_nvfp4_record_bytes(int H, int I) {
+  if (!record_shape_ok(H, I)) return 0;
+  const size_t n = (size_t)H * (size_t)I;
+  return 3 * (n / 2 + n / 16) + 12;
+}
+
+MOE_API size_t moe_nvfp4_record_stride(int H, int I) {
+  const size_t b = moe_nvfp4_record_bytes(H, I);
+  return (b + 4095) / 4096 * 4096;
+}
+
+MOE_API int moe_nvfp4_bank_init(moe_nvfp4_bank* b, void* base, int H, int I, int E) {
+  if (!b || !base) return fail(MOE_EINVAL, "bank_init: null pointer");
+  if (!record_shape_ok(H, I)) return fail(MOE_ESHAPE, "bank_init: H=%d I=%d must be positive multiples of 16", H, I);
+  if (E < 1 || E > 1024) return fail(MOE_ESHAPE, "bank_init: E=%d outside [1, 1024]", E);
+  if (!aligned(base, 4096)) return fail(MOE_EALIGN, "bank_init: base not 4096-byte aligned");
+  std::memset(b, 0, sizeof(*b));
+  b->H = H;
+  b->I = I;
+  b->E = E;
+  const uint64_t n = (uint64_t)H * (uint64_t)I;
+  uint64_t off = 0;
+  for (int p = 0; p < 3; p++) {
+    b->part_off[2 * p] = off;
+    off += n / 2;
+    b->part_off[2 * p + 1] = off;
+    off += n / 16;
+  }
+  for (int p = 0; p < 3; p++) {
+    b->part_off[6 + p] = off;
+    off += 4;
+  }
+  b->record_bytes = off;
+  b->stride = (off + 4095) / 4096 * 4096;
+  b->base = base;
+  return MOE_OK;
+}
+
+// Checks a descriptor and turns it into the kernels' view.
+static int bank_view(const moe_nvfp4_bank* b, BankView* v, const char* who) {
+  if (!b || !b->base) return fail(MOE_EINVAL, "%s: null bank", who);
+  if (!record_shape_ok(b->H, b->I) || b->E < 1 || b->E > 1024)
+    return fail(MOE_ESHAPE, "%s: bank shape H=%d I=%d E=%d", who, b->H, b->I, b->E);
+  if (b->stride < b->record_bytes || b->record_bytes != moe_nvfp4_record_bytes(b->H, b->I))
+    return fail(MOE_EINVAL, "%s: record size/stride inconsistent with H, I", who);
+  if (!aligned(b->base, 256) || b->stride % 256) return fail(MOE_EALIGN, "%s: base/stride alignment", who);
+  const uint64_t n = (uint64_t)b->H * (uint64_t)b->I;
+  for (int p = 0; p < 3; p++) {
+    if (b->part_off[2 * p] % 16 || b->part_off[2 * p + 1] % 16 || b->part_off[6 + p] % 4)
+      return fail(MOE_EALIGN, "%s: part offsets of projection %d not aligned (16 B codes/scales, 4 B g)", who, p);
+    if (b->part_off[2 * p] + n / 2 > b->record_bytes || b->part_off[2 * p + 1] + n / 16 > b->record_bytes ||
+        b->part_off[6 + p] + 4 > b->record_bytes)
+      return fail(MOE_EINVAL, "%s: part of projection %d outside the record", who, p);
+  }
+  v->base = static_cast<const uint8_t*>(b->base);
+  v->stride = b->stride;
+  for (int p = 0; p < 3; p++) {
+    v->codes[p] = b->part_off[2 * p];
+    v->scales[p] = b->part_off[2 * p + 1];
+    v->g[p] = b->part_off[6 + p];
+  }
+  v->H = b->H;
+  v->I = b->I;
+  v->E = b->E;
+  return MOE_OK;
+}
+
+// ---- S0 pack -------------------------------------------------------------------
+MOE_API int moe_pack_nvfp4_bank(const moe_nvfp4_bank* b, const uint32_t* const codes[3],
+                                const uint8_t* const scales[3], const float* const g[3],
+                                void* stream) {
+  BankView v;
+  int rc = bank_view(b, &v, "pack");
+  if (rc) return rc;
+  if (!codes || !scales || !g) return fail(MOE_EINVAL, "pack: null part arrays");
+  for (int p = 0; p < 3; p++)
+    if (!codes[p] || !scales[p] || !g[p]) return fail(MOE_EINVAL, "pack: null part of projection %d", p);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t n = (size_t)b->H * (size_t)b->I;
+  uint8_t* base = static_cast<uint8_t*>(b->base);
+  for (int e = 0; e < b->E; e++) {
+    uint8_t* rec = base + (size_t)e * b->stride;
+    for (int p = 0; p < 3; p++) {
+      rc = hip_check(hipMemcpyAsync(rec + b->part_off[2 * p], reinterpret_cast<const uint8_t*>(codes[p]) + e * (n / 2),
+                                    n / 2, hipMemcpyDefault, s), "pack codes");
+      if (rc) return rc;
+      rc = hip_check(hipMemcpyAsync(rec + b->part_off[2 * p + 1], scales[p] + e * (n / 16), n / 16,
+                                    hipMemcpyDefault, s), "pack scales");
+      if (rc) return rc;
+      rc = hip_check(hipMemcpyAsync(rec + b->part_off[6 + p], g[p] + e, 4, hipMemcpyDefault, s), "pack g");
+      if (rc) return rc;
+    }
+  }
+  return hip_check(launch_zero_tails(base, b->stride, b->record_bytes, b->E, s), "pack zero pad");
+}
+
+// ---- S1 + S2 routing -----------------------------------------------------------
+MOE_API size_t moe_route_workspace_bytes(int T, int H, int E) {
+  if (T < 0 || H <= 0 || E <= 0) return 0;
+  const size_t nchunk = (size_t)(H + kRouterRows - 1) / kRouterRows;
+  return up256(nchunk * (size_t)T * (size_t)E * sizeof(float));
+}
+
+MOE_API int moe_route_topk(const uint16_t* x, const float* w_router, float* logits, int T, int H,
+                           int E, int k, int32_t* idx, float* w, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (T < 0) return fail(MOE_ESHAPE, "route: T=%d < 0", T);
+  if (E < 1 || E > 1024) return fail(MOE_ESHAPE, "route: E=%d outside [1, 1024]", E);
+  if (k < 1 || k > E || k > 64) return fail(MOE_ESHAPE, "route: k=%d outside [1, min(E, 64)]", k);
+  if (!logits || !idx || !w) return fail(MOE_EINVAL, "route: null logits/idx/w");
+  const bool gemm = x && w_router;
+  if ((x == nullptr) != (w_router == nullptr)) return fail(MOE_EINVAL, "route: give both x and w_router, or neither");
+  if (gemm) {
+    if (H <= 0 || H % 16) return fail(MOE_ESHAPE, "route: H=%d must be a positive multiple of 16", H);
+    if (!workspace) return fail(MOE_EINVAL, "route: the router GEMM needs a workspace");
+    if (!aligned(workspace, 256)) return fail(MOE_EALIGN, "route: workspace not 256-byte aligned");
+    if (workspace_bytes < moe_route_workspace_bytes(T, H, E))
+      return fail(MOE_EWORKSPACE, "route: workspace %zu < %zu bytes", workspace_bytes, moe_route_workspace_bytes(T, H, E));
+  }
+  if (T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* partial = nullptr;
+  int nchunk = 0;
+  if (gemm) {
+    partial = static_cast<float*>(workspace);
+    nchunk = (H + kRouterRows - 1) / kRouterRows;
+    int rc = hip_check(launch_router_partial(x, w_router, partial, T, H, E, s), "router");
+    if (rc) return rc;
+  }
+  return hip_check(launch_topk(partial, nchunk, logits, T, E, k, idx, w, s), "topk");
+}
+
+// ---- S3 sort ---------------------------------------------------------------------
+struct FwdLayout {
+  size_t counts, offsets, sorted, active, tile_e, tile_r, mid, part, total;
+  int max_tiles;
+};
+
+static FwdLayout fwd_layout(int T, int k, int H, int I, int E) {
+  FwdLayout L{};
+  const size_t P = (size_t)T * (size_t)k;
+  L.max_tiles = (int)(P / kPrefillMTile + (P < (size_t)E ? P : (size_t)E) + 1);
+  size_t o = 0;
+  L.counts = o;
+  o += 256;
+  L.offsets = o;
+  o += up256(((size_t)E + 1) * 4);
+  L.sorted = o;
+  o += up256(P * 4 + 4);
+  L.active = o;
+  o += up256((size_t)E * 4);
+  L.tile_e = o;
+  o += up256((size_t)L.max_tiles * 4);
+  L.tile_r = o;
+  o += up256((size_t)L.max_tiles * 4);
+  L.mid = o;
+  o += up256(P * (size_t)I * 2);
+  L.part = o;
+  o += up256(P * (size_t)H * 4);
+  L.total = o;
+  return L;
+}
+
+MOE_API int moe_sort_pairs(const int32_t* idx, int T, int k, int E, int32_t* offsets,
+                           int32_t* sorted, void* stream) {
+  if (T < 0 || k < 1 || k > 64) return fail(MOE_ESHAPE, "sort: T=%d k=%d", T, k);
+  if (E < 1 || E > 1024) return fail(MOE_ESHAPE, "sort: E=%d outside [1, 1024]", E);
+  if (!idx || !offsets || !sorted) return fail(MOE_EINVAL, "sort: null pointer");
+  const long long P = (long long)T * k;
+  if (P > (1LL << 30)) return fail(MOE_ESHAPE, "sort: too many pairs");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RouteTables rt{};  // no active list, counters or tile table for this entry point
+  rt.offsets = offsets;
+  rt.sorted = sorted;
+  return hip_check(launch_sort(idx, (int)P, E, rt, 0, 0, s), "sort");
+}
+
+// ---- S3..S7 forward --------------------------------------------------------------
+MOE_API size_t moe_nvfp4_workspace_bytes(int T, int k, int H, int I, int E) {
+  if (T < 0 || k < 1 || E < 1 || H <= 0 || I <= 0) return 0;
+  return fwd_layout(T, k, H, I, E).total;
+}
+
+static int prefill_min_pairs() {
+  static int v = -1;
+  if (v < 0) {
+    const char* s = std::getenv("MOE_PREFILL_MIN_PAIRS");
+    v = (s && *s) ? std::atoi(s) : 1024;
+    if (v < 1) v = 1;
+  }
+  return v;
+}
+
+MOE_API int moe_nvfp4_forward(const moe_nvfp4_bank* b, const uint16_t* x, int T, const int32_t* idx,
+                              const float* w, int k, const uint16_t* residual, void* y,
+                              unsigned flags, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  BankView v;
+  int rc = bank_view(b, &v, "forward");
+  if (rc) return rc;
+  if (v.H % 64 || v.I % 64) return fail(MOE_ESHAPE, "forward: H=%d and I=%d must be multiples of 64", v.H, v.I);
+  if (T < 0) return fail(MOE_ESHAPE, "forward: T=%d < 0", T);
+  if (k < 1 || k > v.E || k > 64) return fail(MOE_ESHAPE, "forward: k=%d outside [1, min(E, 64)]", k);
+  if ((flags & MOE_FORCE_DECODE) && (flags & MOE_FORCE_PREFILL))
+    return fail(MOE_EINVAL, "forward: both FORCE flags set");
+  if (flags & ~(MOE_F32_OUT | MOE_FORCE_DECODE | MOE_FORCE_PREFILL)) return fail(MOE_EINVAL, "forward: unknown flags");
+  if ((long long)T * k > (1LL << 30)) return fail(MOE_ESHAPE, "forward: too many pairs");
+  if (T == 0) return MOE_OK;
+  if (!x || !idx || !w || !y || !workspace) return fail(MOE_EINVAL, "forward: null pointer");
+  if (!aligned(x, 16) || (residual && !aligned(residual, 4)) || !aligned(y, 4) || !aligned(idx, 4) ||
+      !aligned(w, 4))
+    return fail(MOE_EALIGN, "forward: x must be 16-byte aligned, residual/y/idx/w 4-byte aligned");
+  if (!aligned(workspace, 256)) return fail(MOE_EALIGN, "forward: workspace not 256-byte aligned");
+  const FwdLayout L = fwd_layout(T, k, v.H, v.I, v.E);
+  if (workspace_bytes < L.total)
+    return fail(MOE_EWORKSPACE, "forward: workspace %zu < %zu bytes", workspace_bytes, L.total);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  RouteTables rt{};
+  rt.counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  rt.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  rt.sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+  rt.active = reinterpret_cast<int32_t*>(ws + L.active);
+  rt.tile_expert = reinterpret_cast<int32_t*>(ws + L.tile_e);
+  rt.tile_row0 = reinterpret_cast<int32_t*>(ws + L.tile_r);
+  uint16_t* mid = reinterpret_cast<uint16_t*>(ws + L.mid);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  const int P = T * k;
+  bool prefill = P >= prefill_min_pairs();
+  if (flags & MOE_FORCE_DECODE) prefill = false;
+  if (flags & MOE_FORCE_PREFILL) prefill = true;
+
+  rc = hip_check(launch_sort(idx, P, v.E, rt, prefill ? kPrefillMTile : 0, L.max_tiles, s), "sort");
+  if (rc) return rc;
+  if (prefill) {
+    rc = hip_check(launch_prefill_gateup(v, x, k, rt, L.max_tiles, mid, s), "prefill gate/up");
+    if (rc) return rc;
+    rc = hip_check(launch_prefill_down(v, mid, w, k, rt, L.max_tiles, part, s), "prefill down");
+    if (rc) return rc;
+  } else {
+    const int slots = P < v.E ? P : v.E;
+    rc = hip_check(launch_decode_gateup(v, x, k, rt, slots, mid, s), "decode gate/up");
+    if (rc) return rc;
+    rc = hip_check(launch_decode_down(v, mid, w, k, rt, slots, part, s), "decode down");
+    if (rc) return rc;
+  }
+  return hip_check(launch_combine(part, idx, v.E, T, v.H, k, residual, y, (flags & MOE_F32_OUT) != 0, s),
+                   "combine");
+}
+
+// ---- S8 affine8_g64 --------------------------------------------------------------
+MOE_API int affine8_g64_linear(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
+                               const uint16_t* biases, int T, int K, int N, uint16_t* y,
+                               void* stream) {
+  if (T < 0 || N < 1 || K < 64 || K % 64) return fail(MOE_ESHAPE, "affine8: T=%d K=%d N=%d", T, K, N);
+  if (T == 0) return MOE_OK;
+  if (!x || !codes || !scales || !biases || !y) return fail(MOE_EINVAL, "affine8: null pointer");
+  if (!aligned(codes, 16) || !aligned(x, 4) || !aligned(y, 2) || !aligned(scales, 2) || !aligned(biases, 2))
+    return fail(MOE_EALIGN, "affine8: codes must be 16-byte aligned, x 4-byte aligned");
+  return hip_check(launch_affine8(x, codes, scales, biases, T, K, N, y, static_cast<hipStream_t>(stream)),
+                   "affine8");
+}
+
+// ---- S9 rmsnorm --------------------------------------------------------------------
+MOE_API int moe_rmsnorm(const uint16_t* x, int T, int H, float eps, uint16_t* y, void* stream) {
+  if (T < 0 || H < 1) return fail(MOE_ESHAPE, "rmsnorm: T=%d H=%d", T, H);
+  if (!(eps >= 0.0f)) return fail(MOE_EINVAL, "rmsnorm: eps must be >= 0");
+  if (T == 0) return MOE_OK;
+  if (!x || !y) return fail(MOE_EINVAL, "rmsnorm: null pointer");
+  return hip_check(launch_rmsnorm(x, T, H, eps, y, static_cast<hipStream_t>(stream)), "rmsnorm");
+}
+
+// ---- dequant test export -----------------------------------------------------------
+MOE_API int moe_nvfp4_dequant(const moe_nvfp4_bank* b, int expert, int proj, float* out_f32,
+                              uint16_t* out_unit, void* stream) {
+  BankView v;
+  int rc = bank_view(b, &v, "dequant");
+  if (rc) return rc;
+  if (expert < 0 || expert >= v.E) return fail(MOE_EINVAL, "dequant: expert %d outside [0, %d)", expert, v.E);
+  if (proj < 0 || proj > 2) return fail(MOE_EINVAL, "dequant: proj %d outside [0, 2]", proj);
+  if (!out_f32 && !out_unit) return fail(MOE_EINVAL, "dequant: no output");
+  if ((out_f32 && !aligned(out_f32, 4)) || (out_unit && !aligned(out_unit, 2)))
+    return fail(MOE_EALIGN, "dequant: output alignment");
+  return hip_check(launch_dequant(v, expert, proj, out_f32, out_unit, static_cast<hipStream_t>(stream)),
+                   "dequant");
+}
+
+// ---- timing --------------------------------------------------------------------------
+MOE_API int moe_profile_enable(int on) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> lk(p.mu);
+  p.clear();
+  p.on = on != 0;
+  return MOE_OK;
+}
+
+MOE_API int moe_profile_read(const char* name, double* total_ms, int64_t* launches) {
+  if (!name || !total_ms || !launches) return fail(MOE_EINVAL, "profile_read: null pointer");
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> lk(p.mu);
+  double tot = 0.0;
+  int64_t n = 0;
+  auto it = p.done.find(name);
+  if (it != p.done.end()) {
+    for (auto& pe : it->second) {
+      int rc = hip_check(hipEventSynchronize(pe.end), "profile_read");
+      if (rc) return rc;
+      float ms = 0.0f;
+      rc = hip_check(hipEventElapsedTime(&ms, pe.start, pe.end), "profile_read");
+      if (rc) return rc;
+      tot += ms;
+      n++;
+    }
+  }
+  *total_ms = tot;
+  *launches = n;
+  return MOE_OK;
+}

@@ -1,0 +1,69 @@
+// Internal launch interface of libmoe_mi355x.so (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Where one bank's parts live: byte offsets inside every record.
+struct BankView {
+  const uint8_t* base;
+  uint64_t stride;
+  uint64_t codes[3], scales[3], g[3];
+  int H, I, E;
+};
+
+// Routing tables written by the pair sort into the forward's workspace.
+struct RouteTables {
+  int32_t* offsets;     // [E+1] first sorted slot of each expert
+  int32_t* sorted;      // [P] pair ids, grouped by expert, stable
+  int32_t* active;      // [E] experts with at least one pair, ascending
+  int32_t* counts;      // [0] n_active, [1] n_tiles
+  int32_t* tile_expert; // [max_tiles] grouped-GEMM tiles: expert
+  int32_t* tile_row0;   // [max_tiles] first sorted slot of the tile
+};
+
+// router: partial logits over chunks of H, reduced in the top-k kernel
+constexpr int kRouterRows = 64;   // H rows per router block
+constexpr int kRouterTok = 8;     // tokens per router block
+hipError_t launch_router_partial(const uint16_t* x, const float* Wr, float* partial, int T, int H,
+                                 int E, hipStream_t s);
+// top-k + softmax, one wave per token; partial == nullptr: logits are the input
+hipError_t launch_topk(const float* partial, int nchunk, float* logits, int T, int E, int k,
+                       int32_t* idx, float* w, hipStream_t s);
+// stable counting sort of the T*k pairs; also the active list and, when
+// mtile > 0, the grouped-GEMM tile table (tiles of mtile sorted slots)
+hipError_t launch_sort(const int32_t* idx, int P, int E, RouteTables rt, int mtile, int max_tiles,
+                       hipStream_t s);
+
+// expert-streaming (GEMV) kernels
+hipError_t launch_decode_gateup(const BankView& b, const uint16_t* x, int k, const RouteTables& rt,
+                                int slots, uint16_t* mid, hipStream_t s);
+hipError_t launch_decode_down(const BankView& b, const uint16_t* mid, const float* w, int k,
+                              const RouteTables& rt, int slots, float* part, hipStream_t s);
+// y[t] = residual[t] + sum_j part[t*k+j] (j ascending); pairs with idx
+// outside [0, E) contribute nothing
+hipError_t launch_combine(const float* part, const int32_t* idx, int E, int T, int H, int k,
+                          const uint16_t* residual, void* y, bool f32_out, hipStream_t s);
+
+// grouped-GEMM (bf16 MFMA) kernels
+constexpr int kPrefillMTile = 128;
+hipError_t launch_prefill_gateup(const BankView& b, const uint16_t* x, int k, const RouteTables& rt,
+                                 int max_tiles, uint16_t* mid, hipStream_t s);
+hipError_t launch_prefill_down(const BankView& b, const uint16_t* mid, const float* w, int k,
+                               const RouteTables& rt, int max_tiles, float* part, hipStream_t s);
+
+// misc
+hipError_t launch_zero_tails(uint8_t* base, uint64_t stride, uint64_t record_bytes, int E,
+                             hipStream_t s);
+hipError_t launch_dequant(const BankView& b, int expert, int proj, float* out_f32,
+                          uint16_t* out_unit, hipStream_t s);
+hipError_t launch_rmsnorm(const uint16_t* x, int T, int H, float eps, uint16_t* y, hipStream_t s);
+hipError_t launch_affine8(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
+                          const uint16_t* biases, int T, int K, int N, uint16_t* y, hipStream_t s);
+
+// kernel timing (api.hip)
+void prof_begin(const char* name, hipStream_t s);
+void prof_end(const char* name, hipStream_t s);
+
+}  // namespace moe
