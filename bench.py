@@ -67,7 +67,6 @@ class DecodeLeg:
         self.idx = torch.empty((ROTATE, T, k), dtype=torch.int32, device="cuda")
         self.w = torch.empty((ROTATE, T, k), dtype=torch.float32, device="cuda")
         self.y = torch.empty((T, H), dtype=torch.int16, device="cuda")
-        self.rws = wq.workspace(wq.moe_route_workspace_bytes(T, H, E))
         self.ws = wq.workspace(wq.moe_nvfp4_workspace_bytes(T, k, H, I, E))
         self.i = 0
 
@@ -75,7 +74,7 @@ class DecodeLeg:
         c, r = self.c, self.i % ROTATE
         self.i += 1
         wq.moe_route_topk(self.x[r], self.Wr, self.logits, c["T"], c["H"], c["E"], c["k"], self.idx[r],
-                          self.w[r], self.rws)
+                          self.w[r])
         wq.moe_nvfp4_forward(self.bank, self.x[r], c["T"], self.idx[r], self.w[r], c["k"], None, self.y, 0,
                              self.ws)
 
@@ -203,7 +202,9 @@ def main():
     torch.cuda.synchronize()
     kern = {}
     for name in ["router", "topk", "sort", "decode_gateup", "decode_down", "combine"]:
-        kern[name] = kernel_avg_ms(name)
+        avg, cnt = kernel_avg_ms(name)
+        if cnt:
+            kern[name] = (avg, cnt)
     wq.moe_profile_enable(False)
     for n_, (avg, cnt) in kern.items():
         log(f"  {n_:15s} {avg * 1e3:8.2f} us x {cnt}")
@@ -237,6 +238,7 @@ def main():
             pre.step()
         torch.cuda.synchronize()
         pk = {n_: kernel_avg_ms(n_) for n_ in ["topk", "sort", "prefill_gateup", "prefill_down", "combine"]}
+        pk = {n_: v for n_, v in pk.items() if v[1]}
         wq.moe_profile_enable(False)
         for n_, (avg, cnt) in pk.items():
             log(f"  {n_:15s} {avg * 1e3:8.2f} us x {cnt}")

@@ -88,20 +88,18 @@ int moe_pack_nvfp4_bank(const moe_nvfp4_bank* b, const uint32_t* const codes[3],
 
 /* S1 + S2, routing ([PACK] intro: 8 of 256 experts per token; [VQ] "What
  * stays native": FP32 router logits).
- *   If x and w_router are both non-null: logits[t][e] = sum_h x[t][h]*Wr[h][e]
- *   (f32 accumulation, partial sums over 64-row chunks of H added in chunk
- *   order) is computed into `logits` first; the chunk sums need `workspace`
- *   (device, 256-byte aligned, >= moe_route_workspace_bytes(T, H, E) bytes).
- *   Otherwise `logits` is the input and workspace may be NULL. Then per token:
- *   the k largest logits (ties: lower expert index; -0 == +0; a NaN ranks
- *   below every number), idx i32 [T][k] in descending order, and w f32 [T][k]
- *   = softmax over the k selected logits (f32, summed in slot order).
- *   x bf16 [T][H]; w_router f32 [H][E]; logits f32 [T][E].
+ *   If x and w_router are both non-null: logits[t][e] = sum_h x[t][h]*Wr[e][h]
+ *   (f32 accumulation) is computed into `logits` first. Otherwise `logits` is
+ *   the input. Then per token: the k largest logits (ties: lower expert index;
+ *   -0 == +0; a NaN ranks below every number), idx i32 [T][k] in descending
+ *   order, and w f32 [T][k] = softmax over the k selected logits (f32, summed
+ *   in slot order).
+ *   x bf16 [T][H] (8-byte aligned); w_router f32 [E][H], one row per expert
+ *   (16-byte aligned; the routers stay F32 as released, [PACK] residents
+ *   bullet); logits f32 [T][E].
  *   Rules: T >= 0, 1 <= k <= min(E, 64), 1 <= E <= 1024, H % 16 == 0. */
-size_t moe_route_workspace_bytes(int T, int H, int E);
 int moe_route_topk(const uint16_t* x, const float* w_router, float* logits, int T, int H,
-                   int E, int k, int32_t* idx, float* w, void* workspace,
-                   size_t workspace_bytes, void* stream);
+                   int E, int k, int32_t* idx, float* w, void* stream);
 
 /* S3, token -> expert counting sort of the P = T*k pairs (pair p = t*k + j):
  * offsets i32 [E+1] (offsets[e] = first sorted slot of expert e, offsets[E] = P)

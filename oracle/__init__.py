@@ -144,7 +144,8 @@ def router_logits(x_bf16, Wr):
     x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
     W = np.ascontiguousarray(Wr, dtype=np.float32)
     T, H = x.shape
-    E = W.shape[1]
+    E = W.shape[0]
+    assert W.shape[1] == H
     out = np.empty((T, E), dtype=np.float32)
     lib().orc_router_logits(_p(x, C.c_uint16), _p(W, C.c_float), T, H, E, _p(out, C.c_float))
     return out

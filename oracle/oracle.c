@@ -187,7 +187,7 @@ void orc_router_logits(const uint16_t* x, const float* Wr, int T, int H, int E,
     for (int e = 0; e < E; e++) {
       double acc = 0.0;
       for (int h = 0; h < H; h++)
-        acc += (double)orc_bf16_to_f32(x[(size_t)t * H + h]) * (double)Wr[(size_t)h * E + e];
+        acc += (double)orc_bf16_to_f32(x[(size_t)t * H + h]) * (double)Wr[(size_t)e * H + h];
       logits[(size_t)t * E + e] = (float)acc;
     }
 }

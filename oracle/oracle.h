@@ -77,8 +77,10 @@ void orc_dequant_projection(const uint8_t* record, int H, int I, int proj,
                             float* w_out, uint16_t* unit_out);
 
 /* ---- routing ------------------------------------------------------------ */
-/* logits[t][e] = f32( sum_h x[t][h] * Wr[h][e] ), sum in f64; [VQ] "What stays
- * native" keeps router logits in FP32. x bf16 [T][H], Wr f32 [H][E]. */
+/* logits[t][e] = f32( sum_h x[t][h] * Wr[e][h] ), sum in f64; [VQ] "What stays
+ * native" keeps router logits in FP32. x bf16 [T][H], Wr f32 [E][H] (one row
+ * per expert, the layout of a Linear layer's weight; [PACK] residents bullet
+ * keeps the routers in F32 as released). */
 void orc_router_logits(const uint16_t* x, const float* Wr, int T, int H, int E,
                        float* logits);
 /* Per token: the k largest logits (ties: lower expert index first; -0 == +0),

@@ -114,8 +114,8 @@ def activations(seed, T, H, stream=S_X):
 
 
 def router_weights(seed, H, E, layer=0):
-    """f32 N(0, 0.02) [H][E]"""
-    return (normal_np(seed, S_WR + 16 * layer, H * E) * 0.02).astype(np.float32).reshape(H, E)
+    """f32 N(0, 0.02) [E][H] (one row per expert)"""
+    return (normal_np(seed, S_WR + 16 * layer, H * E) * 0.02).astype(np.float32).reshape(E, H)
 
 
 def zipf_ranks(seed, E, s=1.1):

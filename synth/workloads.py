@@ -52,7 +52,7 @@ def host_parts(seed, expert, H, I):
 
 def inputs(name, variant=0):
     """Host inputs of a config: x bf16 bits [T][H], and either the router
-    weights (f32 [H][E]) or the given logits (f32 [T][E]). `variant` draws a
+    weights (f32 [E][H]) or the given logits (f32 [T][E]). `variant` draws a
     different x (and logits) from the same distribution."""
     c = CONFIGS[name]
     seed = c["seed"] + 1000 * variant

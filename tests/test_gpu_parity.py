@@ -164,8 +164,7 @@ def gpu_route(x_bits, Wr, logits_in, E, k):
     w = torch.empty((T, k), dtype=torch.float32, device=DEV)
     if logits_in is None:
         lg = torch.empty((T, E), dtype=torch.float32, device=DEV)
-        ws = wq.workspace(wq.moe_route_workspace_bytes(T, H, E))
-        wq.moe_route_topk(bf16_tensor(x_bits), torch.from_numpy(Wr).to(DEV), lg, T, H, E, k, idx, w, ws)
+        wq.moe_route_topk(bf16_tensor(x_bits), torch.from_numpy(Wr).to(DEV), lg, T, H, E, k, idx, w)
     else:
         lg = torch.from_numpy(np.ascontiguousarray(logits_in)).to(DEV)
         wq.moe_route_topk(None, None, lg, T, H, E, k, idx, w)
@@ -284,6 +283,25 @@ def test_forward_tiny_ragged_and_residual(tiny_bank):
         yf, yb = gpu_forward(bank, x, idx, w, k, flags, residual=res)
         check_f32(yf, ref_f, f"tiny ragged flags={flags}")
         check_bf16(yb, ref_f, "tiny ragged bf16")
+
+
+def test_forward_single_token_paths(tiny_bank):
+    # one token takes the flat kernels (k <= 16); k = 16 is their largest case,
+    # the residual is folded into their combine; flags=2 forces the same path
+    bank, _ = tiny_bank
+    c = W.CONFIGS["tiny"]
+    recs = host_records(c["bank_seed"], range(c["E"]), c["H"], c["I"])
+    for k, seed in [(2, 31), (1, 32), (16, 33), (7, 34)]:
+        x = synth.activations(seed, 1, c["H"])
+        res = synth.activations(seed + 100, 1, c["H"])
+        lg = np.random.default_rng(seed).normal(size=(1, c["E"])).astype(np.float32)
+        idx, w = oracle.route_topk(lg, k)
+        for residual in (None, res):
+            ref_f, _ = oracle.moe_forward(recs, c["E"], c["H"], c["I"], x, idx, w, residual=residual)
+            for flags in (0, 4):
+                yf, yb = gpu_forward(bank, x, idx, w, k, flags, residual=residual)
+                check_f32(yf, ref_f, f"one token k={k} flags={flags} residual={residual is not None}")
+                check_bf16(yb, ref_f, "one token bf16")
 
 
 def test_forward_decode_full_shape(big_bank):

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) >= 15, names
+    assert len(names) >= 14, names
     assert sorted(names) == sorted(wq.EXPORTS)
     L = C.CDLL(wq.LIB_PATH)
     for n in names:
@@ -92,14 +92,13 @@ def test_forward_validation_before_launch():
 def test_route_sort_affine_rmsnorm_validation():
     L = wq.lib()
     fake = C.c_void_p(1 << 26)
-    assert L.moe_route_topk(None, None, fake, 4, 256, 16, 0, fake, fake, None, 0, None) == wq.MOE_ESHAPE
-    assert L.moe_route_topk(None, None, fake, 4, 256, 16, 17, fake, fake, None, 0, None) == wq.MOE_ESHAPE
-    assert L.moe_route_topk(None, None, fake, 4, 256, 2048, 8, fake, fake, None, 0, None) == wq.MOE_ESHAPE
-    assert L.moe_route_topk(fake, None, fake, 4, 256, 16, 2, fake, fake, None, 0, None) == wq.MOE_EINVAL
-    need = L.moe_route_workspace_bytes(4, 256, 16)
-    assert L.moe_route_topk(fake, fake, fake, 4, 256, 16, 2, fake, fake, fake, need - 1, None) == wq.MOE_EWORKSPACE
-    assert L.moe_route_topk(fake, fake, fake, 4, 250, 16, 2, fake, fake, fake, need, None) == wq.MOE_ESHAPE
-    assert L.moe_route_topk(None, None, fake, 0, 256, 16, 2, fake, fake, None, 0, None) == wq.MOE_OK
+    assert L.moe_route_topk(None, None, fake, 4, 256, 16, 0, fake, fake, None) == wq.MOE_ESHAPE
+    assert L.moe_route_topk(None, None, fake, 4, 256, 16, 17, fake, fake, None) == wq.MOE_ESHAPE
+    assert L.moe_route_topk(None, None, fake, 4, 256, 2048, 8, fake, fake, None) == wq.MOE_ESHAPE
+    assert L.moe_route_topk(fake, None, fake, 4, 256, 16, 2, fake, fake, None) == wq.MOE_EINVAL
+    assert L.moe_route_topk(fake, fake, fake, 4, 250, 16, 2, fake, fake, None) == wq.MOE_ESHAPE
+    assert L.moe_route_topk(C.c_void_p((1 << 26) + 2), fake, fake, 4, 256, 16, 2, fake, fake, None) == wq.MOE_EALIGN
+    assert L.moe_route_topk(None, None, fake, 0, 256, 16, 2, fake, fake, None) == wq.MOE_OK
     assert L.moe_sort_pairs(fake, 4, 0, 16, fake, fake, None) == wq.MOE_ESHAPE
     assert L.moe_sort_pairs(None, 4, 2, 16, fake, fake, None) == wq.MOE_EINVAL
     assert L.affine8_g64_linear(fake, fake, fake, fake, 2, 100, 64, fake, None) == wq.MOE_ESHAPE

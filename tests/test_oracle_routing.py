@@ -12,7 +12,7 @@ def test_router_logits_match_numpy_matmul():
     x = synth.activations(1, 5, 256)
     Wr = synth.router_weights(1, 256, 16)
     got = oracle.router_logits(x, Wr)
-    ref = (oracle.bf16_to_f32(x).astype(np.float64) @ Wr.astype(np.float64)).astype(np.float32)
+    ref = (oracle.bf16_to_f32(x).astype(np.float64) @ Wr.astype(np.float64).T).astype(np.float32)
     # both are f64 sums rounded once to f32; the summation orders differ, so
     # allow one f32 ulp
     ulp = np.spacing(np.abs(ref))

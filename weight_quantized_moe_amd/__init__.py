@@ -21,7 +21,7 @@ GATE, UP, DOWN = 0, 1, 2
 
 EXPORTS = [
     "moe_last_error", "moe_nvfp4_record_bytes", "moe_nvfp4_record_stride", "moe_nvfp4_bank_init",
-    "moe_pack_nvfp4_bank", "moe_route_workspace_bytes", "moe_route_topk", "moe_sort_pairs",
+    "moe_pack_nvfp4_bank", "moe_route_topk", "moe_sort_pairs",
     "moe_nvfp4_workspace_bytes", "moe_nvfp4_forward", "affine8_g64_linear", "moe_rmsnorm",
     "moe_nvfp4_dequant", "moe_profile_enable", "moe_profile_read",
 ]
@@ -61,10 +61,8 @@ def lib():
         L.moe_nvfp4_bank_init.argtypes = [bankp, vp, i32, i32, i32]
         L.moe_pack_nvfp4_bank.restype = i32
         L.moe_pack_nvfp4_bank.argtypes = [bankp, C.POINTER(vp), C.POINTER(vp), C.POINTER(vp), vp]
-        L.moe_route_workspace_bytes.restype = sz
-        L.moe_route_workspace_bytes.argtypes = [i32, i32, i32]
         L.moe_route_topk.restype = i32
-        L.moe_route_topk.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+        L.moe_route_topk.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
         L.moe_sort_pairs.restype = i32
         L.moe_sort_pairs.argtypes = [vp, i32, i32, i32, vp, vp, vp]
         L.moe_nvfp4_workspace_bytes.restype = sz
@@ -139,14 +137,9 @@ def moe_pack_nvfp4_bank(bank, codes, scales, g, stream=None):
 
 
 # ---- routing ------------------------------------------------------------------------
-def moe_route_workspace_bytes(T, H, E):
-    return lib().moe_route_workspace_bytes(T, H, E)
-
-
-def moe_route_topk(x, w_router, logits, T, H, E, k, idx, w, workspace=None, stream=None):
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+def moe_route_topk(x, w_router, logits, T, H, E, k, idx, w, stream=None):
     _check(lib().moe_route_topk(_ptr(x), _ptr(w_router), _ptr(logits), T, H, E, k, _ptr(idx), _ptr(w),
-                                _ptr(workspace), ws_bytes, _stream(stream)))
+                                _stream(stream)))
 
 
 def moe_sort_pairs(idx, T, k, E, offsets, sorted_, stream=None):

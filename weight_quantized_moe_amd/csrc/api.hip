@@ -196,15 +196,8 @@ MOE_API int moe_pack_nvfp4_bank(const moe_nvfp4_bank* b, const uint32_t* const c
 }
 
 // ---- S1 + S2 routing -----------------------------------------------------------
-MOE_API size_t moe_route_workspace_bytes(int T, int H, int E) {
-  if (T < 0 || H <= 0 || E <= 0) return 0;
-  const size_t nchunk = (size_t)(H + kRouterRows - 1) / kRouterRows;
-  return up256(nchunk * (size_t)T * (size_t)E * sizeof(float));
-}
-
 MOE_API int moe_route_topk(const uint16_t* x, const float* w_router, float* logits, int T, int H,
-                           int E, int k, int32_t* idx, float* w, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+                           int E, int k, int32_t* idx, float* w, void* stream) {
   if (T < 0) return fail(MOE_ESHAPE, "route: T=%d < 0", T);
   if (E < 1 || E > 1024) return fail(MOE_ESHAPE, "route: E=%d outside [1, 1024]", E);
   if (k < 1 || k > E || k > 64) return fail(MOE_ESHAPE, "route: k=%d outside [1, min(E, 64)]", k);
@@ -213,22 +206,16 @@ MOE_API int moe_route_topk(const uint16_t* x, const float* w_router, float* logi
   if ((x == nullptr) != (w_router == nullptr)) return fail(MOE_EINVAL, "route: give both x and w_router, or neither");
   if (gemm) {
     if (H <= 0 || H % 16) return fail(MOE_ESHAPE, "route: H=%d must be a positive multiple of 16", H);
-    if (!workspace) return fail(MOE_EINVAL, "route: the router GEMM needs a workspace");
-    if (!aligned(workspace, 256)) return fail(MOE_EALIGN, "route: workspace not 256-byte aligned");
-    if (workspace_bytes < moe_route_workspace_bytes(T, H, E))
-      return fail(MOE_EWORKSPACE, "route: workspace %zu < %zu bytes", workspace_bytes, moe_route_workspace_bytes(T, H, E));
+    if (!aligned(x, 8) || !aligned(w_router, 16)) return fail(MOE_EALIGN, "route: x must be 8-byte, w_router 16-byte aligned");
   }
+  if (!aligned(logits, 4)) return fail(MOE_EALIGN, "route: logits alignment");
   if (T == 0) return MOE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* partial = nullptr;
-  int nchunk = 0;
   if (gemm) {
-    partial = static_cast<float*>(workspace);
-    nchunk = (H + kRouterRows - 1) / kRouterRows;
-    int rc = hip_check(launch_router_partial(x, w_router, partial, T, H, E, s), "router");
+    int rc = hip_check(launch_router(x, w_router, logits, T, H, E, s), "router");
     if (rc) return rc;
   }
-  return hip_check(launch_topk(partial, nchunk, logits, T, E, k, idx, w, s), "topk");
+  return hip_check(launch_topk(logits, T, E, k, idx, w, s), "topk");
 }
 
 // ---- S3 sort ---------------------------------------------------------------------
@@ -331,22 +318,33 @@ MOE_API int moe_nvfp4_forward(const moe_nvfp4_bank* b, const uint16_t* x, int T,
   bool prefill = P >= prefill_min_pairs();
   if (flags & MOE_FORCE_DECODE) prefill = false;
   if (flags & MOE_FORCE_PREFILL) prefill = true;
+  const bool f32_out = (flags & MOE_F32_OUT) != 0;
+  if (!prefill && T == 1 && k <= kFlatDecodeMaxK && (size_t)k * v.I * 2 <= 65536)
+    return hip_check(launch_flat_decode(v, x, idx, w, k, residual, mid, y, f32_out, s), "decode");
 
-  rc = hip_check(launch_sort(idx, P, v.E, rt, prefill ? kPrefillMTile : 0, L.max_tiles, s), "sort");
-  if (rc) return rc;
   if (prefill) {
+    rc = hip_check(launch_sort(idx, P, v.E, rt, kPrefillMTile, L.max_tiles, s), "sort");
+    if (rc) return rc;
     rc = hip_check(launch_prefill_gateup(v, x, k, rt, L.max_tiles, mid, s), "prefill gate/up");
     if (rc) return rc;
     rc = hip_check(launch_prefill_down(v, mid, w, k, rt, L.max_tiles, part, s), "prefill down");
     if (rc) return rc;
   } else {
+    // few pairs: each GEMV block routes itself from idx, no sort launch
+    const bool inblock = P <= kDecInblockMaxP;
+    if (!inblock) {
+      rc = hip_check(launch_sort(idx, P, v.E, rt, 0, L.max_tiles, s), "sort");
+      if (rc) return rc;
+    }
+    const RouteTables* rtp = inblock ? nullptr : &rt;
     const int slots = P < v.E ? P : v.E;
-    rc = hip_check(launch_decode_gateup(v, x, k, rt, slots, mid, s), "decode gate/up");
+    const int max_m = T;  // top-k selects an expert at most once per token
+    rc = hip_check(launch_decode_gateup(v, x, idx, P, k, rtp, slots, max_m, mid, s), "decode gate/up");
     if (rc) return rc;
-    rc = hip_check(launch_decode_down(v, mid, w, k, rt, slots, part, s), "decode down");
+    rc = hip_check(launch_decode_down(v, mid, w, idx, P, k, rtp, slots, max_m, part, s), "decode down");
     if (rc) return rc;
   }
-  return hip_check(launch_combine(part, idx, v.E, T, v.H, k, residual, y, (flags & MOE_F32_OUT) != 0, s),
+  return hip_check(launch_combine(part, idx, v.E, T, v.H, k, residual, y, f32_out, s),
                    "combine");
 }
 

@@ -8,14 +8,19 @@
 // native", "Kernel budget on GB10").
 //
 // These kernels are bound by HBM bandwidth: every weight byte is read once per
-// call. A block owns one active expert and a tile of output rows; a wave owns
-// one row at a time and its 64 lanes sweep the row's input blocks, lane l
-// taking blocks l, l+64, ... so each load instruction reads 512 contiguous
-// bytes of codes. Each 8-byte chunk is one E4M3 block (16 E2M1 codes): two
-// U32 words turn into 8 packed bf16 pairs (v_cvt_scalef32_pk_bf16_fp4), eight
-// v_dot2 give the block's partial sum, and one FMA applies the block scale
-// S = f32(e4m3 * t). The expert's token activations sit in LDS; the weights
-// stay in registers while every token of the pass is applied to them.
+// call. A block owns one active expert and a tile of output rows. Inside a
+// wave, G lanes share a row (64/G rows per wave pass); lane `sub` of a row
+// takes the row's 64-input quads sub, sub+G, ... A quad is 4 E4M3 blocks: 32
+// bytes of codes (two 16-byte loads) and 4 scale bytes (one 4-byte load), so
+// every load is wide and each instruction reads G contiguous pieces of a row.
+// All loads of a wave pass are issued before any arithmetic. Each 16-code
+// block turns into 8 packed bf16 pairs (v_cvt_scalef32_pk_bf16_fp4, exact),
+// eight v_dot2 give its partial sum, and one FMA applies the block scale
+// S = f32(e4m3 * t). The expert's token activations sit in LDS (lanes of the
+// 64/G rows read the same addresses: broadcast); a row's G partial sums are
+// added with shuffles inside the G-lane group.
+#include <cstdlib>
+
 #include "common.h"
 #include "internal.h"
 
@@ -23,212 +28,308 @@ namespace moe {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / 64;
-constexpr int kGateUpRows = 16;  // rows of gate (and of up) per block
-constexpr int kDownRows = 32;    // rows of down per block
-constexpr int kDecTok = 4;       // tokens per pass (activations staged in LDS)
-constexpr int kChunksPerLane = 5;
 
 struct DecodeArgs {
   const uint8_t* bank;
   uint64_t stride;
   uint64_t codes[3], scales[3], g[3];
-  int H, I, k;
-  const uint16_t* in;   // gate/up: x [T][H]; down: mid [P][I] in sorted order
-  const float* w;       // down: routing weights [T*k]
-  RouteTables rt;
-  uint16_t* mid;        // gate/up output [P][I], sorted order
-  float* part;          // down output [P][H], pair order
+  int H, I, k, E, P;
+  int passes;           // wave passes (of 64/G rows) per block
+  const int32_t* idx;   // [P] expert of each pair
+  const uint16_t* in;   // gate/up: x [T][H]; down: mid [P][I] by pair id
+  const float* w;       // down: routing weights [P]
+  RouteTables rt;       // sorted tables, or rt.active == nullptr: in-block routing
+  uint16_t* mid;        // gate/up output [P][I] by pair id
+  float* part;          // down output [P][H] by pair id
 };
 
-// Stage the bf16 input rows of tokens m0..m0+mt-1 of expert slot range s0 into
-// LDS: xs[m][0..len/2) as packed pairs. 16-byte copies; len % 8 == 0.
+// In-block routing for P <= 256 pairs: finds the slot-th smallest expert id
+// present in idx and its pairs in ascending pair order (s_pairs). Returns
+// the pair count (0 if there are fewer than slot+1 distinct experts).
+// Block-uniform result; all threads call it.
+__device__ int route_in_block(const int32_t* idx, int P, int E, int slot, int* s_pairs, int* s_e) {
+  __shared__ uint32_t bits[32];  // E <= 1024
+  __shared__ int wcount[kDecWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = (E + 31) / 32;
+  if (tid < 32) bits[tid] = 0;
+  __syncthreads();
+  const int my = (tid < P) ? idx[tid] : -1;
+  const bool valid = my >= 0 && my < E;
+  if (valid) atomicOr(&bits[my >> 5], 1u << (my & 31));
+  __syncthreads();
+  if (tid == 0) {
+    int e = -1, seen = 0;
+    for (int i = 0; i < nw && e < 0; i++) {
+      const uint32_t wv = bits[i];
+      const int pc = __popc(wv);
+      if (seen + pc > slot) {
+        uint32_t v = wv;
+        for (int j = 0; j < slot - seen; j++) v &= v - 1;  // drop lower set bits
+        e = 32 * i + __ffs(v) - 1;
+      }
+      seen += pc;
+    }
+    *s_e = e;
+  }
+  __syncthreads();
+  const int e = *s_e;
+  if (e < 0) return 0;
+  const unsigned long long m = __ballot(valid && my == e);
+  if (lane == 0) wcount[wave] = __popcll(m);
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int wv = 0; wv < kDecWaves; wv++) {
+    if (wv < wave) before += wcount[wv];
+    total += wcount[wv];
+  }
+  if (valid && my == e) s_pairs[before + __popcll(m & ((1ull << lane) - 1ull))] = tid;
+  __syncthreads();
+  return total;
+}
+
+// Stage the bf16 input rows of pairs[m0..m0+mt) into LDS as packed pairs,
+// xs[m][0..len/2). by_token: row = pair / k (x), else row = pair (mid).
 __device__ __forceinline__ void stage_rows(uint32_t* xs, const uint16_t* src, int len,
-                                           const int32_t* sorted, int s0, int m0, int mt, int k,
-                                           bool by_token) {
+                                           const int* pairs, int m0, int mt, int k, bool by_token) {
   for (int m = 0; m < mt; m++) {
-    size_t row = by_token ? (size_t)(sorted[s0 + m0 + m] / k) : (size_t)(s0 + m0 + m);
+    const int p = pairs[m0 + m];
+    const size_t row = by_token ? (size_t)(p / k) : (size_t)p;
     const u32x4* s = reinterpret_cast<const u32x4*>(src + row * (size_t)len);
     u32x4* d = reinterpret_cast<u32x4*>(xs + m * (len / 2));
     for (int i = threadIdx.x; i < len / 8; i += kDecThreads) d[i] = s[i];
   }
 }
 
-__device__ __forceinline__ void lds_x16(const uint32_t* xrow, int blk, uint32_t* xv) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(xrow + 8 * blk);
-  u32x4 a = p[0], b = p[1];
-  xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
-  xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
+// one quad of one projection: 8 code words + 4 scale bytes
+struct Quad {
+  u32x4 c0, c1;
+  uint32_t s;
+};
+
+__device__ __forceinline__ Quad load_quad(const uint8_t* row_codes, const uint8_t* row_scales, int q) {
+  Quad v;
+  const u32x4* cp = reinterpret_cast<const u32x4*>(row_codes + 32 * (size_t)q);
+  v.c0 = cp[0];
+  v.c1 = cp[1];
+  v.s = *reinterpret_cast<const uint32_t*>(row_scales + 4 * (size_t)q);
+  return v;
 }
 
-// ---- S4 + S5 ------------------------------------------------------------------
-__global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a) {
-  const int slot = blockIdx.y;
-  if (slot >= a.rt.counts[0]) return;
-  const int e = a.rt.active[slot];
-  const int s0 = a.rt.offsets[e], M = a.rt.offsets[e + 1] - s0;
-  const int H = a.H, I = a.I, NB = H / 16;
+// the 8 packed input pairs of block b (0..3) of quad q, from LDS
+__device__ __forceinline__ void load_x8(const uint32_t* xrow, int q, int b, uint32_t* xw) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(xrow + 32 * q + 8 * b);
+  const u32x4 v0 = p[0], v1 = p[1];
+  xw[0] = v0.x;
+  xw[1] = v0.y;
+  xw[2] = v0.z;
+  xw[3] = v0.w;
+  xw[4] = v1.x;
+  xw[5] = v1.y;
+  xw[6] = v1.z;
+  xw[7] = v1.w;
+}
+
+// code words of block b of a quad
+__device__ __forceinline__ uint32_t quad_word(const Quad& v, int i) {
+  switch (i) {
+    case 0: return v.c0.x;
+    case 1: return v.c0.y;
+    case 2: return v.c0.z;
+    case 3: return v.c0.w;
+    case 4: return v.c1.x;
+    case 5: return v.c1.y;
+    case 6: return v.c1.z;
+    default: return v.c1.w;
+  }
+}
+
+__device__ __forceinline__ float quad_scale(const Quad& v, int b) {
+  switch (b) {
+    case 0: return e4m3_f32<0>(v.s);
+    case 1: return e4m3_f32<1>(v.s);
+    case 2: return e4m3_f32<2>(v.s);
+    default: return e4m3_f32<3>(v.s);
+  }
+}
+
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// NPROJ = 2: gate and up rows (input x, SwiGLU into mid); NPROJ = 1: down
+// rows (input mid, routing-weighted f32 into part). MT tokens per pass.
+// A wave walks its rows in steps (pass, quad batch); all loads of a step are
+// issued together before its arithmetic.
+template <int G, int kQB, int MT, int NPROJ>
+__global__ __launch_bounds__(kDecThreads) void gemv_kernel(DecodeArgs a) {
+  constexpr int R = 64 / G;  // rows per wave pass
+  __shared__ int s_pairs[kDecInblockMaxP];
+  __shared__ int s_e;
+  int e, M;
+  const int* pairs;
+  if (a.rt.active == nullptr) {
+    M = route_in_block(a.idx, a.P, a.E, blockIdx.y, s_pairs, &s_e);
+    e = s_e;
+    pairs = s_pairs;
+  } else {
+    if ((int)blockIdx.y >= a.rt.counts[0]) return;
+    e = a.rt.active[blockIdx.y];
+    const int s0 = a.rt.offsets[e];
+    M = a.rt.offsets[e + 1] - s0;
+    pairs = a.rt.sorted + s0;
+  }
+  if (M == 0) return;
+  const int K = (NPROJ == 2) ? a.H : a.I;  // inputs
+  const int N = (NPROJ == 2) ? a.I : a.H;  // output rows
+  const int nquads = K / 64;
+  const int nqb = (nquads + G * kQB - 1) / (G * kQB);  // quad batches per row
+  const int p0 = (NPROJ == 2) ? 0 : 2;
   const uint8_t* rec = a.bank + (size_t)e * a.stride;
-  const uint8_t* cg = rec + a.codes[0];
-  const uint8_t* sg = rec + a.scales[0];
-  const uint8_t* cu = rec + a.codes[1];
-  const uint8_t* su = rec + a.scales[1];
-  const float tg = global_factor(*reinterpret_cast<const float*>(rec + a.g[0]));
-  const float tu = global_factor(*reinterpret_cast<const float*>(rec + a.g[1]));
-  extern __shared__ uint32_t xs[];  // [kDecTok][H/2]
+  extern __shared__ uint32_t xs[];  // [MT][K/2]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r0 = blockIdx.x * kGateUpRows, r1 = min(I, r0 + kGateUpRows);
-  for (int m0 = 0; m0 < M; m0 += kDecTok) {
-    const int mt = min(kDecTok, M - m0);
-    __syncthreads();
-    stage_rows(xs, a.in, H, a.rt.sorted, s0, m0, mt, a.k, true);
-    __syncthreads();
-    for (int r = r0 + wave; r < r1; r += kDecWaves) {
-      float ag[kDecTok], au[kDecTok];
+  const int rsub = lane / G, sub = lane % G;
+  const int rows_per_block = a.passes * kDecWaves * R;
+  const int r0 = blockIdx.x * rows_per_block, r1 = min(N, r0 + rows_per_block);
+  // this wave's passes: rows r0 + (p * kDecWaves + wave) * R + rsub
+  int np = 0;
+  while (np < a.passes && r0 + (np * kDecWaves + wave) * R < r1) np++;
+  const int nsteps = np * nqb;
+
+  Quad v[NPROJ][kQB];
+  auto load_step = [&](int st) {
+    const int p = st / nqb, qb = (st % nqb) * G * kQB;
+    const int r = r0 + (p * kDecWaves + wave) * R + rsub;
+    if (r < r1) {
 #pragma unroll
-      for (int m = 0; m < kDecTok; m++) ag[m] = au[m] = 0.0f;
-      const uint8_t* rcg = cg + (size_t)r * (H / 2);
-      const uint8_t* rcu = cu + (size_t)r * (H / 2);
-      const uint8_t* rsg = sg + (size_t)r * NB;
-      const uint8_t* rsu = su + (size_t)r * NB;
-      for (int cb = 0; cb < NB; cb += 64 * kChunksPerLane) {
-        u32x2 wg[kChunksPerLane], wu[kChunksPerLane];
-        uint32_t bg[kChunksPerLane], bu[kChunksPerLane];
+      for (int q = 0; q < NPROJ; q++) {
+        const uint8_t* rc = rec + a.codes[p0 + q] + (size_t)r * (K / 2);
+        const uint8_t* rs = rec + a.scales[p0 + q] + (size_t)r * (K / 16);
 #pragma unroll
-        for (int i = 0; i < kChunksPerLane; i++) {
-          int c = cb + lane + 64 * i;
-          if (c < NB) {
-            wg[i] = *reinterpret_cast<const u32x2*>(rcg + 8 * (size_t)c);
-            wu[i] = *reinterpret_cast<const u32x2*>(rcu + 8 * (size_t)c);
-            bg[i] = rsg[c];
-            bu[i] = rsu[c];
-          }
+        for (int i = 0; i < kQB; i++) {
+          const int qd = qb + sub + G * i;
+          if (qd < nquads) v[q][i] = load_quad(rc, rs, qd);
         }
+      }
+    }
+  };
+  float t[NPROJ];
 #pragma unroll
-        for (int i = 0; i < kChunksPerLane; i++) {
-          int c = cb + lane + 64 * i;
-          if (c < NB) {
-            const float Sg = e4m3_f32_dyn(bg[i]) * tg;
-            const float Su = e4m3_f32_dyn(bu[i]) * tu;
+  for (int q = 0; q < NPROJ; q++) t[q] = global_factor(*reinterpret_cast<const float*>(rec + a.g[p0 + q]));
+
+  for (int m0 = 0; m0 < M; m0 += MT) {
+    const int mt = min(MT, M - m0);
+    __syncthreads();
+    stage_rows(xs, a.in, K, pairs, m0, mt, a.k, NPROJ == 2);
+    __syncthreads();
+    float wt[MT];
+    int pr[MT];
 #pragma unroll
-            for (int m = 0; m < kDecTok; m++) {
-              if (m < mt) {
-                uint32_t xv[8];
-                lds_x16(xs + m * (H / 2), c, xv);
-                ag[m] = fmaf(Sg, block_dot16(wg[i].x, wg[i].y, xv), ag[m]);
-                au[m] = fmaf(Su, block_dot16(wu[i].x, wu[i].y, xv), au[m]);
+    for (int m = 0; m < MT; m++) {
+      pr[m] = (m < mt) ? pairs[m0 + m] : 0;
+      wt[m] = (NPROJ == 1 && m < mt) ? a.w[pr[m]] : 0.0f;
+    }
+    float acc[NPROJ][MT];
+#pragma unroll
+    for (int q = 0; q < NPROJ; q++)
+#pragma unroll
+      for (int m = 0; m < MT; m++) acc[q][m] = 0.0f;
+    for (int st = 0; st < nsteps; st++) {
+      load_step(st);
+      const int p = st / nqb, qb = (st % nqb) * G * kQB;
+      const int r = r0 + (p * kDecWaves + wave) * R + rsub;
+      const bool row_ok = r < r1;
+#pragma unroll
+      for (int i = 0; i < kQB; i++) {
+        const int qd = qb + sub + G * i;
+        if (row_ok && qd < nquads) {
+#pragma unroll
+          for (int m = 0; m < MT; m++) {
+            if (m < mt) {
+#pragma unroll
+              for (int b = 0; b < 4; b++) {
+                uint32_t xw[8];
+                load_x8(xs + m * (K / 2), qd, b, xw);
+#pragma unroll
+                for (int q = 0; q < NPROJ; q++) {
+                  const float S = quad_scale(v[q][i], b) * t[q];
+                  acc[q][m] = fmaf(S, block_dot16(quad_word(v[q][i], 2 * b), quad_word(v[q][i], 2 * b + 1), xw),
+                                   acc[q][m]);
+                }
               }
             }
           }
         }
       }
+      if (st % nqb == nqb - 1) {  // the pass's rows are complete
 #pragma unroll
-      for (int m = 0; m < kDecTok; m++) {
-        if (m < mt) {
-          float g = wave_sum(ag[m]);
-          float u = wave_sum(au[m]);
-          if (lane == 0) a.mid[(size_t)(s0 + m0 + m) * I + r] = f32_to_bf16(silu_mul(g, u));
+        for (int m = 0; m < MT; m++) {
+          if (m < mt) {
+            float sm[NPROJ];
+#pragma unroll
+            for (int q = 0; q < NPROJ; q++) sm[q] = group_sum<G>(acc[q][m]);
+            if (sub == 0 && row_ok) {
+              if (NPROJ == 2)
+                a.mid[(size_t)pr[m] * N + r] = f32_to_bf16(silu_mul(sm[0], sm[NPROJ - 1]));
+              else
+                a.part[(size_t)pr[m] * N + r] = wt[m] * sm[0];
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < NPROJ; q++) acc[q][m] = 0.0f;
         }
       }
     }
   }
 }
 
-hipError_t launch_decode_gateup(const BankView& b, const uint16_t* x, int k, const RouteTables& rt,
-                                int slots, uint16_t* mid, hipStream_t s) {
-  DecodeArgs a{};
-  a.bank = b.base;
-  a.stride = b.stride;
-  for (int p = 0; p < 3; p++) {
-    a.codes[p] = b.codes[p];
-    a.scales[p] = b.scales[p];
-    a.g[p] = b.g[p];
+static int env_int(const char* name, int dflt) {
+  const char* s = std::getenv(name);
+  return (s && *s) ? std::atoi(s) : dflt;
+}
+
+template <int G, int QB, int NPROJ>
+static void launch_gemv_g(const DecodeArgs& b, dim3 grid, size_t lds, bool one, hipStream_t s) {
+  if (one)
+    hipLaunchKernelGGL((gemv_kernel<G, QB, 1, NPROJ>), grid, dim3(kDecThreads), lds, s, b);
+  else
+    hipLaunchKernelGGL((gemv_kernel<G, QB, 4, NPROJ>), grid, dim3(kDecThreads), lds, s, b);
+}
+
+// Tuning knobs (environment, read at each launch): MOE_GEMV_QB_{GATEUP,DOWN}
+// quads per lane per load step (1, 2 or 5); MOE_GEMV_PASSES_{GATEUP,DOWN} wave
+// passes per block.
+template <int NPROJ>
+static hipError_t launch_gemv(const DecodeArgs& a, int slots, int max_m, hipStream_t s) {
+  const int K = (NPROJ == 2) ? a.H : a.I;
+  const int N = (NPROJ == 2) ? a.I : a.H;
+  const int nquads = K / 64;
+  const int G = (nquads % 16 == 0 || nquads > 40) ? 16 : 8;
+  const int R = 64 / G;
+  const int qb = env_int(NPROJ == 2 ? "MOE_GEMV_QB_GATEUP" : "MOE_GEMV_QB_DOWN", 5);
+  DecodeArgs b = a;
+  b.passes = env_int(NPROJ == 2 ? "MOE_GEMV_PASSES_GATEUP" : "MOE_GEMV_PASSES_DOWN", 1);
+  if (b.passes < 1) b.passes = 1;
+  const int rows_per_block = b.passes * kDecWaves * R;
+  dim3 grid((N + rows_per_block - 1) / rows_per_block, slots);
+  const bool one = max_m <= 1;
+  const size_t lds = (size_t)(one ? 1 : 4) * K * 2;
+  if (G == 16) {
+    if (qb <= 1) launch_gemv_g<16, 1, NPROJ>(b, grid, lds, one, s);
+    else if (qb == 2) launch_gemv_g<16, 2, NPROJ>(b, grid, lds, one, s);
+    else launch_gemv_g<16, 5, NPROJ>(b, grid, lds, one, s);
+  } else {
+    if (qb <= 1) launch_gemv_g<8, 1, NPROJ>(b, grid, lds, one, s);
+    else if (qb == 2) launch_gemv_g<8, 2, NPROJ>(b, grid, lds, one, s);
+    else launch_gemv_g<8, 5, NPROJ>(b, grid, lds, one, s);
   }
-  a.H = b.H;
-  a.I = b.I;
-  a.k = k;
-  a.in = x;
-  a.rt = rt;
-  a.mid = mid;
-  dim3 grid((b.I + kGateUpRows - 1) / kGateUpRows, slots);
-  size_t lds = (size_t)kDecTok * b.H * 2;
-  prof_begin("decode_gateup", s);
-  hipLaunchKernelGGL(decode_gateup_kernel, grid, dim3(kDecThreads), lds, s, a);
-  prof_end("decode_gateup", s);
   return hipGetLastError();
 }
 
-// ---- S6: down, per pair, scaled by the routing weight --------------------------
-__global__ __launch_bounds__(kDecThreads) void decode_down_kernel(DecodeArgs a) {
-  const int slot = blockIdx.y;
-  if (slot >= a.rt.counts[0]) return;
-  const int e = a.rt.active[slot];
-  const int s0 = a.rt.offsets[e], M = a.rt.offsets[e + 1] - s0;
-  const int H = a.H, I = a.I, NB = I / 16;
-  const uint8_t* rec = a.bank + (size_t)e * a.stride;
-  const uint8_t* cd = rec + a.codes[2];
-  const uint8_t* sd = rec + a.scales[2];
-  const float td = global_factor(*reinterpret_cast<const float*>(rec + a.g[2]));
-  extern __shared__ uint32_t ms[];  // [kDecTok][I/2]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r0 = blockIdx.x * kDownRows, r1 = min(H, r0 + kDownRows);
-  for (int m0 = 0; m0 < M; m0 += kDecTok) {
-    const int mt = min(kDecTok, M - m0);
-    __syncthreads();
-    stage_rows(ms, a.in, I, a.rt.sorted, s0, m0, mt, a.k, false);
-    __syncthreads();
-    float wt[kDecTok];
-    int pr[kDecTok];
-#pragma unroll
-    for (int m = 0; m < kDecTok; m++) {
-      pr[m] = (m < mt) ? a.rt.sorted[s0 + m0 + m] : 0;
-      wt[m] = (m < mt) ? a.w[pr[m]] : 0.0f;
-    }
-    for (int r = r0 + wave; r < r1; r += kDecWaves) {
-      float ad[kDecTok];
-#pragma unroll
-      for (int m = 0; m < kDecTok; m++) ad[m] = 0.0f;
-      const uint8_t* rcd = cd + (size_t)r * (I / 2);
-      const uint8_t* rsd = sd + (size_t)r * NB;
-      for (int cb = 0; cb < NB; cb += 64 * kChunksPerLane) {
-        u32x2 wd[kChunksPerLane];
-        uint32_t bd[kChunksPerLane];
-#pragma unroll
-        for (int i = 0; i < kChunksPerLane; i++) {
-          int c = cb + lane + 64 * i;
-          if (c < NB) {
-            wd[i] = *reinterpret_cast<const u32x2*>(rcd + 8 * (size_t)c);
-            bd[i] = rsd[c];
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < kChunksPerLane; i++) {
-          int c = cb + lane + 64 * i;
-          if (c < NB) {
-            const float Sd = e4m3_f32_dyn(bd[i]) * td;
-#pragma unroll
-            for (int m = 0; m < kDecTok; m++) {
-              if (m < mt) {
-                uint32_t xv[8];
-                lds_x16(ms + m * (I / 2), c, xv);
-                ad[m] = fmaf(Sd, block_dot16(wd[i].x, wd[i].y, xv), ad[m]);
-              }
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < kDecTok; m++) {
-        if (m < mt) {
-          float d = wave_sum(ad[m]);
-          if (lane == 0) a.part[(size_t)pr[m] * H + r] = wt[m] * d;
-        }
-      }
-    }
-  }
-}
-
-hipError_t launch_decode_down(const BankView& b, const uint16_t* mid, const float* w, int k,
-                              const RouteTables& rt, int slots, float* part, hipStream_t s) {
+static DecodeArgs make_args(const BankView& b, const int32_t* idx, int P, int k, const RouteTables* rt) {
   DecodeArgs a{};
   a.bank = b.base;
   a.stride = b.stride;
@@ -239,15 +340,236 @@ hipError_t launch_decode_down(const BankView& b, const uint16_t* mid, const floa
   }
   a.H = b.H;
   a.I = b.I;
+  a.E = b.E;
   a.k = k;
+  a.P = P;
+  a.idx = idx;
+  if (rt) a.rt = *rt;  // else all-null tables: in-block routing
+  return a;
+}
+
+hipError_t launch_decode_gateup(const BankView& b, const uint16_t* x, const int32_t* idx, int P, int k,
+                                const RouteTables* rt, int slots, int max_m, uint16_t* mid,
+                                hipStream_t s) {
+  DecodeArgs a = make_args(b, idx, P, k, rt);
+  a.in = x;
+  a.mid = mid;
+  prof_begin("decode_gateup", s);
+  hipError_t e = launch_gemv<2>(a, slots, max_m, s);
+  prof_end("decode_gateup", s);
+  return e;
+}
+
+hipError_t launch_decode_down(const BankView& b, const uint16_t* mid, const float* w,
+                              const int32_t* idx, int P, int k, const RouteTables* rt, int slots,
+                              int max_m, float* part, hipStream_t s) {
+  DecodeArgs a = make_args(b, idx, P, k, rt);
   a.in = mid;
   a.w = w;
-  a.rt = rt;
   a.part = part;
-  dim3 grid((b.H + kDownRows - 1) / kDownRows, slots);
-  size_t lds = (size_t)kDecTok * b.I * 2;
   prof_begin("decode_down", s);
-  hipLaunchKernelGGL(decode_down_kernel, grid, dim3(kDecThreads), lds, s, a);
+  hipError_t e = launch_gemv<1>(a, slots, max_m, s);
+  prof_end("decode_down", s);
+  return e;
+}
+
+// ---- one token (T = 1): flat kernels ---------------------------------------------
+// With one token every pair has its own expert, so the token's activations are
+// shared by all of them. Gate/up: a fixed grid of blocks stages x in LDS once;
+// its waves then walk a flat list of (pair, 4-row group) items with no further
+// barrier, each item one batch of 16-byte loads (the 4 rows of gate and up).
+// Down + combine: a block owns 8 output rows for all k pairs; its 4 waves take
+// pairs j = wave, wave + 4, ..., the routing-weighted row sums meet in LDS and
+// are added in slot order (j ascending) onto the residual, and y is written
+// directly: no per-pair partial rows and no separate combine pass.
+struct FlatArgs {
+  const uint8_t* bank;
+  uint64_t stride;
+  uint64_t codes[3], scales[3], g[3];
+  int H, I, E, k;
+  const int32_t* idx;       // [k]
+  const float* w;           // [k]
+  const uint16_t* x;        // [H]
+  const uint16_t* residual; // [H] or null
+  uint16_t* mid;            // [k][I]
+  void* y;                  // [H] bf16 or f32
+  int f32_out;
+};
+
+__global__ __launch_bounds__(kDecThreads) void flat_gateup_kernel(FlatArgs a) {
+  constexpr int G = 16, R = 64 / G, QB = 5;
+  extern __shared__ uint32_t xs[];  // [H/2]
+  __shared__ int s_idx[kFlatDecodeMaxK];
+  const int H = a.H, I = a.I, nquads = H / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rsub = lane / G, sub = lane % G;
+  if (threadIdx.x < a.k) {
+    const int e = a.idx[threadIdx.x];
+    s_idx[threadIdx.x] = (e >= 0 && e < a.E) ? e : -1;
+  }
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.x);
+    u32x4* dst = reinterpret_cast<u32x4*>(xs);
+    for (int i = threadIdx.x; i < H / 8; i += kDecThreads) dst[i] = src[i];
+  }
+  __syncthreads();
+  const int groups = (I + R - 1) / R;
+  const int n_items = a.k * groups;
+  for (int it = blockIdx.x * kDecWaves + wave; it < n_items; it += gridDim.x * kDecWaves) {
+    const int j = it / groups;
+    const int r = (it % groups) * R + rsub;
+    const int e = s_idx[j];
+    if (e < 0) continue;
+    const bool row_ok = r < I;
+    const uint8_t* rec = a.bank + (size_t)e * a.stride;
+    const float tg = global_factor(*reinterpret_cast<const float*>(rec + a.g[0]));
+    const float tu = global_factor(*reinterpret_cast<const float*>(rec + a.g[1]));
+    const uint8_t* cg = rec + a.codes[0] + (size_t)(row_ok ? r : 0) * (H / 2);
+    const uint8_t* sg = rec + a.scales[0] + (size_t)(row_ok ? r : 0) * (H / 16);
+    const uint8_t* cu = rec + a.codes[1] + (size_t)(row_ok ? r : 0) * (H / 2);
+    const uint8_t* su = rec + a.scales[1] + (size_t)(row_ok ? r : 0) * (H / 16);
+    float ag = 0.0f, au = 0.0f;
+    for (int qb = 0; qb < nquads; qb += G * QB) {
+      Quad vg[QB], vu[QB];
+#pragma unroll
+      for (int i = 0; i < QB; i++) {
+        const int qd = qb + sub + G * i;
+        if (row_ok && qd < nquads) {
+          vg[i] = load_quad(cg, sg, qd);
+          vu[i] = load_quad(cu, su, qd);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < QB; i++) {
+        const int qd = qb + sub + G * i;
+        if (row_ok && qd < nquads) {
+#pragma unroll
+          for (int b = 0; b < 4; b++) {
+            uint32_t xw[8];
+            load_x8(xs, qd, b, xw);
+            ag = fmaf(quad_scale(vg[i], b) * tg,
+                      block_dot16(quad_word(vg[i], 2 * b), quad_word(vg[i], 2 * b + 1), xw), ag);
+            au = fmaf(quad_scale(vu[i], b) * tu,
+                      block_dot16(quad_word(vu[i], 2 * b), quad_word(vu[i], 2 * b + 1), xw), au);
+          }
+        }
+      }
+    }
+    const float g = group_sum<G>(ag), u = group_sum<G>(au);
+    if (sub == 0 && row_ok) a.mid[(size_t)j * I + r] = f32_to_bf16(silu_mul(g, u));
+  }
+}
+
+__global__ __launch_bounds__(kDecThreads) void flat_down_kernel(FlatArgs a) {
+  constexpr int G = 8, R = 64 / G, QB = 5;
+  extern __shared__ uint32_t ms[];  // [k][I/2]
+  __shared__ int s_idx[kFlatDecodeMaxK];
+  __shared__ float s_w[kFlatDecodeMaxK];
+  __shared__ float s_d[kFlatDecodeMaxK][R];
+  const int H = a.H, I = a.I, k = a.k, nquads = I / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rsub = lane / G, sub = lane % G;
+  const int r = blockIdx.x * R + rsub;
+  const bool row_ok = r < H;
+  if (threadIdx.x < k) {
+    const int e = a.idx[threadIdx.x];
+    s_idx[threadIdx.x] = (e >= 0 && e < a.E) ? e : -1;
+    s_w[threadIdx.x] = a.w[threadIdx.x];
+  }
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.mid);
+    u32x4* dst = reinterpret_cast<u32x4*>(ms);
+    for (int i = threadIdx.x; i < k * I / 8; i += kDecThreads) dst[i] = src[i];
+  }
+  __syncthreads();
+  for (int j = wave; j < k; j += kDecWaves) {
+    const int e = s_idx[j];
+    float ad = 0.0f;
+    if (e >= 0) {
+      const uint8_t* rec = a.bank + (size_t)e * a.stride;
+      const float td = global_factor(*reinterpret_cast<const float*>(rec + a.g[2]));
+      const uint8_t* cd = rec + a.codes[2] + (size_t)(row_ok ? r : 0) * (I / 2);
+      const uint8_t* sd = rec + a.scales[2] + (size_t)(row_ok ? r : 0) * (I / 16);
+      const uint32_t* mrow = ms + (size_t)j * (I / 2);
+      for (int qb = 0; qb < nquads; qb += G * QB) {
+        Quad vd[QB];
+#pragma unroll
+        for (int i = 0; i < QB; i++) {
+          const int qd = qb + sub + G * i;
+          if (row_ok && qd < nquads) vd[i] = load_quad(cd, sd, qd);
+        }
+#pragma unroll
+        for (int i = 0; i < QB; i++) {
+          const int qd = qb + sub + G * i;
+          if (row_ok && qd < nquads) {
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+              uint32_t xw[8];
+              load_x8(mrow, qd, b, xw);
+              ad = fmaf(quad_scale(vd[i], b) * td,
+                        block_dot16(quad_word(vd[i], 2 * b), quad_word(vd[i], 2 * b + 1), xw), ad);
+            }
+          }
+        }
+      }
+    }
+    const float d = group_sum<G>(ad);
+    if (sub == 0) s_d[j][rsub] = (e >= 0) ? s_w[j] * d : 0.0f;
+  }
+  __syncthreads();
+  if (threadIdx.x < R) {
+    const int rr = blockIdx.x * R + threadIdx.x;
+    if (rr < H) {
+      float acc = a.residual ? bf16_to_f32(a.residual[rr]) : 0.0f;
+      for (int j = 0; j < k; j++) acc += s_d[j][threadIdx.x];  // slot order
+      if (a.f32_out)
+        reinterpret_cast<float*>(a.y)[rr] = acc;
+      else
+        reinterpret_cast<uint16_t*>(a.y)[rr] = f32_to_bf16(acc);
+    }
+  }
+}
+
+static int flat_blocks(int n_items) {
+  // enough waves for about two items each; the grid never exceeds what the
+  // items need
+  int b = env_int("MOE_FLAT_GATEUP_BLOCKS", 0);
+  if (b <= 0) b = (n_items + 2 * kDecWaves - 1) / (2 * kDecWaves);
+  return b < 1 ? 1 : b;
+}
+
+hipError_t launch_flat_decode(const BankView& b, const uint16_t* x, const int32_t* idx,
+                              const float* w, int k, const uint16_t* residual, uint16_t* mid,
+                              void* y, bool f32_out, hipStream_t s) {
+  FlatArgs a{};
+  a.bank = b.base;
+  a.stride = b.stride;
+  for (int p = 0; p < 3; p++) {
+    a.codes[p] = b.codes[p];
+    a.scales[p] = b.scales[p];
+    a.g[p] = b.g[p];
+  }
+  a.H = b.H;
+  a.I = b.I;
+  a.E = b.E;
+  a.k = k;
+  a.idx = idx;
+  a.w = w;
+  a.x = x;
+  a.residual = residual;
+  a.mid = mid;
+  a.y = y;
+  a.f32_out = f32_out ? 1 : 0;
+  const int groups = (b.I + 3) / 4;
+  prof_begin("decode_gateup", s);
+  hipLaunchKernelGGL(flat_gateup_kernel, dim3(flat_blocks(k * groups)), dim3(kDecThreads),
+                     (size_t)b.H * 2, s, a);
+  prof_end("decode_gateup", s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  prof_begin("decode_down", s);
+  hipLaunchKernelGGL(flat_down_kernel, dim3((b.H + 7) / 8), dim3(kDecThreads),
+                     (size_t)k * b.I * 2, s, a);
   prof_end("decode_down", s);
   return hipGetLastError();
 }

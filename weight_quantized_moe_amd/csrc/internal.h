@@ -23,24 +23,38 @@ struct RouteTables {
   int32_t* tile_row0;   // [max_tiles] first sorted slot of the tile
 };
 
-// router: partial logits over chunks of H, reduced in the top-k kernel
-constexpr int kRouterRows = 64;   // H rows per router block
-constexpr int kRouterTok = 8;     // tokens per router block
-hipError_t launch_router_partial(const uint16_t* x, const float* Wr, float* partial, int T, int H,
-                                 int E, hipStream_t s);
-// top-k + softmax, one wave per token; partial == nullptr: logits are the input
-hipError_t launch_topk(const float* partial, int nchunk, float* logits, int T, int E, int k,
-                       int32_t* idx, float* w, hipStream_t s);
+// router: logits = x . Wr^T with Wr f32 [E][H]; one block per (expert, 8 tokens)
+constexpr int kRouterTok = 8;
+hipError_t launch_router(const uint16_t* x, const float* Wr, float* logits, int T, int H, int E,
+                         hipStream_t s);
+// top-k + softmax over given logits, one block per token
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                       hipStream_t s);
 // stable counting sort of the T*k pairs; also the active list and, when
 // mtile > 0, the grouped-GEMM tile table (tiles of mtile sorted slots)
 hipError_t launch_sort(const int32_t* idx, int P, int E, RouteTables rt, int mtile, int max_tiles,
                        hipStream_t s);
 
-// expert-streaming (GEMV) kernels
-hipError_t launch_decode_gateup(const BankView& b, const uint16_t* x, int k, const RouteTables& rt,
-                                int slots, uint16_t* mid, hipStream_t s);
-hipError_t launch_decode_down(const BankView& b, const uint16_t* mid, const float* w, int k,
-                              const RouteTables& rt, int slots, float* part, hipStream_t s);
+// expert-streaming (GEMV) kernels. rt == nullptr: each block finds its
+// expert (the slot-th smallest present in idx) and that expert's pairs itself,
+// which needs P <= kDecInblockMaxP; else the sorted tables are used. mid and part
+// are indexed by pair id. max_m: the expected largest pair count of one
+// expert, a hint only (1 picks the single-token kernels, which still loop
+// over any number of pairs).
+constexpr int kDecInblockMaxP = 256;
+hipError_t launch_decode_gateup(const BankView& b, const uint16_t* x, const int32_t* idx, int P, int k,
+                                const RouteTables* rt, int slots, int max_m, uint16_t* mid,
+                                hipStream_t s);
+hipError_t launch_decode_down(const BankView& b, const uint16_t* mid, const float* w,
+                              const int32_t* idx, int P, int k, const RouteTables* rt, int slots,
+                              int max_m, float* part, hipStream_t s);
+// one token (T = 1, k <= kFlatDecodeMaxK, k * I * 2 <= 64 KiB of mids in
+// LDS): gate/up then down with the combine folded in; mid [k][I] is scratch,
+// y [H] the layer output
+constexpr int kFlatDecodeMaxK = 16;
+hipError_t launch_flat_decode(const BankView& b, const uint16_t* x, const int32_t* idx,
+                              const float* w, int k, const uint16_t* residual, uint16_t* mid,
+                              void* y, bool f32_out, hipStream_t s);
 // y[t] = residual[t] + sum_j part[t*k+j] (j ascending); pairs with idx
 // outside [0, E) contribute nothing
 hipError_t launch_combine(const float* part, const int32_t* idx, int E, int T, int H, int k,

@@ -12,137 +12,123 @@
 
 namespace moe {
 
-// ---- S1: partial logits ----------------------------------------------------
-// Block (chunk c, token group tg): rows h in [64c, 64c+64) of Wr, up to 8
-// tokens. Thread j owns experts j, j+256, j+512, j+768. Each Wr row is read
-// once per block with coalesced 4-byte loads (1 KiB per row at E = 256); the x
-// values are uniform across the block. Output partial[c][t][e] (f32); the
-// top-k kernel sums the chunks in ascending order, so logits are deterministic.
-__global__ __launch_bounds__(256) void router_partial_kernel(const uint16_t* __restrict__ x,
-                                                             const float* __restrict__ Wr,
-                                                             float* __restrict__ partial, int T,
-                                                             int H, int E) {
-  const int c = blockIdx.x, t0 = blockIdx.y * kRouterTok;
+// ---- S1: router logits --------------------------------------------------------
+// Router weights are f32 [E][H], one contiguous row per expert. Block
+// (expert e, token group) computes the whole dot product of that row with up
+// to 8 token rows: thread j reads 16-byte pieces h = 4j, 4j + 1024, ... of the
+// row (coalesced) and the matching x values; the sum is reduced in the wave,
+// then over the 4 waves in wave order. One block per expert keeps every CU
+// busy at E = 256 without partial sums across blocks.
+__global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict__ x,
+                                                     const float* __restrict__ Wr,
+                                                     float* __restrict__ logits, int T, int H,
+                                                     int E) {
+  const int e = blockIdx.x, t0 = blockIdx.y * kRouterTok;
   const int nt = min(kRouterTok, T - t0);
-  const int h0 = c * kRouterRows, h1 = min(H, h0 + kRouterRows);
-  __shared__ float xs[kRouterTok][kRouterRows];
-  for (int i = threadIdx.x; i < kRouterTok * kRouterRows; i += blockDim.x) {
-    int tt = i / kRouterRows, hh = i % kRouterRows;
-    xs[tt][hh] = (tt < nt && h0 + hh < h1) ? bf16_to_f32(x[(size_t)(t0 + tt) * H + h0 + hh]) : 0.0f;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ float red[4][kRouterTok];
+  float acc[kRouterTok];
+#pragma unroll
+  for (int tt = 0; tt < kRouterTok; tt++) acc[tt] = 0.0f;
+  const float* row = Wr + (size_t)e * H;
+  for (int h = 4 * threadIdx.x; h < H; h += 1024) {
+    const f32x4 wv = *reinterpret_cast<const f32x4*>(row + h);
+#pragma unroll
+    for (int tt = 0; tt < kRouterTok; tt++) {
+      if (tt < nt) {
+        const u32x2 xv = *reinterpret_cast<const u32x2*>(x + (size_t)(t0 + tt) * H + h);
+        acc[tt] = fmaf(bf16_to_f32(xv.x & 0xFFFFu), wv.x, acc[tt]);
+        acc[tt] = fmaf(bf16_to_f32(xv.x >> 16), wv.y, acc[tt]);
+        acc[tt] = fmaf(bf16_to_f32(xv.y & 0xFFFFu), wv.z, acc[tt]);
+        acc[tt] = fmaf(bf16_to_f32(xv.y >> 16), wv.w, acc[tt]);
+      }
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < kRouterTok; tt++) {
+    const float s = wave_sum(acc[tt]);
+    if (lane == 0) red[wave][tt] = s;
   }
   __syncthreads();
-  float acc[kRouterTok][4];
-#pragma unroll
-  for (int tt = 0; tt < kRouterTok; tt++)
-#pragma unroll
-    for (int q = 0; q < 4; q++) acc[tt][q] = 0.0f;
-  for (int h = h0; h < h1; h++) {
-    const float* wrow = Wr + (size_t)h * E;
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-      int e = threadIdx.x + 256 * q;
-      float wv = (e < E) ? wrow[e] : 0.0f;
-#pragma unroll
-      for (int tt = 0; tt < kRouterTok; tt++) acc[tt][q] = fmaf(xs[tt][h - h0], wv, acc[tt][q]);
-    }
+  if (threadIdx.x < nt) {
+    const int tt = threadIdx.x;
+    logits[(size_t)(t0 + tt) * E + e] = ((red[0][tt] + red[1][tt]) + red[2][tt]) + red[3][tt];
   }
-  for (int tt = 0; tt < nt; tt++)
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-      int e = threadIdx.x + 256 * q;
-      if (e < E) partial[((size_t)c * T + t0 + tt) * E + e] = acc[tt][q];
-    }
 }
 
-hipError_t launch_router_partial(const uint16_t* x, const float* Wr, float* partial, int T, int H,
-                                 int E, hipStream_t s) {
-  dim3 grid((H + kRouterRows - 1) / kRouterRows, (T + kRouterTok - 1) / kRouterTok);
+hipError_t launch_router(const uint16_t* x, const float* Wr, float* logits, int T, int H, int E,
+                         hipStream_t s) {
+  dim3 grid(E, (T + kRouterTok - 1) / kRouterTok);
   prof_begin("router", s);
-  hipLaunchKernelGGL(router_partial_kernel, grid, dim3(256), 0, s, x, Wr, partial, T, H, E);
+  hipLaunchKernelGGL(router_kernel, grid, dim3(256), 0, s, x, Wr, logits, T, H, E);
   prof_end("router", s);
   return hipGetLastError();
 }
 
-// ---- S2: top-k + softmax, one wave64 per token --------------------------------
-// Ordering key: larger logit first, then lower expert index; NaN ranks below
-// every number; -0 and +0 compare equal (IEEE comparison).
-__device__ __forceinline__ bool better(float a, int ea, float b, int eb) {
-  bool na = a != a, nb = b != b;
-  if (na != nb) return nb;  // the non-NaN one wins
-  if (!na && a != b) return a > b;
-  return ea < eb;
+// ---- S2: top-k + softmax ------------------------------------------------------
+// Order: larger logit first, then lower expert index; -0 and +0 are equal; a
+// NaN ranks below every number. Each logit becomes an unsigned key that
+// preserves that order, and candidate e's rank is the number of candidates
+// ahead of it. One block of 1024 threads per token: thread (candidate slot c,
+// quarter q) counts the candidates of quarter q that are ahead of the
+// candidates c, c+256, ...; the four partial counts are added in LDS. The k
+// candidates with rank < k are the top-k in order; the softmax over them is
+// f32, summed in slot order.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t b = __float_as_uint(v);
+  if ((b & 0x7FFFFFFFu) == 0) b = 0;                     // -0 -> +0
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0;        // NaN: below everything
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);    // monotone in v
 }
 
-constexpr int kTopkMaxPerLane = 16;  // E <= 1024
-
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ partial, int nchunk,
-                                                   float* __restrict__ logits, int T, int E, int k,
-                                                   int32_t* __restrict__ idx, float* __restrict__ w) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  float v[kTopkMaxPerLane];
-  const int per = (E + 63) / 64;
-#pragma unroll
-  for (int i = 0; i < kTopkMaxPerLane; i++) {
-    int e = lane + 64 * i;
-    float a = -__builtin_inff();
-    if (i < per && e < E) {
-      if (partial) {
-        a = 0.0f;
-        for (int c = 0; c < nchunk; c++) a += partial[((size_t)c * T + t) * E + e];
-        logits[(size_t)t * E + e] = a;
-      } else {
-        a = logits[(size_t)t * E + e];
-      }
+__global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                    int k, int32_t* __restrict__ idx,
+                                                    float* __restrict__ w) {
+  const int t = blockIdx.x;
+  __shared__ uint32_t key[1024];
+  __shared__ uint16_t prank[4][1024];
+  __shared__ float sel_v[64];
+  __shared__ int sel_e[64];
+  const float* lt = logits + (size_t)t * E;
+  for (int e = threadIdx.x; e < E; e += 1024) key[e] = order_key(lt[e]);
+  __syncthreads();
+  const int c = threadIdx.x & 255, q = threadIdx.x >> 8;
+  const int j0 = q * E / 4, j1 = (q + 1) * E / 4;
+  for (int e = c; e < E; e += 256) {
+    const uint32_t ke = key[e];
+    int n = 0;
+    for (int j = j0; j < j1; j++) {
+      const uint32_t kj = key[j];
+      n += (kj > ke || (kj == ke && j < e)) ? 1 : 0;
     }
-    v[i] = a;
+    prank[q][e] = (uint16_t)n;
   }
-  uint32_t taken = 0;  // bit i: candidate i of this lane already selected
-  float top0 = 0.0f, sel_v = 0.0f;
-  int sel_e = 0;
-  for (int j = 0; j < k; j++) {
-    float bv = 0.0f;
-    int be = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < kTopkMaxPerLane; i++) {
-      int e = lane + 64 * i;
-      if (i < per && e < E && !((taken >> i) & 1u) && (be == 0x7FFFFFFF || better(v[i], e, bv, be))) {
-        bv = v[i];
-        be = e;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      float ov = __shfl_xor(bv, o, 64);
-      int oe = __shfl_xor(be, o, 64);
-      if (oe != 0x7FFFFFFF && (be == 0x7FFFFFFF || better(ov, oe, bv, be))) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (j == 0) top0 = bv;
-    if (lane == j) {
-      sel_v = bv;
-      sel_e = be;
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    const int rank = prank[0][e] + prank[1][e] + prank[2][e] + prank[3][e];
+    if (rank < k) {
+      sel_v[rank] = lt[e];
+      sel_e[rank] = e;
     }
   }
-  // softmax over the k selected logits, f32, summed in slot order
-  float a = (lane < k) ? expf(sel_v - top0) : 0.0f;
-  float sum = 0.0f;
-  for (int j = 0; j < k; j++) sum += __shfl(a, j, 64);
-  if (lane < k) {
-    idx[(size_t)t * k + lane] = sel_e;
-    w[(size_t)t * k + lane] = a / sum;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const float top0 = sel_v[0];
+    const float a = (lane < k) ? expf(sel_v[lane] - top0) : 0.0f;
+    float sum = 0.0f;
+    for (int j = 0; j < k; j++) sum += __shfl(a, j, 64);
+    if (lane < k) {
+      idx[(size_t)t * k + lane] = sel_e[lane];
+      w[(size_t)t * k + lane] = a / sum;
+    }
   }
 }
 
-hipError_t launch_topk(const float* partial, int nchunk, float* logits, int T, int E, int k,
-                       int32_t* idx, float* w, hipStream_t s) {
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                       hipStream_t s) {
   prof_begin("topk", s);
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, partial, nchunk, logits, T,
-                     E, k, idx, w);
+  hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(1024), 0, s, logits, T, E, k, idx, w);
   prof_end("topk", s);
   return hipGetLastError();
 }
@@ -166,7 +152,7 @@ __global__ __launch_bounds__(kSortThreads) void sort_kernel(const int32_t* __res
   __shared__ uint16_t wcnt[kSortWaves][kMaxE];
   __shared__ int scan_tmp[kSortThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < kMaxE; e += kSortThreads) {
+  for (int e = tid; e < E; e += kSortThreads) {
     cnt[e] = 0;
     for (int wv = 0; wv < kSortWaves; wv++) wcnt[wv][e] = 0;
   }
