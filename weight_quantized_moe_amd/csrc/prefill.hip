@@ -14,15 +14,25 @@
 // follow "Beam-1.0-501B-A23B VQ GGUF" ("What stays native", "Kernel budget on
 // GB10").
 //
-// Data paths. B never touches LDS: in the 32x32x16 layout lane l supplies
-// 8 consecutive inputs of weight row l%32, which is one U32 word of codes, so
-// every lane loads its own codes and scales from HBM and dequantizes them in
-// registers right before the MFMA that uses them. The inputs of a 64-wide k
-// step are assigned to the MFMA's four k-slices so that lane half h = l/32
-// takes inputs 32h..32h+31 (four words, one 16-byte load per row); the A
-// operand uses the same assignment, which only permutes the order of the sum.
-// A (activation rows, shared by the 4 waves) goes through a double-buffered
-// LDS tile.
+// Data paths. Every load of the k loop goes from HBM straight into LDS
+// (global_load_lds_dwordx4: lane l's 16 bytes land at a wave-uniform LDS base
+// + 16 l), so no registers hold data in flight, and each wave-wide load covers
+// whole 64- or 128-byte row segments (the texture unit's cost grows with the
+// number of distinct rows a load touches, not with its bytes):
+//   A    the tile's 128 activation rows, 128 bytes (64 inputs) per row and step,
+//        8 rows per load, double-buffered and shared by the 4 waves;
+//   B    each wave's 64 weight rows, 64 bytes of codes (two steps) per row,
+//        16 rows per load, double-buffered, private to the wave;
+//   S    each wave's 64 rows' scales, 16 bytes (four steps) per row, one row
+//        per lane, double-buffered, private to the wave.
+// 16-byte pieces are stored XOR-swizzled within their row so the fragment
+// reads of 16 consecutive rows fall in distinct banks. The B operand is
+// dequantized in registers right before the MFMA: in the 32x32x16 layout lane
+// l supplies 8 consecutive inputs of weight row l%32, one U32 word of codes.
+// The inputs of a 64-wide k step are assigned to the MFMA's four k-slices so
+// that lane half h = l/32 takes inputs 32h..32h+31 (one 16-byte piece of codes
+// per row); the A operand uses the same assignment, which only permutes the
+// order of the sum.
 #include "common.h"
 #include "internal.h"
 
@@ -31,7 +41,9 @@ namespace moe {
 constexpr int kPM = kPrefillMTile;  // 128 sorted slots per tile
 constexpr int kWR = 64;             // weight rows per wave
 constexpr int kPK = 64;             // inputs per k step
-constexpr int kLdsRow = kPK + 8;    // bf16 per LDS row (16-byte pad against bank conflicts)
+constexpr int kABuf = kPM * kPK * 2;          // bytes of one A tile (16 KiB)
+constexpr int kBStage = kWR * kPK;            // bytes of one wave's codes for two k steps (4 KiB)
+constexpr int kSGroup = kWR * 16;             // bytes of one wave's scales for four k steps (1 KiB)
 
 struct PrefillArgs {
   const uint8_t* bank;
@@ -45,43 +57,75 @@ struct PrefillArgs {
   float* part;
 };
 
-// One k step of this thread's A half row (32 bf16 = 4 blocks of 8).
-struct ARegs {
-  u32x4 q[4];
-};
-// One k step of this lane's two weight rows: 32 codes (16 bytes) and the
-// row's 4 scale bytes of the step, for each row.
-struct BRegs {
-  u32x4 c[2];
-  uint32_t s[2];
-};
+// One wave-wide HBM -> LDS load (global_load_lds_dwordx4): lane l's 16 bytes
+// at base + voff land at LDS byte address lds + 16 l; base and lds are
+// wave-uniform. Issued from inline asm so the compiler's wait insertion does
+// not make every later LDS access and barrier wait for it: the k loop waits
+// for its loads itself (wait_vmcnt) before the barrier that publishes them.
+// The instruction writes no registers. The loop issues no other vector-memory
+// loads, so vmcnt counts exactly these.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(lds)
+               : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ const uint8_t* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint8_t*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+}
+
+// s_waitcnt vmcnt(n) alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier after this wave's LDS accesses have completed. No memory
+// fence: a fence would also wait for every HBM -> LDS load in flight. The
+// asm statement keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void step_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// 16-byte slot of piece j in A row r (8 pieces per row)
+__device__ __forceinline__ int a_slot(int r, int j) { return j ^ ((r & 7) ^ ((r >> 3) & 1)); }
+// 16-byte slot of piece c in B row r (4 pieces per row)
+__device__ __forceinline__ int b_slot(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
 
 struct TileCtx {
-  const uint16_t* a_ptr;  // A half row of this thread at k = 0
-  const uint8_t* bc[2];   // codes of this lane's rows at k = 0, offset by lane half
-  const uint8_t* bs[2];   // scales of this lane's rows at k = 0
+  const uint8_t* in;      // A matrix (bytes), uniform
+  const uint8_t* rec;     // the expert's record, uniform
+  uint32_t a_off[4];      // byte offsets in A of this lane's pieces at k = 0, loads i = 0..3
+  uint32_t b_off[4];      // byte offsets in the record of this lane's code pieces at k = 0
+  uint32_t s_off;         // byte offset in the record of weight row (wave row = lane)'s scales at k = 0
+  uint32_t a_lds[2];      // this wave's LDS bases for its A loads (rows 32w..), per A tile
+  uint32_t b_lds[2];      // the wave's code stages
+  uint32_t s_lds[2];      // the wave's scale groups
 };
 
-__device__ __forceinline__ void load_a(const TileCtx& c, int ks, ARegs& r) {
-  const u32x4* s = reinterpret_cast<const u32x4*>(c.a_ptr + ks * kPK);
+// A of step ks -> A tile t: the wave loads rows 32w + 8i + l/8 (i = 0..3).
+__device__ __forceinline__ void dma_a(const TileCtx& c, int ks, int t) {
 #pragma unroll
-  for (int q = 0; q < 4; q++) r.q[q] = s[q];
+  for (int i = 0; i < 4; i++) dma16(c.in + ks * (kPK * 2), c.a_off[i], c.a_lds[t] + 1024 * i);
 }
-
-__device__ __forceinline__ void load_b(const TileCtx& c, int ks, BRegs& r) {
+// codes of stage g (k steps 2g, 2g+1) -> the wave's stage buffer t
+__device__ __forceinline__ void dma_b(const TileCtx& c, int g, int t) {
 #pragma unroll
-  for (int f = 0; f < 2; f++) {
-    r.c[f] = *reinterpret_cast<const u32x4*>(c.bc[f] + ks * (kPK / 2));
-    r.s[f] = *reinterpret_cast<const uint32_t*>(c.bs[f] + ks * (kPK / 16));
-  }
+  for (int i = 0; i < 4; i++) dma16(c.rec + g * 64, c.b_off[i], c.b_lds[t] + 1024 * i);
 }
-
-// LDS row layout: input block j (8 bf16) of a k step sits at position
-// 2 (j % 4) + j / 4, so that the fragment of k-slice kk for lane half h
-// (block 4h + kk) is at element 16 kk + 8 h.
-__device__ __forceinline__ void write_a_q(uint16_t* As, const ARegs& r, int q) {
-  const int tid = threadIdx.x, row = tid >> 1, h = tid & 1;
-  *reinterpret_cast<u32x4*>(As + row * kLdsRow + 8 * (2 * q + h)) = r.q[q];
+// scales of group G (k steps 4G..4G+3) -> the wave's group buffer t
+__device__ __forceinline__ void dma_s(const TileCtx& c, int G, int t) {
+  dma16(c.rec + G * 16, c.s_off, c.s_lds[t]);
 }
 
 // word of 8 E2M1 codes -> 8 bf16 unit values e2m1 * e4m3 (exact)
@@ -93,55 +137,61 @@ __device__ __forceinline__ bf16x8 deq8(uint32_t word, float sb) {
   return __builtin_bit_cast(bf16x8, o);
 }
 
-// The MFMAs of one k step: A from LDS tile As, B from registers b; the next
-// step's A (regs aw) is written to LDS tile As2 along the way.
-__device__ __forceinline__ void step_mfma(const uint16_t* As, const BRegs& b, f32x16 (&acc)[4][2],
-                                          const ARegs& aw, uint16_t* As2) {
-  const int lane = threadIdx.x & 63, h = lane >> 5;
+// The MFMAs of one k step. As: A tile; Bs: the wave's code stage, half t;
+// Ss: the wave's scale group, step q within it.
+__device__ __forceinline__ void step_mfma(const uint8_t* As, const uint8_t* Bs, int t, const uint8_t* Ss, int q,
+                                          f32x16 (&acc)[4][2]) {
+  const int lane = threadIdx.x & 63, h = lane >> 5, n = lane & 31;
+  u32x4 bc[2];
   float sb[2][2];
 #pragma unroll
   for (int f = 0; f < 2; f++) {
-    const uint32_t sw = b.s[f] >> (16 * h);  // scale bytes 2h, 2h+1: inputs 32h..32h+15, +16..+31
-    sb[f][0] = e4m3_f32<0>(sw);
-    sb[f][1] = e4m3_f32<1>(sw);
+    const int r = 32 * f + n;
+    bc[f] = *reinterpret_cast<const u32x4*>(Bs + r * 64 + 16 * b_slot(r, 2 * t + h));
+    // scale bytes 2h, 2h+1 of the step: inputs 32h..32h+15 and +16..+31
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(Ss + r * 16 + 4 * q) >> (16 * h);
+    sb[f][0] = e4m3_f32<0>(v);
+    sb[f][1] = e4m3_f32<1>(v);
   }
 #pragma unroll
   for (int kk = 0; kk < 4; kk++) {
     bf16x8 af[4], bfr[2];
 #pragma unroll
-    for (int ms = 0; ms < 4; ms++)
-      af[ms] = *reinterpret_cast<const bf16x8*>(As + (32 * ms + (lane & 31)) * kLdsRow + 16 * kk + 8 * h);
+    for (int ms = 0; ms < 4; ms++) {
+      const int r = 32 * ms + n;
+      af[ms] = *reinterpret_cast<const bf16x8*>(As + r * 128 + 16 * a_slot(r, 4 * h + kk));
+    }
 #pragma unroll
-    for (int f = 0; f < 2; f++) bfr[f] = deq8(b.c[f][kk], sb[f][kk >> 1]);
+    for (int f = 0; f < 2; f++) bfr[f] = deq8(bc[f][kk], sb[f][kk >> 1]);
 #pragma unroll
     for (int ms = 0; ms < 4; ms++)
 #pragma unroll
       for (int f = 0; f < 2; f++)
         acc[ms][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bfr[f], acc[ms][f], 0, 0, 0);
-    if (kk >= 2) {
-      write_a_q(As2, aw, 2 * (kk - 2));
-      write_a_q(As2, aw, 2 * (kk - 2) + 1);
-    }
   }
 }
 
-// Step s of the k loop (I = s mod 6 picks the register sets): loads of step
-// s+2 are issued (A into the set that held step s, B into the set that held
-// step s-1), the MFMAs of step s run on LDS tile s%2 and B set s%3 while
-// step s+1's A is written to LDS tile (s+1)%2; one barrier.
+// Step s of the k loop, I = s mod 8. Issue order (the waits count on it):
+// A of step s+1 into A tile (s+1)%2 (4 loads); on even steps the codes of
+// the next stage (4 loads); every fourth step the scales of the next group
+// (1 load). Then the MFMAs of step s. Before the barrier, wait until A of
+// step s+1 has landed: only this step's later loads may still be in flight,
+// which on odd steps means none, so the codes issued on the step before are
+// in too. Buffers written here were last read on the step before, which
+// every wave has finished (barrier). Loads past the last step repeat it
+// (they go to buffers never read again).
 template <int I>
-__device__ __forceinline__ void kstep(const TileCtx& c, int s, int nk, uint16_t* L0, uint16_t* L1,
-                                      ARegs& a0, ARegs& a1, BRegs& b0, BRegs& b1, BRegs& b2,
+__device__ __forceinline__ void kstep(const TileCtx& c, int s, int nk, const uint8_t* A0, const uint8_t* A1,
+                                      const uint8_t* B0, const uint8_t* B1, const uint8_t* S0, const uint8_t* S1,
                                       f32x16 (&acc)[4][2]) {
-  const int ld = min(s + 2, nk - 1);  // past the end: reload the last step (never used)
-  ARegs& a_ld = (I % 2 == 0) ? a0 : a1;
-  ARegs& a_wr = (I % 2 == 0) ? a1 : a0;
-  BRegs& b_ld = ((I + 2) % 3 == 0) ? b0 : ((I + 2) % 3 == 1) ? b1 : b2;
-  BRegs& b_use = (I % 3 == 0) ? b0 : (I % 3 == 1) ? b1 : b2;
-  load_a(c, ld, a_ld);
-  load_b(c, ld, b_ld);
-  step_mfma((I % 2 == 0) ? L0 : L1, b_use, acc, a_wr, (I % 2 == 0) ? L1 : L0);
-  __syncthreads();
+  dma_a(c, min(s + 1, nk - 1), (I + 1) % 2);
+  if (I % 2 == 0) dma_b(c, min(s / 2 + 1, (nk - 1) / 2), (I / 2 + 1) % 2);
+  if (I % 4 == 0) dma_s(c, min(s / 4 + 1, (nk - 1) / 4), (I / 4 + 1) % 2);
+  __builtin_amdgcn_sched_barrier(0);
+  step_mfma((I % 2) ? A1 : A0, ((I / 2) % 2) ? B1 : B0, I % 2, ((I / 4) % 2) ? S1 : S0, I % 4, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<((I % 2 == 0) ? 4 : 0) + ((I % 4 == 0) ? 1 : 0)>();
+  step_barrier();
 }
 
 // NPROJ = 2: gate and up (wave w: gate rows n0+32w.. and the same up rows, for
@@ -149,7 +199,7 @@ __device__ __forceinline__ void kstep(const TileCtx& c, int s, int nk, uint16_t*
 // (wave w: rows n0+64w.., 256 output columns per tile), routing-weighted f32
 // rows into part.
 //
-// Two workgroups share a CU (at most 256 registers per lane, 37 KB of LDS
+// Two workgroups share a CU (at most 256 registers per lane, 73 KB of LDS
 // each), so one workgroup's MFMAs cover the other's loads and barriers.
 //
 // Work mapping: the hardware hands out workgroups round-robin over the 8
@@ -181,31 +231,67 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   const int row0 = a.rt.tile_row0[tile];
   const int rows = min(kPM, e_hi - row0);
   const int n0 = (local / ce) * ncol;
-  const uint8_t* rec = a.bank + (size_t)e * a.stride;
   const int p0 = (NPROJ == 2) ? 0 : 2;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kPM * kLdsRow];
+  // separate arrays per buffer
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a0[kABuf];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a1[kABuf];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b0[4 * kBStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b1[4 * kBStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_s0[4 * kSGroup];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_s1[4 * kSGroup];
   __shared__ int src_row[kPM];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (tid < kPM) {
     // rows past the tile's end read a valid stand-in row; their outputs are not stored
     const int r = min(tid, rows - 1);
     src_row[tid] = (NPROJ == 2) ? a.rt.sorted[row0 + r] / a.k : row0 + r;
   }
+  TileCtx c;
+  c.in = uniform_ptr(a.in);
+  c.rec = uniform_ptr(a.bank + (size_t)e * a.stride);
   float t_p[NPROJ];
 #pragma unroll
-  for (int q = 0; q < NPROJ; q++) t_p[q] = global_factor(*reinterpret_cast<const float*>(rec + a.g[p0 + q]));
-  TileCtx c;
+  for (int q = 0; q < NPROJ; q++) t_p[q] = global_factor(*reinterpret_cast<const float*>(c.rec + a.g[p0 + q]));
+  // weight row (output index, projection) of the wave's row r (0..63); rows
+  // past N read row 0 (their outputs are not stored)
+  auto wrow = [&](int r, int& q) {
+    q = (NPROJ == 2) ? (r >> 5) : 0;
+    const int n = (NPROJ == 2) ? n0 + 32 * wave + (r & 31) : n0 + kWR * wave + r;
+    return n < N ? n : 0;
+  };
 #pragma unroll
-  for (int f = 0; f < 2; f++) {
-    // weight row of fragment f for this lane; rows past N read row 0 (outputs not stored)
-    const int q = (NPROJ == 2) ? f : 0;
-    int n = (NPROJ == 2) ? n0 + 32 * wave + (lane & 31) : n0 + kWR * wave + 32 * f + (lane & 31);
-    if (n >= N) n = 0;
-    c.bc[f] = rec + a.codes[p0 + q] + (size_t)n * (K / 2) + 16 * h;
-    c.bs[f] = rec + a.scales[p0 + q] + (size_t)n * (K / 16);
+  for (int i = 0; i < 4; i++) {
+    const int r = 16 * i + (lane >> 2);
+    int q;
+    const int n = wrow(r, q);
+    const int piece = b_slot(r, lane & 3);  // slot lane&3 of row r holds this piece
+    c.b_off[i] = (uint32_t)(a.codes[p0 + q] + (size_t)n * (K / 2) + 16 * piece);
   }
+  {
+    int q;
+    const int n = wrow(lane, q);
+    c.s_off = (uint32_t)(a.scales[p0 + q] + (size_t)n * (K / 16));
+  }
+  const uint8_t* const A0 = lds_a0;
+  const uint8_t* const A1 = lds_a1;
+  const uint8_t* const B0 = lds_b0 + wave * kBStage;
+  const uint8_t* const B1 = lds_b1 + wave * kBStage;
+  const uint8_t* const S0 = lds_s0 + wave * kSGroup;
+  const uint8_t* const S1 = lds_s1 + wave * kSGroup;
+  c.a_lds[0] = __builtin_amdgcn_readfirstlane(lds_addr(A0 + 32 * wave * 128));
+  c.a_lds[1] = __builtin_amdgcn_readfirstlane(lds_addr(A1 + 32 * wave * 128));
+  c.b_lds[0] = __builtin_amdgcn_readfirstlane(lds_addr(B0));
+  c.b_lds[1] = __builtin_amdgcn_readfirstlane(lds_addr(B1));
+  c.s_lds[0] = __builtin_amdgcn_readfirstlane(lds_addr(S0));
+  c.s_lds[1] = __builtin_amdgcn_readfirstlane(lds_addr(S1));
   __syncthreads();
-  c.a_ptr = a.in + (size_t)src_row[tid >> 1] * K + 32 * (tid & 1);
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int r = 32 * wave + 8 * i + (lane >> 3);
+    const int piece = a_slot(r, lane & 7);
+    c.a_off[i] = (uint32_t)src_row[r] * (uint32_t)(K * 2) + 16 * piece;
+  }
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -214,31 +300,30 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     for (int f = 0; f < 2; f++) acc[ms][f] = f32x16{};
 
   const int nk = K / kPK;
-  uint16_t* const L0 = lds;
-  uint16_t* const L1 = lds + kPM * kLdsRow;
-  ARegs a0, a1;
-  BRegs b0, b1, b2;
-  load_a(c, 0, a0);
-  load_b(c, 0, b0);
-  load_a(c, min(1, nk - 1), a1);
-  load_b(c, min(1, nk - 1), b1);
-#pragma unroll
-  for (int q = 0; q < 4; q++) write_a_q(L0, a0, q);
-  __syncthreads();
+  dma_a(c, 0, 0);
+  dma_b(c, 0, 0);
+  dma_s(c, 0, 0);
+  wait_vmcnt<0>();
+  step_barrier();
   int s = 0;
-  for (; s + 6 <= nk; s += 6) {
-    kstep<0>(c, s, nk, L0, L1, a0, a1, b0, b1, b2, acc);
-    kstep<1>(c, s + 1, nk, L0, L1, a0, a1, b0, b1, b2, acc);
-    kstep<2>(c, s + 2, nk, L0, L1, a0, a1, b0, b1, b2, acc);
-    kstep<3>(c, s + 3, nk, L0, L1, a0, a1, b0, b1, b2, acc);
-    kstep<4>(c, s + 4, nk, L0, L1, a0, a1, b0, b1, b2, acc);
-    kstep<5>(c, s + 5, nk, L0, L1, a0, a1, b0, b1, b2, acc);
+  for (; s + 8 <= nk; s += 8) {
+    kstep<0>(c, s, nk, A0, A1, B0, B1, S0, S1, acc);
+    kstep<1>(c, s + 1, nk, A0, A1, B0, B1, S0, S1, acc);
+    kstep<2>(c, s + 2, nk, A0, A1, B0, B1, S0, S1, acc);
+    kstep<3>(c, s + 3, nk, A0, A1, B0, B1, S0, S1, acc);
+    kstep<4>(c, s + 4, nk, A0, A1, B0, B1, S0, S1, acc);
+    kstep<5>(c, s + 5, nk, A0, A1, B0, B1, S0, S1, acc);
+    kstep<6>(c, s + 6, nk, A0, A1, B0, B1, S0, S1, acc);
+    kstep<7>(c, s + 7, nk, A0, A1, B0, B1, S0, S1, acc);
   }
-  if (s < nk) kstep<0>(c, s, nk, L0, L1, a0, a1, b0, b1, b2, acc);
-  if (s + 1 < nk) kstep<1>(c, s + 1, nk, L0, L1, a0, a1, b0, b1, b2, acc);
-  if (s + 2 < nk) kstep<2>(c, s + 2, nk, L0, L1, a0, a1, b0, b1, b2, acc);
-  if (s + 3 < nk) kstep<3>(c, s + 3, nk, L0, L1, a0, a1, b0, b1, b2, acc);
-  if (s + 4 < nk) kstep<4>(c, s + 4, nk, L0, L1, a0, a1, b0, b1, b2, acc);
+  if (s < nk) kstep<0>(c, s, nk, A0, A1, B0, B1, S0, S1, acc);
+  if (s + 1 < nk) kstep<1>(c, s + 1, nk, A0, A1, B0, B1, S0, S1, acc);
+  if (s + 2 < nk) kstep<2>(c, s + 2, nk, A0, A1, B0, B1, S0, S1, acc);
+  if (s + 3 < nk) kstep<3>(c, s + 3, nk, A0, A1, B0, B1, S0, S1, acc);
+  if (s + 4 < nk) kstep<4>(c, s + 4, nk, A0, A1, B0, B1, S0, S1, acc);
+  if (s + 5 < nk) kstep<5>(c, s + 5, nk, A0, A1, B0, B1, S0, S1, acc);
+  if (s + 6 < nk) kstep<6>(c, s + 6, nk, A0, A1, B0, B1, S0, S1, acc);
+  wait_vmcnt<0>();  // the loads past the last step
 
   // epilogue; accumulator element r of lane l is (row 8(r/4) + 4(l/32) + r%4,
   // column l%32) of its 32 x 32 block
