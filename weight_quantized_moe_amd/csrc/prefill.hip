@@ -153,21 +153,40 @@ __device__ __forceinline__ void step_mfma(const uint8_t* As, const uint8_t* Bs, 
     sb[f][0] = e4m3_f32<0>(v);
     sb[f][1] = e4m3_f32<1>(v);
   }
+  // software pipeline over the four k-slices: the A fragments and the
+  // dequantized B fragments of slice kk+1 are prepared while the MFMAs of
+  // slice kk run
+  bf16x8 af[4], bfr[2];
+#pragma unroll
+  for (int ms = 0; ms < 4; ms++) {
+    const int r = 32 * ms + n;
+    af[ms] = *reinterpret_cast<const bf16x8*>(As + r * 128 + 16 * a_slot(r, 4 * h));
+  }
+#pragma unroll
+  for (int f = 0; f < 2; f++) bfr[f] = deq8(bc[f][0], sb[f][0]);
 #pragma unroll
   for (int kk = 0; kk < 4; kk++) {
-    bf16x8 af[4], bfr[2];
+    bf16x8 an[4], bn[2];
+    if (kk < 3) {
 #pragma unroll
-    for (int ms = 0; ms < 4; ms++) {
-      const int r = 32 * ms + n;
-      af[ms] = *reinterpret_cast<const bf16x8*>(As + r * 128 + 16 * a_slot(r, 4 * h + kk));
+      for (int ms = 0; ms < 4; ms++) {
+        const int r = 32 * ms + n;
+        an[ms] = *reinterpret_cast<const bf16x8*>(As + r * 128 + 16 * a_slot(r, 4 * h + kk + 1));
+      }
+#pragma unroll
+      for (int f = 0; f < 2; f++) bn[f] = deq8(bc[f][kk + 1], sb[f][(kk + 1) >> 1]);
     }
-#pragma unroll
-    for (int f = 0; f < 2; f++) bfr[f] = deq8(bc[f][kk], sb[f][kk >> 1]);
 #pragma unroll
     for (int ms = 0; ms < 4; ms++)
 #pragma unroll
       for (int f = 0; f < 2; f++)
         acc[ms][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bfr[f], acc[ms][f], 0, 0, 0);
+    if (kk < 3) {
+#pragma unroll
+      for (int ms = 0; ms < 4; ms++) af[ms] = an[ms];
+#pragma unroll
+      for (int f = 0; f < 2; f++) bfr[f] = bn[f];
+    }
   }
 }
 
