@@ -115,7 +115,8 @@ int moe_sort_pairs(const int32_t* idx, int T, int k, int E, int32_t* offsets, in
  * with e = idx[t][j], each projection dequantized by the [PACK] global-scales
  * rule (weight = e2m1 * f32(e4m3 * f32(g / 2688))), f32 accumulation, FP32
  * SwiGLU and BF16 mids ([VQ]). x, residual (nullable): bf16 [T][H]; idx i32
- * [T][k]; w f32 [T][k]; y bf16 [T][H], or f32 with MOE_F32_OUT.
+ * [T][k]; w f32 [T][k]; y bf16 [T][H], or f32 with MOE_F32_OUT. Alignment:
+ * x and y 16 bytes, residual 8 bytes, idx and w 4 bytes (else MOE_EALIGN).
  * Expert-streaming (GEMV) kernels are used for small T*k, grouped-GEMM (bf16
  * MFMA) kernels for large T*k; flags can force either.
  * workspace: device, >= moe_nvfp4_workspace_bytes(T, k, H, I, E) bytes,

@@ -76,6 +76,8 @@ def test_forward_validation_before_launch():
     assert call(args(wsb=ws_need - 1)) == wq.MOE_EWORKSPACE
     assert call(args(ws=C.c_void_p((1 << 26) + 16))) == wq.MOE_EALIGN
     assert call(args(x=C.c_void_p((1 << 26) + 2))) == wq.MOE_EALIGN
+    assert call(args(y=C.c_void_p((1 << 26) + 8))) == wq.MOE_EALIGN
+    assert call(args(res=C.c_void_p((1 << 26) + 4))) == wq.MOE_EALIGN
     assert call(args(flags=wq.MOE_FORCE_DECODE | wq.MOE_FORCE_PREFILL)) == wq.MOE_EINVAL
     assert call(args(flags=64)) == wq.MOE_EINVAL
     assert call(args(T=0)) == wq.MOE_OK  # nothing to do, nothing launched

@@ -295,9 +295,9 @@ MOE_API int moe_nvfp4_forward(const moe_nvfp4_bank* b, const uint16_t* x, int T,
   if ((long long)T * k > (1LL << 30)) return fail(MOE_ESHAPE, "forward: too many pairs");
   if (T == 0) return MOE_OK;
   if (!x || !idx || !w || !y || !workspace) return fail(MOE_EINVAL, "forward: null pointer");
-  if (!aligned(x, 16) || (residual && !aligned(residual, 4)) || !aligned(y, 4) || !aligned(idx, 4) ||
+  if (!aligned(x, 16) || (residual && !aligned(residual, 8)) || !aligned(y, 16) || !aligned(idx, 4) ||
       !aligned(w, 4))
-    return fail(MOE_EALIGN, "forward: x must be 16-byte aligned, residual/y/idx/w 4-byte aligned");
+    return fail(MOE_EALIGN, "forward: x and y must be 16-byte aligned, residual 8-byte, idx/w 4-byte");
   if (!aligned(workspace, 256)) return fail(MOE_EALIGN, "forward: workspace not 256-byte aligned");
   const FwdLayout L = fwd_layout(T, k, v.H, v.I, v.E);
   if (workspace_bytes < L.total)

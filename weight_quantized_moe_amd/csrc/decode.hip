@@ -575,35 +575,44 @@ hipError_t launch_flat_decode(const BankView& b, const uint16_t* x, const int32_
 }
 
 // ---- S7: weighted combine (the routing weight is already in `part`) -----------
+// y[t] = residual[t] + sum_j part[t*k + j] in slot order j (f32), four
+// consecutive outputs per thread (16-byte loads of part).
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part,
                                                      const int32_t* __restrict__ idx, int E, int T,
                                                      int H, int k, const uint16_t* __restrict__ res,
                                                      void* y, int f32_out) {
-  const size_t n = (size_t)T * H;
-  for (size_t o = (size_t)blockIdx.x * blockDim.x + threadIdx.x; o < n;
+  const size_t n4 = (size_t)T * H / 4;  // H is a multiple of 4
+  for (size_t o = (size_t)blockIdx.x * blockDim.x + threadIdx.x; o < n4;
        o += (size_t)gridDim.x * blockDim.x) {
-    const size_t t = o / H, h = o % H;
-    float acc = res ? bf16_to_f32(res[o]) : 0.0f;
+    const size_t t = o * 4 / H, hh = o * 4 % H;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (res) {
+      const u32x2 r = *reinterpret_cast<const u32x2*>(res + t * H + hh);
+      acc = f32x4{bf16_to_f32(r.x & 0xFFFFu), bf16_to_f32(r.x >> 16), bf16_to_f32(r.y & 0xFFFFu),
+                  bf16_to_f32(r.y >> 16)};
+    }
     for (int j = 0; j < k; j++) {
       const size_t p = t * k + j;
       const int e = idx[p];
-      if (e >= 0 && e < E) acc += part[p * H + h];
+      if (e >= 0 && e < E) acc += *reinterpret_cast<const f32x4*>(part + p * H + hh);
     }
-    if (f32_out)
-      reinterpret_cast<float*>(y)[o] = acc;
-    else
-      reinterpret_cast<uint16_t*>(y)[o] = f32_to_bf16(acc);
+    if (f32_out) {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(y) + t * H + hh) = acc;
+    } else {
+      const u32x2 b = {f32x2_to_bf16x2(acc.x, acc.y), f32x2_to_bf16x2(acc.z, acc.w)};
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(y) + t * H + hh) = b;
+    }
   }
 }
 
 hipError_t launch_combine(const float* part, const int32_t* idx, int E, int T, int H, int k,
                           const uint16_t* residual, void* y, bool f32_out, hipStream_t s) {
-  size_t n = (size_t)T * H;
-  int blocks = (int)((n + 255) / 256);
-  if (blocks > 4096) blocks = 4096;
+  const size_t n4 = (size_t)T * H / 4;
+  size_t blocks = (n4 + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
   if (blocks < 1) blocks = 1;
   prof_begin("combine", s);
-  hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, s, part, idx, E, T, H, k,
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, part, idx, E, T, H, k,
                      residual, y, f32_out ? 1 : 0);
   prof_end("combine", s);
   return hipGetLastError();

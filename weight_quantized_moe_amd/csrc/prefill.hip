@@ -102,29 +102,45 @@ __device__ __forceinline__ int a_slot(int r, int j) { return j ^ ((r & 7) ^ ((r 
 // 16-byte slot of piece c in B row r (4 pieces per row)
 __device__ __forceinline__ int b_slot(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
 
+// NW waves per workgroup: the A tile is shared by all of them, and an A ring
+// of RA tiles gives the A loads RA-1 steps to land. The launches use 4 waves
+// (two workgroups per CU); 8 waves with a 3-deep A ring (one workgroup per
+// CU) measured slower on the T=8192 workload.
+constexpr int kWaves = 4;
+template <int NW>
+struct Cfg {
+  static constexpr int kRA = (NW == 8) ? 3 : 2;
+  static constexpr int kALoads = kPM / NW / 8;  // wave-wide A loads per step (8 rows each)
+};
+
+template <int NW>
 struct TileCtx {
   const uint8_t* in;      // A matrix (bytes), uniform
   const uint8_t* rec;     // the expert's record, uniform
-  uint32_t a_off[4];      // byte offsets in A of this lane's pieces at k = 0, loads i = 0..3
+  uint32_t a_off[Cfg<NW>::kALoads];  // byte offsets in A of this lane's pieces at k = 0
   uint32_t b_off[4];      // byte offsets in the record of this lane's code pieces at k = 0
   uint32_t s_off;         // byte offset in the record of weight row (wave row = lane)'s scales at k = 0
-  uint32_t a_lds[2];      // this wave's LDS bases for its A loads (rows 32w..), per A tile
+  uint32_t a_lds;         // LDS base of this wave's A rows in A tile 0
   uint32_t b_lds[2];      // the wave's code stages
   uint32_t s_lds[2];      // the wave's scale groups
 };
 
-// A of step ks -> A tile t: the wave loads rows 32w + 8i + l/8 (i = 0..3).
-__device__ __forceinline__ void dma_a(const TileCtx& c, int ks, int t) {
+// A of step ks -> A tile t: the wave loads rows (kPM/NW) w + 8i + l/8.
+template <int NW>
+__device__ __forceinline__ void dma_a(const TileCtx<NW>& c, int ks, int t) {
 #pragma unroll
-  for (int i = 0; i < 4; i++) dma16(c.in + ks * (kPK * 2), c.a_off[i], c.a_lds[t] + 1024 * i);
+  for (int i = 0; i < Cfg<NW>::kALoads; i++)
+    dma16(c.in + ks * (kPK * 2), c.a_off[i], c.a_lds + t * kABuf + 1024 * i);
 }
 // codes of stage g (k steps 2g, 2g+1) -> the wave's stage buffer t
-__device__ __forceinline__ void dma_b(const TileCtx& c, int g, int t) {
+template <int NW>
+__device__ __forceinline__ void dma_b(const TileCtx<NW>& c, int g, int t) {
 #pragma unroll
   for (int i = 0; i < 4; i++) dma16(c.rec + g * 64, c.b_off[i], c.b_lds[t] + 1024 * i);
 }
 // scales of group G (k steps 4G..4G+3) -> the wave's group buffer t
-__device__ __forceinline__ void dma_s(const TileCtx& c, int G, int t) {
+template <int NW>
+__device__ __forceinline__ void dma_s(const TileCtx<NW>& c, int G, int t) {
   dma16(c.rec + G * 16, c.s_off, c.s_lds[t]);
 }
 
@@ -191,35 +207,39 @@ __device__ __forceinline__ void step_mfma(const uint8_t* As, const uint8_t* Bs, 
 }
 
 // Step s of the k loop, I = s mod 8. Issue order (the waits count on it):
-// A of step s+1 into A tile (s+1)%2 (4 loads); on even steps the codes of
-// the next stage (4 loads); every fourth step the scales of the next group
-// (1 load). Then the MFMAs of step s. Before the barrier, wait until A of
-// step s+1 has landed: only this step's later loads may still be in flight,
-// which on odd steps means none, so the codes issued on the step before are
-// in too. Buffers written here were last read on the step before, which
-// every wave has finished (barrier). Loads past the last step repeat it
-// (they go to buffers never read again).
-template <int I>
-__device__ __forceinline__ void kstep(const TileCtx& c, int s, int nk, const uint8_t* A0, const uint8_t* A1,
-                                      const uint8_t* B0, const uint8_t* B1, const uint8_t* S0, const uint8_t* S1,
+// A of step s+RA-1 into A tile (s+RA-1)%RA; on even steps the codes of the
+// next stage (4 loads); every fourth step the scales of the next group (1
+// load). Then the MFMAs of step s on A tile s%RA. Before the barrier, wait
+// until everything step s+1 reads has landed: with RA = 2 that is A of step
+// s+1, the first loads of this step (on odd steps also the codes issued on
+// the step before); with RA = 3, every load issued before this step. Buffers
+// written here were last read on the step before, which every wave has
+// finished (barrier). Loads past the last step repeat it (into buffers never
+// read again).
+template <int NW, int I>
+__device__ __forceinline__ void kstep(const TileCtx<NW>& c, int s, int nk, const uint8_t* As, const uint8_t* B0,
+                                      const uint8_t* B1, const uint8_t* S0, const uint8_t* S1,
                                       f32x16 (&acc)[4][2]) {
-  dma_a(c, min(s + 1, nk - 1), (I + 1) % 2);
+  constexpr int RA = Cfg<NW>::kRA;
+  dma_a(c, min(s + RA - 1, nk - 1), (s + RA - 1) % RA);
   if (I % 2 == 0) dma_b(c, min(s / 2 + 1, (nk - 1) / 2), (I / 2 + 1) % 2);
   if (I % 4 == 0) dma_s(c, min(s / 4 + 1, (nk - 1) / 4), (I / 4 + 1) % 2);
   __builtin_amdgcn_sched_barrier(0);
-  step_mfma((I % 2) ? A1 : A0, ((I / 2) % 2) ? B1 : B0, I % 2, ((I / 4) % 2) ? S1 : S0, I % 4, acc);
+  step_mfma(As + (s % RA) * kABuf, ((I / 2) % 2) ? B1 : B0, I % 2, ((I / 4) % 2) ? S1 : S0, I % 4, acc);
   __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt<((I % 2 == 0) ? 4 : 0) + ((I % 4 == 0) ? 1 : 0)>();
+  constexpr int later = ((I % 2 == 0) ? 4 : 0) + ((I % 4 == 0) ? 1 : 0);  // issued after this step's A
+  wait_vmcnt<(RA == 2) ? later : later + Cfg<NW>::kALoads>();
   step_barrier();
 }
 
-// NPROJ = 2: gate and up (wave w: gate rows n0+32w.. and the same up rows, for
-// 128 output columns per tile), SwiGLU epilogue into mid; NPROJ = 1: down
-// (wave w: rows n0+64w.., 256 output columns per tile), routing-weighted f32
-// rows into part.
+// NPROJ = 2: gate and up (wave w: gate rows n0+32w.. and the same up rows,
+// 32 NW output columns per tile), SwiGLU epilogue into mid; NPROJ = 1: down
+// (wave w: rows n0+64w.., 64 NW output columns per tile), routing-weighted
+// f32 rows into part.
 //
-// Two workgroups share a CU (at most 256 registers per lane, 73 KB of LDS
-// each), so one workgroup's MFMAs cover the other's loads and barriers.
+// NW = 4: two workgroups share a CU (at most 256 registers per lane, 73 KB
+// of LDS each), so one workgroup's MFMAs cover the other's loads and
+// barriers.
 //
 // Work mapping: the hardware hands out workgroups round-robin over the 8
 // XCDs, each with its own L2. Workgroup L runs item (L % 8) * per + L / 8, so
@@ -227,9 +247,10 @@ __device__ __forceinline__ void kstep(const TileCtx& c, int s, int nk, const uin
 // within an expert n-tile major with the expert's M tiles adjacent: those
 // tiles read the same weight rows at the same time from the same L2, and the
 // expert's activation rows stay there across its n-tiles.
-template <int NPROJ>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
-  const int ncol = (NPROJ == 2) ? 2 * 64 : 4 * kWR;  // output columns per tile
+template <int NPROJ, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a) {
+  constexpr int RA = Cfg<NW>::kRA;
+  const int ncol = (NPROJ == 2) ? 32 * NW : kWR * NW;  // output columns per tile
   const int N = (NPROJ == 2) ? a.I : a.H;
   const int K = (NPROJ == 2) ? a.H : a.I;
   const int ntn = (N + ncol - 1) / ncol;
@@ -251,13 +272,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   const int rows = min(kPM, e_hi - row0);
   const int n0 = (local / ce) * ncol;
   const int p0 = (NPROJ == 2) ? 0 : 2;
-  // separate arrays per buffer
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a0[kABuf];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a1[kABuf];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b0[4 * kBStage];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b1[4 * kBStage];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_s0[4 * kSGroup];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_s1[4 * kSGroup];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[RA * kABuf];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b0[NW * kBStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b1[NW * kBStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_s0[NW * kSGroup];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_s1[NW * kSGroup];
   __shared__ int src_row[kPM];
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -266,7 +285,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int r = min(tid, rows - 1);
     src_row[tid] = (NPROJ == 2) ? a.rt.sorted[row0 + r] / a.k : row0 + r;
   }
-  TileCtx c;
+  TileCtx<NW> c;
   c.in = uniform_ptr(a.in);
   c.rec = uniform_ptr(a.bank + (size_t)e * a.stride);
   float t_p[NPROJ];
@@ -292,22 +311,20 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int n = wrow(lane, q);
     c.s_off = (uint32_t)(a.scales[p0 + q] + (size_t)n * (K / 16));
   }
-  const uint8_t* const A0 = lds_a0;
-  const uint8_t* const A1 = lds_a1;
+  constexpr int arows = kPM / NW;  // A rows loaded by each wave
   const uint8_t* const B0 = lds_b0 + wave * kBStage;
   const uint8_t* const B1 = lds_b1 + wave * kBStage;
   const uint8_t* const S0 = lds_s0 + wave * kSGroup;
   const uint8_t* const S1 = lds_s1 + wave * kSGroup;
-  c.a_lds[0] = __builtin_amdgcn_readfirstlane(lds_addr(A0 + 32 * wave * 128));
-  c.a_lds[1] = __builtin_amdgcn_readfirstlane(lds_addr(A1 + 32 * wave * 128));
+  c.a_lds = __builtin_amdgcn_readfirstlane(lds_addr(lds_a + arows * wave * 128));
   c.b_lds[0] = __builtin_amdgcn_readfirstlane(lds_addr(B0));
   c.b_lds[1] = __builtin_amdgcn_readfirstlane(lds_addr(B1));
   c.s_lds[0] = __builtin_amdgcn_readfirstlane(lds_addr(S0));
   c.s_lds[1] = __builtin_amdgcn_readfirstlane(lds_addr(S1));
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int r = 32 * wave + 8 * i + (lane >> 3);
+  for (int i = 0; i < Cfg<NW>::kALoads; i++) {
+    const int r = arows * wave + 8 * i + (lane >> 3);
     const int piece = a_slot(r, lane & 7);
     c.a_off[i] = (uint32_t)src_row[r] * (uint32_t)(K * 2) + 16 * piece;
   }
@@ -319,29 +336,30 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     for (int f = 0; f < 2; f++) acc[ms][f] = f32x16{};
 
   const int nk = K / kPK;
-  dma_a(c, 0, 0);
+#pragma unroll
+  for (int j = 0; j < RA - 1; j++) dma_a(c, min(j, nk - 1), j);
   dma_b(c, 0, 0);
   dma_s(c, 0, 0);
   wait_vmcnt<0>();
   step_barrier();
   int s = 0;
   for (; s + 8 <= nk; s += 8) {
-    kstep<0>(c, s, nk, A0, A1, B0, B1, S0, S1, acc);
-    kstep<1>(c, s + 1, nk, A0, A1, B0, B1, S0, S1, acc);
-    kstep<2>(c, s + 2, nk, A0, A1, B0, B1, S0, S1, acc);
-    kstep<3>(c, s + 3, nk, A0, A1, B0, B1, S0, S1, acc);
-    kstep<4>(c, s + 4, nk, A0, A1, B0, B1, S0, S1, acc);
-    kstep<5>(c, s + 5, nk, A0, A1, B0, B1, S0, S1, acc);
-    kstep<6>(c, s + 6, nk, A0, A1, B0, B1, S0, S1, acc);
-    kstep<7>(c, s + 7, nk, A0, A1, B0, B1, S0, S1, acc);
+    kstep<NW, 0>(c, s, nk, lds_a, B0, B1, S0, S1, acc);
+    kstep<NW, 1>(c, s + 1, nk, lds_a, B0, B1, S0, S1, acc);
+    kstep<NW, 2>(c, s + 2, nk, lds_a, B0, B1, S0, S1, acc);
+    kstep<NW, 3>(c, s + 3, nk, lds_a, B0, B1, S0, S1, acc);
+    kstep<NW, 4>(c, s + 4, nk, lds_a, B0, B1, S0, S1, acc);
+    kstep<NW, 5>(c, s + 5, nk, lds_a, B0, B1, S0, S1, acc);
+    kstep<NW, 6>(c, s + 6, nk, lds_a, B0, B1, S0, S1, acc);
+    kstep<NW, 7>(c, s + 7, nk, lds_a, B0, B1, S0, S1, acc);
   }
-  if (s < nk) kstep<0>(c, s, nk, A0, A1, B0, B1, S0, S1, acc);
-  if (s + 1 < nk) kstep<1>(c, s + 1, nk, A0, A1, B0, B1, S0, S1, acc);
-  if (s + 2 < nk) kstep<2>(c, s + 2, nk, A0, A1, B0, B1, S0, S1, acc);
-  if (s + 3 < nk) kstep<3>(c, s + 3, nk, A0, A1, B0, B1, S0, S1, acc);
-  if (s + 4 < nk) kstep<4>(c, s + 4, nk, A0, A1, B0, B1, S0, S1, acc);
-  if (s + 5 < nk) kstep<5>(c, s + 5, nk, A0, A1, B0, B1, S0, S1, acc);
-  if (s + 6 < nk) kstep<6>(c, s + 6, nk, A0, A1, B0, B1, S0, S1, acc);
+  if (s < nk) kstep<NW, 0>(c, s, nk, lds_a, B0, B1, S0, S1, acc);
+  if (s + 1 < nk) kstep<NW, 1>(c, s + 1, nk, lds_a, B0, B1, S0, S1, acc);
+  if (s + 2 < nk) kstep<NW, 2>(c, s + 2, nk, lds_a, B0, B1, S0, S1, acc);
+  if (s + 3 < nk) kstep<NW, 3>(c, s + 3, nk, lds_a, B0, B1, S0, S1, acc);
+  if (s + 4 < nk) kstep<NW, 4>(c, s + 4, nk, lds_a, B0, B1, S0, S1, acc);
+  if (s + 5 < nk) kstep<NW, 5>(c, s + 5, nk, lds_a, B0, B1, S0, S1, acc);
+  if (s + 6 < nk) kstep<NW, 6>(c, s + 6, nk, lds_a, B0, B1, S0, S1, acc);
   wait_vmcnt<0>();  // the loads past the last step
 
   // epilogue; accumulator element r of lane l is (row 8(r/4) + 4(l/32) + r%4,
@@ -392,10 +410,10 @@ hipError_t launch_prefill_gateup(const BankView& b, const uint16_t* x, int k, co
   PrefillArgs a = make_args(b, k, rt);
   a.in = x;
   a.mid = mid;
-  const int items = ((b.I + 127) / 128) * max_tiles;
+  const int items = ((b.I + 32 * kWaves - 1) / (32 * kWaves)) * max_tiles;
   dim3 grid((items + 7) / 8 * 8);
   prof_begin("prefill_gateup", s);
-  hipLaunchKernelGGL(prefill_kernel<2>, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((prefill_kernel<2, kWaves>), grid, dim3(64 * kWaves), 0, s, a);
   prof_end("prefill_gateup", s);
   return hipGetLastError();
 }
@@ -406,10 +424,10 @@ hipError_t launch_prefill_down(const BankView& b, const uint16_t* mid, const flo
   a.in = mid;
   a.w = w;
   a.part = part;
-  const int items = ((b.H + 255) / 256) * max_tiles;
+  const int items = ((b.H + 64 * kWaves - 1) / (64 * kWaves)) * max_tiles;
   dim3 grid((items + 7) / 8 * 8);
   prof_begin("prefill_down", s);
-  hipLaunchKernelGGL(prefill_kernel<1>, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((prefill_kernel<1, kWaves>), grid, dim3(64 * kWaves), 0, s, a);
   prof_end("prefill_down", s);
   return hipGetLastError();
 }
