@@ -17,9 +17,22 @@ on the stream it runs on.
 cpu_baseline: the CPU oracle (as is) on a bounded sample of the decode
 workload, on this host's cores.
 
+roofline.traffic: HBM bytes per launch of the dominant decode kernel, from
+rocprofv3 FETCH_SIZE + WRITE_SIZE counter runs scaled by what the same
+counters read for a plain device copy of known size; read from
+profiles/traffic_decode_gateup.txt and reported only while the kernel source
+it was measured on is unchanged (its SHA-1 is recorded there), else null.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--prefill-steps P]
+       [--only decode|prefill] [--no-cpu-baseline]
+Profiling helpers: --copy-calibration (device copies of 1 GiB, for the
+counter scale factor); --summarize-pmc DIR (per-kernel mean counter values
+per dispatch from a rocprofv3 --pmc output directory; no GPU needed).
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -127,6 +140,47 @@ def timed(fn, steps, warmup):
     return e0.elapsed_time(e1), (time.perf_counter() - t0) * 1e3
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_gateup.txt")
+DECODE_SRC = os.path.join(ROOT, "weight_quantized_moe_amd", "csrc", "decode.hip")
+
+
+def recorded_traffic():
+    """Bytes per launch of the decode gate/up kernel from the committed counter
+    summary, if it was measured on the current kernel source; else None."""
+    try:
+        fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line)
+        src = hashlib.sha1(open(DECODE_SRC, "rb").read()).hexdigest()
+        if fields.get("source_sha1", "").strip() != src:
+            return None
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """Plain device copies of nbytes, for scaling FETCH_SIZE / WRITE_SIZE."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} copies of {nbytes} bytes")
+
+
+def summarize_pmc(d):
+    """Mean counter value per dispatch and kernel over rocprofv3 counter CSVs."""
+    agg, disp = {}, {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            k = r["Kernel_Name"]
+            key = (k, r["Counter_Name"])
+            agg[key] = agg.get(key, 0.0) + float(r["Counter_Value"])
+            disp.setdefault(k, set()).add(r["Dispatch_Id"])
+    for (k, cname), v in sorted(agg.items()):
+        print(f"{k[:70]:70s} {cname:12s} dispatches={len(disp[k]):4d} mean_per_dispatch={v / len(disp[k]):.6g}")
+
+
 def cpu_baseline(c, budget_s=20.0):
     """The oracle, as it stands, on decode steps (router + top-k + layer), on
     this host; as many steps as fit the time budget (at least one, at most 8)."""
@@ -159,6 +213,33 @@ def cpu_baseline(c, budget_s=20.0):
             "sample": f"{n} decode steps (T=1, router + top-8 + layer), {t_total:.1f} s, f64-accumulating C oracle"}
 
 
+def prefill_leg(bank, P):
+    pre = PrefillLeg(bank)
+    pms, _ = timed(pre.step, P, 2)
+    tflops = pre.flop / (pms / P * 1e-3) / 1e12
+    wq.moe_profile_enable(True)
+    for _ in range(P):
+        pre.step()
+    torch.cuda.synchronize()
+    pk = {n_: kernel_avg_ms(n_) for n_ in ["topk", "sort", "prefill_gateup", "prefill_down", "combine"]}
+    pk = {n_: v for n_, v in pk.items() if v[1]}
+    wq.moe_profile_enable(False)
+    for n_, (avg, cnt) in pk.items():
+        log(f"  {n_:15s} {avg * 1e3:8.2f} us x {cnt}")
+    gu_flop = 2 * pre.c["T"] * pre.c["k"] * 2 * pre.c["H"] * pre.c["I"]
+    gu_tf = gu_flop / (pk["prefill_gateup"][0] * 1e-3) / 1e12
+    log(f"prefill: {pms / P:.3f} ms/step, {tflops:.1f} TFLOP/s")
+    return {"value": round(tflops, 2), "unit": "TFLOP/s", "steps": P, "ms_per_step": round(pms / P, 4),
+            "workload": "prefill: T=8192, top-8 of 256 on Zipf(1.1)-skewed logits (given), "
+                        "65,536 pairs, 5.154 TFLOP per step",
+            "roofline": {"kernel": "prefill_gateup", "bound": "mfma", "achieved": round(gu_tf, 2),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(gu_tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "flop_per_launch": gu_flop,
+                         "avg_launch_ms": round(pk["prefill_gateup"][0], 4)},
+            "kernels_us": {n_: round(v[0] * 1e3, 2) for n_, v in pk.items()}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,7 +248,15 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill"])
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-pmc")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
+    if args.only == "decode":
+        args.no_prefill = True
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the layer runs on one MI355X; --gpus must be 1).", file=sys.stderr)
@@ -175,11 +264,17 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wq.lib()
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     c = W.CONFIGS["decode"]
     log(f"building the bank: {c['E']} records of {wq.moe_nvfp4_record_bytes(c['H'], c['I'])} B")
     t0 = time.time()
     bank, base = W.build_bank(c["bank_seed"], c["H"], c["I"], c["E"])
     log(f"bank ready in {time.time() - t0:.1f} s")
+    if args.only == "prefill":
+        print(json.dumps({"prefill": prefill_leg(bank, args.prefill_steps)}), flush=True)
+        return
 
     # ---- decode leg
     dec = DecodeLeg(bank)
@@ -212,7 +307,7 @@ def main():
     gu_ms = kern["decode_gateup"][0]
     achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
     roofline = {"kernel": "decode_gateup", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                 "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(gu_ms * 1e3, 2)}
 
     out = {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": Wm,
@@ -229,31 +324,7 @@ def main():
     if not args.no_prefill:
         del dec
         torch.cuda.empty_cache()
-        pre = PrefillLeg(bank)
-        P = args.prefill_steps
-        pms, _ = timed(pre.step, P, 2)
-        tflops = pre.flop / (pms / P * 1e-3) / 1e12
-        wq.moe_profile_enable(True)
-        for _ in range(P):
-            pre.step()
-        torch.cuda.synchronize()
-        pk = {n_: kernel_avg_ms(n_) for n_ in ["topk", "sort", "prefill_gateup", "prefill_down", "combine"]}
-        pk = {n_: v for n_, v in pk.items() if v[1]}
-        wq.moe_profile_enable(False)
-        for n_, (avg, cnt) in pk.items():
-            log(f"  {n_:15s} {avg * 1e3:8.2f} us x {cnt}")
-        gu_flop = 2 * pre.c["T"] * pre.c["k"] * 2 * pre.c["H"] * pre.c["I"]
-        gu_tf = gu_flop / (pk["prefill_gateup"][0] * 1e-3) / 1e12
-        out["prefill"] = {"value": round(tflops, 2), "unit": "TFLOP/s", "steps": P, "ms_per_step": round(pms / P, 4),
-                          "workload": "prefill: T=8192, top-8 of 256 on Zipf(1.1)-skewed logits (given), "
-                                      "65,536 pairs, 5.154 TFLOP per step",
-                          "roofline": {"kernel": "prefill_gateup", "bound": "mfma", "achieved": round(gu_tf, 2),
-                                       "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                       "frac": round(gu_tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                                       "flop_per_launch": gu_flop,
-                                       "avg_launch_ms": round(pk["prefill_gateup"][0], 4)},
-                          "kernels_us": {n_: round(v[0] * 1e3, 2) for n_, v in pk.items()}}
-        log(f"prefill: {pms / P:.3f} ms/step, {tflops:.1f} TFLOP/s")
+        out["prefill"] = prefill_leg(bank, args.prefill_steps)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(c)

@@ -146,9 +146,9 @@ int moe_rmsnorm(const uint16_t* x, int T, int H, float eps, uint16_t* y, void* s
 int moe_nvfp4_dequant(const moe_nvfp4_bank* b, int expert, int proj, float* out_f32,
                       uint16_t* out_unit, void* stream);
 
-/* Kernel timing with HIP events recorded around each launch on its stream.
- * moe_profile_enable(1) clears and starts collection (it adds a little launch
- * overhead); moe_profile_read(name, ...) synchronizes the recorded events and
+/* Kernel timing with HIP events that hipExtLaunchKernel records at each
+ * kernel's own start and end on its stream. moe_profile_enable(1) clears and
+ * starts collection; moe_profile_read(name, ...) synchronizes the events and
  * returns the summed duration and count of the kernel family `name` since the
  * last enable. Names: "router", "topk", "sort", "decode_gateup", "decode_down",
  * "combine", "prefill_gateup", "prefill_down", "affine8", "rmsnorm". */

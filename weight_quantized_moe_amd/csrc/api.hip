@@ -46,7 +46,6 @@ struct Profiler {
   std::mutex mu;
   bool on = false;
   std::map<std::string, std::vector<ProfEntry>> done;
-  std::map<std::string, hipEvent_t> open;
   void clear() {
     for (auto& kv : done)
       for (auto& pe : kv.second) {
@@ -54,8 +53,6 @@ struct Profiler {
         hipEventDestroy(pe.end);
       }
     done.clear();
-    for (auto& kv : open) hipEventDestroy(kv.second);
-    open.clear();
   }
 };
 Profiler& prof() {
@@ -67,27 +64,17 @@ Profiler& prof() {
 
 namespace moe {
 
-void prof_begin(const char* name, hipStream_t s) {
+bool prof_events(const char* name, hipEvent_t* start, hipEvent_t* stop) {
   Profiler& p = prof();
   std::lock_guard<std::mutex> lk(p.mu);
-  if (!p.on) return;
-  hipEvent_t ev;
-  if (hipEventCreate(&ev) != hipSuccess) return;
-  hipEventRecord(ev, s);
-  p.open[name] = ev;
-}
-
-void prof_end(const char* name, hipStream_t s) {
-  Profiler& p = prof();
-  std::lock_guard<std::mutex> lk(p.mu);
-  if (!p.on) return;
-  auto it = p.open.find(name);
-  if (it == p.open.end()) return;
-  hipEvent_t ev;
-  if (hipEventCreate(&ev) != hipSuccess) return;
-  hipEventRecord(ev, s);
-  p.done[name].push_back({it->second, ev});
-  p.open.erase(it);
+  if (!p.on) return false;
+  if (hipEventCreate(start) != hipSuccess) return false;
+  if (hipEventCreate(stop) != hipSuccess) {
+    hipEventDestroy(*start);
+    return false;
+  }
+  p.done[name].push_back({*start, *stop});
+  return true;
 }
 
 }  // namespace moe

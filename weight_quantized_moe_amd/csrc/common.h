@@ -98,4 +98,13 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + expf(-g)) * u;
 }
 
+// Total order of logits for top-k as an unsigned key: larger logit first,
+// -0 and +0 equal, NaN below every number.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t b = __float_as_uint(v);
+  if ((b & 0x7FFFFFFFu) == 0) b = 0;                     // -0 -> +0
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0;        // NaN: below everything
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);    // monotone in v
+}
+
 }  // namespace moe

@@ -22,6 +22,7 @@
 #include <cstdlib>
 
 #include "common.h"
+#include "gemv_util.h"
 #include "internal.h"
 
 namespace moe {
@@ -99,65 +100,6 @@ __device__ __forceinline__ void stage_rows(uint32_t* xs, const uint16_t* src, in
     u32x4* d = reinterpret_cast<u32x4*>(xs + m * (len / 2));
     for (int i = threadIdx.x; i < len / 8; i += kDecThreads) d[i] = s[i];
   }
-}
-
-// one quad of one projection: 8 code words + 4 scale bytes
-struct Quad {
-  u32x4 c0, c1;
-  uint32_t s;
-};
-
-__device__ __forceinline__ Quad load_quad(const uint8_t* row_codes, const uint8_t* row_scales, int q) {
-  Quad v;
-  const u32x4* cp = reinterpret_cast<const u32x4*>(row_codes + 32 * (size_t)q);
-  v.c0 = cp[0];
-  v.c1 = cp[1];
-  v.s = *reinterpret_cast<const uint32_t*>(row_scales + 4 * (size_t)q);
-  return v;
-}
-
-// the 8 packed input pairs of block b (0..3) of quad q, from LDS
-__device__ __forceinline__ void load_x8(const uint32_t* xrow, int q, int b, uint32_t* xw) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(xrow + 32 * q + 8 * b);
-  const u32x4 v0 = p[0], v1 = p[1];
-  xw[0] = v0.x;
-  xw[1] = v0.y;
-  xw[2] = v0.z;
-  xw[3] = v0.w;
-  xw[4] = v1.x;
-  xw[5] = v1.y;
-  xw[6] = v1.z;
-  xw[7] = v1.w;
-}
-
-// code words of block b of a quad
-__device__ __forceinline__ uint32_t quad_word(const Quad& v, int i) {
-  switch (i) {
-    case 0: return v.c0.x;
-    case 1: return v.c0.y;
-    case 2: return v.c0.z;
-    case 3: return v.c0.w;
-    case 4: return v.c1.x;
-    case 5: return v.c1.y;
-    case 6: return v.c1.z;
-    default: return v.c1.w;
-  }
-}
-
-__device__ __forceinline__ float quad_scale(const Quad& v, int b) {
-  switch (b) {
-    case 0: return e4m3_f32<0>(v.s);
-    case 1: return e4m3_f32<1>(v.s);
-    case 2: return e4m3_f32<2>(v.s);
-    default: return e4m3_f32<3>(v.s);
-  }
-}
-
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
 }
 
 // NPROJ = 2: gate and up rows (input x, SwiGLU into mid); NPROJ = 1: down
@@ -293,10 +235,11 @@ static int env_int(const char* name, int dflt) {
 
 template <int G, int QB, int NPROJ>
 static void launch_gemv_g(const DecodeArgs& b, dim3 grid, size_t lds, bool one, hipStream_t s) {
+  const char* name = (NPROJ == 2) ? "decode_gateup" : "decode_down";
   if (one)
-    hipLaunchKernelGGL((gemv_kernel<G, QB, 1, NPROJ>), grid, dim3(kDecThreads), lds, s, b);
+    launch_kernel(name, gemv_kernel<G, QB, 1, NPROJ>, grid, dim3(kDecThreads), (uint32_t)lds, s, b);
   else
-    hipLaunchKernelGGL((gemv_kernel<G, QB, 4, NPROJ>), grid, dim3(kDecThreads), lds, s, b);
+    launch_kernel(name, gemv_kernel<G, QB, 4, NPROJ>, grid, dim3(kDecThreads), (uint32_t)lds, s, b);
 }
 
 // Tuning knobs (environment, read at each launch): MOE_GEMV_QB_{GATEUP,DOWN}
@@ -354,10 +297,7 @@ hipError_t launch_decode_gateup(const BankView& b, const uint16_t* x, const int3
   DecodeArgs a = make_args(b, idx, P, k, rt);
   a.in = x;
   a.mid = mid;
-  prof_begin("decode_gateup", s);
-  hipError_t e = launch_gemv<2>(a, slots, max_m, s);
-  prof_end("decode_gateup", s);
-  return e;
+  return launch_gemv<2>(a, slots, max_m, s);
 }
 
 hipError_t launch_decode_down(const BankView& b, const uint16_t* mid, const float* w,
@@ -367,10 +307,7 @@ hipError_t launch_decode_down(const BankView& b, const uint16_t* mid, const floa
   a.in = mid;
   a.w = w;
   a.part = part;
-  prof_begin("decode_down", s);
-  hipError_t e = launch_gemv<1>(a, slots, max_m, s);
-  prof_end("decode_down", s);
-  return e;
+  return launch_gemv<1>(a, slots, max_m, s);
 }
 
 // ---- one token (T = 1): flat kernels ---------------------------------------------
@@ -378,8 +315,9 @@ hipError_t launch_decode_down(const BankView& b, const uint16_t* mid, const floa
 // shared by all of them. Gate/up: a fixed grid of blocks stages x in LDS once;
 // its waves then walk a flat list of (pair, 4-row group) items with no further
 // barrier, each item one batch of 16-byte loads (the 4 rows of gate and up).
-// Down + combine: a block owns 8 output rows for all k pairs; its 4 waves take
-// pairs j = wave, wave + 4, ..., the routing-weighted row sums meet in LDS and
+// Down + combine: a block owns 8 output rows for all k pairs; its k waves take
+// one pair each (all loads of a block in flight at once), the routing-weighted
+// row sums meet in LDS and
 // are added in slot order (j ascending) onto the residual, and y is written
 // directly: no per-pair partial rows and no separate combine pass.
 struct FlatArgs {
@@ -460,7 +398,7 @@ __global__ __launch_bounds__(kDecThreads) void flat_gateup_kernel(FlatArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kDecThreads) void flat_down_kernel(FlatArgs a) {
+__global__ __launch_bounds__(64 * kFlatDecodeMaxK) void flat_down_kernel(FlatArgs a) {
   constexpr int G = 8, R = 64 / G, QB = 5;
   extern __shared__ uint32_t ms[];  // [k][I/2]
   __shared__ int s_idx[kFlatDecodeMaxK];
@@ -479,10 +417,11 @@ __global__ __launch_bounds__(kDecThreads) void flat_down_kernel(FlatArgs a) {
   {
     const u32x4* src = reinterpret_cast<const u32x4*>(a.mid);
     u32x4* dst = reinterpret_cast<u32x4*>(ms);
-    for (int i = threadIdx.x; i < k * I / 8; i += kDecThreads) dst[i] = src[i];
+    for (int i = threadIdx.x; i < k * I / 8; i += blockDim.x) dst[i] = src[i];
   }
   __syncthreads();
-  for (int j = wave; j < k; j += kDecWaves) {
+  {
+    const int j = wave;  // one wave per pair
     const int e = s_idx[j];
     float ad = 0.0f;
     if (e >= 0) {
@@ -561,16 +500,12 @@ hipError_t launch_flat_decode(const BankView& b, const uint16_t* x, const int32_
   a.y = y;
   a.f32_out = f32_out ? 1 : 0;
   const int groups = (b.I + 3) / 4;
-  prof_begin("decode_gateup", s);
-  hipLaunchKernelGGL(flat_gateup_kernel, dim3(flat_blocks(k * groups)), dim3(kDecThreads),
-                     (size_t)b.H * 2, s, a);
-  prof_end("decode_gateup", s);
+  launch_kernel("decode_gateup", flat_gateup_kernel, dim3(flat_blocks(k * groups)), dim3(kDecThreads),
+                (uint32_t)(b.H * 2), s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  prof_begin("decode_down", s);
-  hipLaunchKernelGGL(flat_down_kernel, dim3((b.H + 7) / 8), dim3(kDecThreads),
-                     (size_t)k * b.I * 2, s, a);
-  prof_end("decode_down", s);
+  launch_kernel("decode_down", flat_down_kernel, dim3((b.H + 7) / 8), dim3(64 * k),
+                (uint32_t)(k * b.I * 2), s, a);
   return hipGetLastError();
 }
 
@@ -611,10 +546,8 @@ hipError_t launch_combine(const float* part, const int32_t* idx, int E, int T, i
   size_t blocks = (n4 + 255) / 256;
   if (blocks > 16384) blocks = 16384;
   if (blocks < 1) blocks = 1;
-  prof_begin("combine", s);
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, part, idx, E, T, H, k,
-                     residual, y, f32_out ? 1 : 0);
-  prof_end("combine", s);
+  launch_kernel("combine", combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, part, idx, E, T, H, k,
+                residual, y, f32_out ? 1 : 0);
   return hipGetLastError();
 }
 

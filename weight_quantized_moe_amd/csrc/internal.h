@@ -1,5 +1,6 @@
 // Internal launch interface of libmoe_mi355x.so (not part of the C ABI).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -77,7 +78,19 @@ hipError_t launch_affine8(const uint16_t* x, const uint32_t* codes, const uint16
                           const uint16_t* biases, int T, int K, int N, uint16_t* y, hipStream_t s);
 
 // kernel timing (api.hip)
-void prof_begin(const char* name, hipStream_t s);
-void prof_end(const char* name, hipStream_t s);
+// Kernel timing (moe_profile_enable). When on, prof_events hands out a pair
+// of events for one launch of kernel `name`; launch_kernel passes them to
+// hipExtLaunchKernel, which records them at the kernel's own start and end.
+bool prof_events(const char* name, hipEvent_t* start, hipEvent_t* stop);
+
+template <typename F, typename... Args>
+inline void launch_kernel(const char* name, F kernel, dim3 grid, dim3 block, uint32_t shm, hipStream_t s,
+                          Args... args) {
+  hipEvent_t e0, e1;
+  if (prof_events(name, &e0, &e1))
+    hipExtLaunchKernelGGL(kernel, grid, block, shm, s, e0, e1, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, shm, s, args...);
+}
 
 }  // namespace moe

@@ -102,9 +102,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* x, int H, 
 }
 
 hipError_t launch_rmsnorm(const uint16_t* x, int T, int H, float eps, uint16_t* y, hipStream_t s) {
-  prof_begin("rmsnorm", s);
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(256), 0, s, x, H, eps, y);
-  prof_end("rmsnorm", s);
+  launch_kernel("rmsnorm", rmsnorm_kernel, dim3(T), dim3(256), 0, s, x, H, eps, y);
   return hipGetLastError();
 }
 
@@ -200,10 +198,8 @@ __global__ __launch_bounds__(256) void affine8_kernel(const uint16_t* __restrict
 hipError_t launch_affine8(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
                           const uint16_t* biases, int T, int K, int N, uint16_t* y, hipStream_t s) {
   size_t lds = (size_t)kAffTok * (K / 2) * 4 + (size_t)kAffTok * (K / 16) * 4;
-  prof_begin("affine8", s);
-  hipLaunchKernelGGL(affine8_kernel, dim3((N + kAffRows - 1) / kAffRows), dim3(256), lds, s, x,
-                     codes, scales, biases, T, K, N, y);
-  prof_end("affine8", s);
+  launch_kernel("affine8", affine8_kernel, dim3((N + kAffRows - 1) / kAffRows), dim3(256), (uint32_t)lds, s, x,
+                codes, scales, biases, T, K, N, y);
   return hipGetLastError();
 }
 

@@ -412,9 +412,7 @@ hipError_t launch_prefill_gateup(const BankView& b, const uint16_t* x, int k, co
   a.mid = mid;
   const int items = ((b.I + 32 * kWaves - 1) / (32 * kWaves)) * max_tiles;
   dim3 grid((items + 7) / 8 * 8);
-  prof_begin("prefill_gateup", s);
-  hipLaunchKernelGGL((prefill_kernel<2, kWaves>), grid, dim3(64 * kWaves), 0, s, a);
-  prof_end("prefill_gateup", s);
+  launch_kernel("prefill_gateup", prefill_kernel<2, kWaves>, grid, dim3(64 * kWaves), 0, s, a);
   return hipGetLastError();
 }
 
@@ -426,9 +424,7 @@ hipError_t launch_prefill_down(const BankView& b, const uint16_t* mid, const flo
   a.part = part;
   const int items = ((b.H + 64 * kWaves - 1) / (64 * kWaves)) * max_tiles;
   dim3 grid((items + 7) / 8 * 8);
-  prof_begin("prefill_down", s);
-  hipLaunchKernelGGL((prefill_kernel<1, kWaves>), grid, dim3(64 * kWaves), 0, s, a);
-  prof_end("prefill_down", s);
+  launch_kernel("prefill_down", prefill_kernel<1, kWaves>, grid, dim3(64 * kWaves), 0, s, a);
   return hipGetLastError();
 }
 

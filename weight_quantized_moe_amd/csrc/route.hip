@@ -59,9 +59,7 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict_
 hipError_t launch_router(const uint16_t* x, const float* Wr, float* logits, int T, int H, int E,
                          hipStream_t s) {
   dim3 grid(E, (T + kRouterTok - 1) / kRouterTok);
-  prof_begin("router", s);
-  hipLaunchKernelGGL(router_kernel, grid, dim3(256), 0, s, x, Wr, logits, T, H, E);
-  prof_end("router", s);
+  launch_kernel("router", router_kernel, grid, dim3(256), 0, s, x, Wr, logits, T, H, E);
   return hipGetLastError();
 }
 
@@ -74,12 +72,6 @@ hipError_t launch_router(const uint16_t* x, const float* Wr, float* logits, int 
 // candidates c, c+256, ...; the four partial counts are added in LDS. The k
 // candidates with rank < k are the top-k in order; the softmax over them is
 // f32, summed in slot order.
-__device__ __forceinline__ uint32_t order_key(float v) {
-  uint32_t b = __float_as_uint(v);
-  if ((b & 0x7FFFFFFFu) == 0) b = 0;                     // -0 -> +0
-  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0;        // NaN: below everything
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);    // monotone in v
-}
 
 __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ logits, int T, int E,
                                                     int k, int32_t* __restrict__ idx,
@@ -127,9 +119,7 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ lo
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                        hipStream_t s) {
-  prof_begin("topk", s);
-  hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(1024), 0, s, logits, T, E, k, idx, w);
-  prof_end("topk", s);
+  launch_kernel("topk", topk_kernel, dim3(T), dim3(1024), 0, s, logits, T, E, k, idx, w);
   return hipGetLastError();
 }
 
@@ -260,10 +250,7 @@ __global__ __launch_bounds__(kSortThreads) void sort_kernel(const int32_t* __res
 
 hipError_t launch_sort(const int32_t* idx, int P, int E, RouteTables rt, int mtile, int max_tiles,
                        hipStream_t s) {
-  prof_begin("sort", s);
-  hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(kSortThreads), 0, s, idx, P, E, rt, mtile,
-                     max_tiles);
-  prof_end("sort", s);
+  launch_kernel("sort", sort_kernel, dim3(1), dim3(kSortThreads), 0, s, idx, P, E, rt, mtile, max_tiles);
   return hipGetLastError();
 }
 
