@@ -83,6 +83,13 @@ __device__ __forceinline__ float block_dot16(uint32_t w0, uint32_t w1, const uin
   return s;
 }
 
+// DPP move of a float from another lane of the same 16-lane row (CTRL: a
+// dpp_ctrl value, e.g. 0x111 = row_shr:1); lanes with no source read 0.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);

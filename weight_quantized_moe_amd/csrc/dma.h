@@ -1,0 +1,37 @@
+// HBM -> LDS loads for gfx950 kernels that manage their own waits.
+#pragma once
+#include "common.h"
+
+namespace moe {
+
+// One wave-wide HBM -> LDS load (global_load_lds_dwordx4): lane l's 16 bytes
+// at base + voff land at LDS byte address lds + 16 l; base and lds are
+// wave-uniform. Issued from inline asm so the compiler's wait insertion does
+// not make every later LDS access and barrier wait for it: a kernel using it
+// waits for these loads itself (wait_vmcnt) before it reads their data, and
+// must not have other vector-memory loads in flight that the count would
+// miss. The instruction writes no registers.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(lds)
+               : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ const uint8_t* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint8_t*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+}
+
+// s_waitcnt vmcnt(n) alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+}  // namespace moe

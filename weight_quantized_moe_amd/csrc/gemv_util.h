@@ -62,6 +62,19 @@ __device__ __forceinline__ float quad_scale(const Quad& v, int b) {
   }
 }
 
+// Sum over each aligned group of G (2..16) lanes, left in the group's last
+// lane (sub == G - 1): DPP row shifts inside a 16-lane row, no LDS traffic.
+// Other lanes hold partial sums.
+template <int G>
+__device__ __forceinline__ float group_sum_last(float v) {
+  static_assert(G >= 2 && G <= 16 && (G & (G - 1)) == 0, "G: 2..16, a power of two");
+  v += dpp_f32<0x111>(v);                     // row_shr:1
+  if (G > 2) v += dpp_f32<0x112>(v);          // row_shr:2
+  if (G > 4) v += dpp_f32<0x114>(v);          // row_shr:4
+  if (G > 8) v += dpp_f32<0x118>(v);          // row_shr:8
+  return v;
+}
+
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll

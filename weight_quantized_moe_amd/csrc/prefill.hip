@@ -34,6 +34,7 @@
 // per row); the A operand uses the same assignment, which only permutes the
 // order of the sum.
 #include "common.h"
+#include "dma.h"
 #include "internal.h"
 
 namespace moe {
@@ -56,36 +57,6 @@ struct PrefillArgs {
   uint16_t* mid;
   float* part;
 };
-
-// One wave-wide HBM -> LDS load (global_load_lds_dwordx4): lane l's 16 bytes
-// at base + voff land at LDS byte address lds + 16 l; base and lds are
-// wave-uniform. Issued from inline asm so the compiler's wait insertion does
-// not make every later LDS access and barrier wait for it: the k loop waits
-// for its loads itself (wait_vmcnt) before the barrier that publishes them.
-// The instruction writes no registers. The loop issues no other vector-memory
-// loads, so vmcnt counts exactly these.
-__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(lds)
-               : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-__device__ __forceinline__ const uint8_t* uniform_ptr(const void* p) {
-  const uint64_t v = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<const uint8_t*>((uintptr_t)(((uint64_t)hi << 32) | lo));
-}
-
-// s_waitcnt vmcnt(n) alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
-// expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // Workgroup barrier after this wave's LDS accesses have completed. No memory
 // fence: a fence would also wait for every HBM -> LDS load in flight. The
