@@ -126,6 +126,7 @@ __device__ __forceinline__ bf16x8 deq8(uint32_t word, float sb) {
 
 // The MFMAs of one k step. As: A tile; Bs: the wave's code stage, half t;
 // Ss: the wave's scale group, step q within it.
+template <int NMS>
 __device__ __forceinline__ void step_mfma(const uint8_t* As, const uint8_t* Bs, int t, const uint8_t* Ss, int q,
                                           f32x16 (&acc)[4][2]) {
   const int lane = threadIdx.x & 63, h = lane >> 5, n = lane & 31;
@@ -145,7 +146,7 @@ __device__ __forceinline__ void step_mfma(const uint8_t* As, const uint8_t* Bs, 
   // slice kk run
   bf16x8 af[4], bfr[2];
 #pragma unroll
-  for (int ms = 0; ms < 4; ms++) {
+  for (int ms = 0; ms < NMS; ms++) {
     const int r = 32 * ms + n;
     af[ms] = *reinterpret_cast<const bf16x8*>(As + r * 128 + 16 * a_slot(r, 4 * h));
   }
@@ -156,7 +157,7 @@ __device__ __forceinline__ void step_mfma(const uint8_t* As, const uint8_t* Bs, 
     bf16x8 an[4], bn[2];
     if (kk < 3) {
 #pragma unroll
-      for (int ms = 0; ms < 4; ms++) {
+      for (int ms = 0; ms < NMS; ms++) {
         const int r = 32 * ms + n;
         an[ms] = *reinterpret_cast<const bf16x8*>(As + r * 128 + 16 * a_slot(r, 4 * h + kk + 1));
       }
@@ -164,13 +165,13 @@ __device__ __forceinline__ void step_mfma(const uint8_t* As, const uint8_t* Bs, 
       for (int f = 0; f < 2; f++) bn[f] = deq8(bc[f][kk + 1], sb[f][(kk + 1) >> 1]);
     }
 #pragma unroll
-    for (int ms = 0; ms < 4; ms++)
+    for (int ms = 0; ms < NMS; ms++)
 #pragma unroll
       for (int f = 0; f < 2; f++)
         acc[ms][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bfr[f], acc[ms][f], 0, 0, 0);
     if (kk < 3) {
 #pragma unroll
-      for (int ms = 0; ms < 4; ms++) af[ms] = an[ms];
+      for (int ms = 0; ms < NMS; ms++) af[ms] = an[ms];
 #pragma unroll
       for (int f = 0; f < 2; f++) bfr[f] = bn[f];
     }
@@ -187,7 +188,7 @@ __device__ __forceinline__ void step_mfma(const uint8_t* As, const uint8_t* Bs, 
 // written here were last read on the step before, which every wave has
 // finished (barrier). Loads past the last step repeat it (into buffers never
 // read again).
-template <int NW, int I>
+template <int NW, int NMS, int I>
 __device__ __forceinline__ void kstep(const TileCtx<NW>& c, int s, int nk, const uint8_t* As, const uint8_t* B0,
                                       const uint8_t* B1, const uint8_t* S0, const uint8_t* S1,
                                       f32x16 (&acc)[4][2]) {
@@ -196,11 +197,35 @@ __device__ __forceinline__ void kstep(const TileCtx<NW>& c, int s, int nk, const
   if (I % 2 == 0) dma_b(c, min(s / 2 + 1, (nk - 1) / 2), (I / 2 + 1) % 2);
   if (I % 4 == 0) dma_s(c, min(s / 4 + 1, (nk - 1) / 4), (I / 4 + 1) % 2);
   __builtin_amdgcn_sched_barrier(0);
-  step_mfma(As + (s % RA) * kABuf, ((I / 2) % 2) ? B1 : B0, I % 2, ((I / 4) % 2) ? S1 : S0, I % 4, acc);
+  step_mfma<NMS>(As + (s % RA) * kABuf, ((I / 2) % 2) ? B1 : B0, I % 2, ((I / 4) % 2) ? S1 : S0, I % 4, acc);
   __builtin_amdgcn_sched_barrier(0);
   constexpr int later = ((I % 2 == 0) ? 4 : 0) + ((I % 4 == 0) ? 1 : 0);  // issued after this step's A
   wait_vmcnt<(RA == 2) ? later : later + Cfg<NW>::kALoads>();
   step_barrier();
+}
+
+template <int NW, int NMS>
+__device__ __forceinline__ void kloop(const TileCtx<NW>& c, int nk, const uint8_t* lds_a, const uint8_t* B0,
+                                      const uint8_t* B1, const uint8_t* S0, const uint8_t* S1,
+                                      f32x16 (&acc)[4][2]) {
+  int s = 0;
+  for (; s + 8 <= nk; s += 8) {
+    kstep<NW, NMS, 0>(c, s, nk, lds_a, B0, B1, S0, S1, acc);
+    kstep<NW, NMS, 1>(c, s + 1, nk, lds_a, B0, B1, S0, S1, acc);
+    kstep<NW, NMS, 2>(c, s + 2, nk, lds_a, B0, B1, S0, S1, acc);
+    kstep<NW, NMS, 3>(c, s + 3, nk, lds_a, B0, B1, S0, S1, acc);
+    kstep<NW, NMS, 4>(c, s + 4, nk, lds_a, B0, B1, S0, S1, acc);
+    kstep<NW, NMS, 5>(c, s + 5, nk, lds_a, B0, B1, S0, S1, acc);
+    kstep<NW, NMS, 6>(c, s + 6, nk, lds_a, B0, B1, S0, S1, acc);
+    kstep<NW, NMS, 7>(c, s + 7, nk, lds_a, B0, B1, S0, S1, acc);
+  }
+  if (s < nk) kstep<NW, NMS, 0>(c, s, nk, lds_a, B0, B1, S0, S1, acc);
+  if (s + 1 < nk) kstep<NW, NMS, 1>(c, s + 1, nk, lds_a, B0, B1, S0, S1, acc);
+  if (s + 2 < nk) kstep<NW, NMS, 2>(c, s + 2, nk, lds_a, B0, B1, S0, S1, acc);
+  if (s + 3 < nk) kstep<NW, NMS, 3>(c, s + 3, nk, lds_a, B0, B1, S0, S1, acc);
+  if (s + 4 < nk) kstep<NW, NMS, 4>(c, s + 4, nk, lds_a, B0, B1, S0, S1, acc);
+  if (s + 5 < nk) kstep<NW, NMS, 5>(c, s + 5, nk, lds_a, B0, B1, S0, S1, acc);
+  if (s + 6 < nk) kstep<NW, NMS, 6>(c, s + 6, nk, lds_a, B0, B1, S0, S1, acc);
 }
 
 // NPROJ = 2: gate and up (wave w: gate rows n0+32w.. and the same up rows,
@@ -229,8 +254,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a)
   const int per = (n_items + 7) / 8;
   const int slot = blockIdx.x / 8, xcd = blockIdx.x % 8;
   if (slot >= per) return;
-  const int item = xcd * per + slot;
+  int item = xcd * per + slot;
   if (item >= n_items) return;
+  if (NPROJ == 1) item = n_items - 1 - item;  // down: most recently written mids first
   // items of one expert: n-tile major, its M tiles adjacent (they share weight rows)
   const int t_any = item / ntn;
   const int e = a.rt.tile_expert[t_any];
@@ -313,24 +339,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a)
   dma_s(c, 0, 0);
   wait_vmcnt<0>();
   step_barrier();
-  int s = 0;
-  for (; s + 8 <= nk; s += 8) {
-    kstep<NW, 0>(c, s, nk, lds_a, B0, B1, S0, S1, acc);
-    kstep<NW, 1>(c, s + 1, nk, lds_a, B0, B1, S0, S1, acc);
-    kstep<NW, 2>(c, s + 2, nk, lds_a, B0, B1, S0, S1, acc);
-    kstep<NW, 3>(c, s + 3, nk, lds_a, B0, B1, S0, S1, acc);
-    kstep<NW, 4>(c, s + 4, nk, lds_a, B0, B1, S0, S1, acc);
-    kstep<NW, 5>(c, s + 5, nk, lds_a, B0, B1, S0, S1, acc);
-    kstep<NW, 6>(c, s + 6, nk, lds_a, B0, B1, S0, S1, acc);
-    kstep<NW, 7>(c, s + 7, nk, lds_a, B0, B1, S0, S1, acc);
+  // 32-row blocks that hold rows of this tile: a partial last tile of an
+  // expert runs the k loop without the MFMAs of the rest
+  switch (min(4, (rows + 31) / 32)) {
+    case 1: kloop<NW, 1>(c, nk, lds_a, B0, B1, S0, S1, acc); break;
+    case 2: kloop<NW, 2>(c, nk, lds_a, B0, B1, S0, S1, acc); break;
+    case 3: kloop<NW, 3>(c, nk, lds_a, B0, B1, S0, S1, acc); break;
+    default: kloop<NW, 4>(c, nk, lds_a, B0, B1, S0, S1, acc); break;
   }
-  if (s < nk) kstep<NW, 0>(c, s, nk, lds_a, B0, B1, S0, S1, acc);
-  if (s + 1 < nk) kstep<NW, 1>(c, s + 1, nk, lds_a, B0, B1, S0, S1, acc);
-  if (s + 2 < nk) kstep<NW, 2>(c, s + 2, nk, lds_a, B0, B1, S0, S1, acc);
-  if (s + 3 < nk) kstep<NW, 3>(c, s + 3, nk, lds_a, B0, B1, S0, S1, acc);
-  if (s + 4 < nk) kstep<NW, 4>(c, s + 4, nk, lds_a, B0, B1, S0, S1, acc);
-  if (s + 5 < nk) kstep<NW, 5>(c, s + 5, nk, lds_a, B0, B1, S0, S1, acc);
-  if (s + 6 < nk) kstep<NW, 6>(c, s + 6, nk, lds_a, B0, B1, S0, S1, acc);
   wait_vmcnt<0>();  // the loads past the last step
 
   // epilogue; accumulator element r of lane l is (row 8(r/4) + 4(l/32) + r%4,
