@@ -2,7 +2,9 @@
 
 One step = the whole hot path on one batch: router logits + top-k (S1, S2),
 pair sort (S3), gate/up + SwiGLU (S4, S5), down (S6) and the weighted combine
-(S7), all through the C ABI, inputs resident in HBM.
+(S7), all through the C ABI, inputs resident in HBM. The decode step is one
+moe_nvfp4_layer call (router and top-k inside the gate/up launch); with
+--two-call it is moe_route_topk followed by moe_nvfp4_forward.
 
 Headline (value): decode, T=1, H=5120, I=2560, 256 experts, top-8, as HBM
 GB/s of algorithmic bytes (the 8 selected records of 22,118,412 B + the f32
@@ -24,7 +26,7 @@ profiles/traffic_decode_gateup.txt and reported only while the kernel source
 it was measured on is unchanged (its SHA-1 is recorded there), else null.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--prefill-steps P]
-       [--only decode|prefill] [--no-cpu-baseline]
+       [--only decode|prefill] [--no-cpu-baseline] [--two-call]
 Profiling helpers: --copy-calibration (device copies of 1 GiB, for the
 counter scale factor); --summarize-pmc DIR (per-kernel mean counter values
 per dispatch from a rocprofv3 --pmc output directory; no GPU needed).
@@ -82,14 +84,19 @@ class DecodeLeg:
         self.y = torch.empty((T, H), dtype=torch.int16, device="cuda")
         self.ws = wq.workspace(wq.moe_nvfp4_workspace_bytes(T, k, H, I, E))
         self.i = 0
+        self.two_call = False
 
     def step(self):
         c, r = self.c, self.i % ROTATE
         self.i += 1
-        wq.moe_route_topk(self.x[r], self.Wr, self.logits, c["T"], c["H"], c["E"], c["k"], self.idx[r],
-                          self.w[r])
-        wq.moe_nvfp4_forward(self.bank, self.x[r], c["T"], self.idx[r], self.w[r], c["k"], None, self.y, 0,
-                             self.ws)
+        if self.two_call:
+            wq.moe_route_topk(self.x[r], self.Wr, self.logits, c["T"], c["H"], c["E"], c["k"], self.idx[r],
+                              self.w[r])
+            wq.moe_nvfp4_forward(self.bank, self.x[r], c["T"], self.idx[r], self.w[r], c["k"], None, self.y, 0,
+                                 self.ws)
+        else:
+            wq.moe_nvfp4_layer(self.bank, self.x[r], self.Wr, c["T"], c["k"], None, self.logits, self.idx[r],
+                               self.w[r], self.y, 0, self.ws)
 
     def step_bytes(self, r):
         """algorithmic HBM bytes of the step that used activation r"""
@@ -99,10 +106,16 @@ class DecodeLeg:
         return n_unique * rec + c["H"] * c["E"] * 4 + 2 * c["T"] * c["H"] * 2
 
     def gateup_bytes(self, r):
+        """algorithmic bytes of the gate/up launch: gate and up of the selected
+        records, x, the bf16 mids written; in the one-call layer also the f32
+        router weights and the logits, idx and w written"""
         c = self.c
         n_unique = len(np.unique(self.idx_host[r]))
         per_proj = c["H"] * c["I"] // 2 + c["H"] * c["I"] // 16
-        return n_unique * 2 * per_proj + c["T"] * c["H"] * 2 + len(self.idx_host[r].ravel()) * c["I"] * 2
+        b = n_unique * 2 * per_proj + c["T"] * c["H"] * 2 + len(self.idx_host[r].ravel()) * c["I"] * 2
+        if not self.two_call:
+            b += c["H"] * c["E"] * 4 + c["T"] * (c["E"] + 2 * c["k"]) * 4
+        return b
 
 
 class PrefillLeg:
@@ -144,13 +157,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_gateup.txt")
 DECODE_SRC = os.path.join(ROOT, "weight_quantized_moe_amd", "csrc", "decode.hip")
 
 
-def recorded_traffic():
-    """Bytes per launch of the decode gate/up kernel from the committed counter
-    summary, if it was measured on the current kernel source; else None."""
+def recorded_traffic(name):
+    """Bytes per launch of the decode gate/up launch `name` from the committed
+    counter summary, if it was measured on that launch and the current kernel
+    source; else None."""
     try:
         fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line)
         src = hashlib.sha1(open(DECODE_SRC, "rb").read()).hexdigest()
-        if fields.get("source_sha1", "").strip() != src:
+        if fields.get("source_sha1", "").strip() != src or fields.get("launch", "").strip() != name:
             return None
         return int(float(fields["traffic_bytes_per_launch"]))
     except (OSError, KeyError, ValueError):
@@ -249,6 +263,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill"])
+    ap.add_argument("--two-call", action="store_true",
+                    help="decode step as moe_route_topk + moe_nvfp4_forward instead of moe_nvfp4_layer")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-pmc")
     args = ap.parse_args()
@@ -278,6 +294,7 @@ def main():
 
     # ---- decode leg
     dec = DecodeLeg(bank)
+    dec.two_call = args.two_call
     K, Wm = args.steps, args.warmup
     ms_total, wall_ms = timed(dec.step, K, Wm)
     dec.idx_host = dec.idx.cpu().numpy()
@@ -296,18 +313,20 @@ def main():
         dec.step()
     torch.cuda.synchronize()
     kern = {}
-    for name in ["router", "topk", "sort", "decode_gateup", "decode_down", "combine"]:
+    for name in ["router", "topk", "sort", "decode_route_gateup", "decode_gateup", "decode_down", "combine"]:
         avg, cnt = kernel_avg_ms(name)
         if cnt:
             kern[name] = (avg, cnt)
     wq.moe_profile_enable(False)
     for n_, (avg, cnt) in kern.items():
         log(f"  {n_:15s} {avg * 1e3:8.2f} us x {cnt}")
+    gu_name = "decode_gateup" if dec.two_call else "decode_route_gateup"
     gu_bytes = np.mean([dec.gateup_bytes(r) for r in rs])
-    gu_ms = kern["decode_gateup"][0]
+    gu_ms = kern[gu_name][0]
     achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
-    roofline = {"kernel": "decode_gateup", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
+    roofline = {"kernel": gu_name, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": recorded_traffic(gu_name),
                 "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(gu_ms * 1e3, 2)}
 
     out = {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": Wm,

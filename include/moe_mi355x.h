@@ -127,6 +127,29 @@ int moe_nvfp4_forward(const moe_nvfp4_bank* b, const uint16_t* x, int T, const i
                       const float* w, int k, const uint16_t* residual, void* y, unsigned flags,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* S1..S7 in one call: the router, the top-k with its softmax and the layer,
+ * i.e. moe_route_topk(x, w_router, logits, ...) followed by
+ * moe_nvfp4_forward(..., idx, w, ...), with the same results: logits f32
+ * [T][E], idx i32 [T][k] and w f32 [T][k] are written as moe_route_topk
+ * writes them, y as moe_nvfp4_forward writes it. Arguments, flags, alignment
+ * and workspace as for those two calls (w_router f32 [E][H], 16-byte
+ * aligned; logits 4-byte aligned; E <= 1024).
+ * For one token (T = 1, k <= 16, k*I*2 <= 65536 bytes of mids, no
+ * MOE_FORCE_PREFILL) the router and the top-k run inside the gate/up launch
+ * (two launches in all): the router logits pass through the workspace as
+ * 64-bit tags stamped with a per-call number, so the workspace needs no
+ * clearing between calls, must not be shared by calls that can overlap, and
+ * a region never written by this library matches a call number with
+ * probability 2^-32 per tag. The wait for the tags is bounded; if it ever
+ * expires (it does not in a correct launch), bit 0 of the 32-bit word at byte
+ * offset 8 of the workspace is set (a caller that checks it clears it first;
+ * the library never clears it), idx holds -1 and the call's outputs are
+ * invalid. Otherwise the call runs the router, top-k and forward launches in
+ * order. */
+int moe_nvfp4_layer(const moe_nvfp4_bank* b, const uint16_t* x, const float* w_router, int T, int k,
+                    const uint16_t* residual, float* logits, int32_t* idx, float* w, void* y,
+                    unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
+
 /* S8, resident linear in MLX affine 8-bit, group 64 ([PACK] residents and
  * q8-rule bullets): y[t][n] = sum_k x[t][k] * (scale[n][k/64]*q[n][k] +
  * bias[n][k/64]), f32 accumulation, bf16 out.

@@ -337,6 +337,79 @@ def test_forward_decode_full_shape(big_bank):
             check_bf16_of(yb, yf, "decode bf16")
 
 
+def gpu_layer(bank, x_bits, Wr, k, flags=0, residual=None, ws=None):
+    """moe_nvfp4_layer: router, top-k and layer in one call. Returns logits,
+    idx, w, y f32 and y bf16 (two calls, the second with the f32 flag off) and
+    the workspace's status word."""
+    T, H = x_bits.shape
+    E = Wr.shape[0]
+    if ws is None:
+        ws = wq.workspace(wq.moe_nvfp4_workspace_bytes(T, k, bank.H, bank.I, bank.E))
+    ws.view(torch.int32)[2] = 0  # the status word: set only if a bounded wait expires
+    xd = bf16_tensor(x_bits)
+    wrd = torch.from_numpy(np.ascontiguousarray(Wr)).to(DEV)
+    rd = None if residual is None else bf16_tensor(residual)
+    lg = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    yf = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    yb = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    wq.moe_nvfp4_layer(bank, xd, wrd, T, k, rd, lg, idx, w, yf, flags | wq.MOE_F32_OUT, ws)
+    wq.moe_nvfp4_layer(bank, xd, wrd, T, k, rd, lg, idx, w, yb, flags, ws)
+    torch.cuda.synchronize()
+    status = int(ws.view(torch.int32)[2].item())
+    return lg.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy(), yf.cpu().numpy(), to_np_bits(yb), status
+
+
+def check_layer_call(bank, name, x, Wr, k, residual=None, ws=None, flags=0):
+    """The one-call layer against the two-call path it stands for (router and
+    top-k by moe_route_topk, then moe_nvfp4_forward on its idx and w): logits,
+    idx, w and both outputs bit for bit; the separate path is held to the
+    oracle by the tests above and here again through the logits."""
+    lg, idx, w, yf, yb, status = gpu_layer(bank, x, Wr, k, flags, residual, ws)
+    assert status == 0, (name, status)
+    lg2, idx2, w2 = gpu_route(x, Wr, None, bank.E, k)
+    assert np.array_equal(lg.view(np.uint32), lg2.view(np.uint32)), (name, "logits")
+    assert np.array_equal(idx, idx2), (name, "idx")
+    assert np.array_equal(w.view(np.uint32), w2.view(np.uint32)), (name, "w")
+    yf2, yb2 = gpu_forward(bank, x, idx2, w2, k, flags, residual)
+    assert np.array_equal(yf.view(np.uint32), yf2.view(np.uint32)), (name, "y f32")
+    assert np.array_equal(yb, yb2), (name, "y bf16")
+    ref_lg = oracle.router_logits(x, Wr)
+    rms = np.sqrt(np.mean(ref_lg.astype(np.float64) ** 2))
+    assert np.max(np.abs(lg - ref_lg)) <= 1e-5 * rms, (name, "logits vs oracle")
+    say(f"layer call {name}: matches route + forward bit for bit")
+    return idx, w, yf
+
+
+def test_layer_call_tiny(tiny_bank):
+    bank, _ = tiny_bank
+    c = W.CONFIGS["tiny"]
+    x, Wr, _ = W.inputs("tiny")
+    check_layer_call(bank, "tiny T=4", x, Wr, c["k"])
+    check_layer_call(bank, "tiny T=4 grouped GEMM", x, Wr, c["k"], flags=4)
+    res = synth.activations(77, c["T"], c["H"])
+    ws = wq.workspace(wq.moe_nvfp4_workspace_bytes(1, 8, bank.H, bank.I, bank.E))
+    for t in range(c["T"]):  # one token: router and top-k inside the gate/up launch
+        for kk in (1, 2, 8, 16):
+            check_layer_call(bank, f"tiny token {t} k={kk}", x[t:t + 1], Wr, kk, res[t:t + 1] if t % 2 else None,
+                             ws if kk <= 8 else None)
+
+
+def test_layer_call_decode_full_shape(big_bank):
+    bank, _ = big_bank
+    c = W.CONFIGS["decode"]
+    ws = wq.workspace(wq.moe_nvfp4_workspace_bytes(1, c["k"], c["H"], c["I"], c["E"]))
+    for variant in range(3):  # one workspace: the tags of earlier calls stay behind
+        x, Wr, _ = W.inputs("decode", variant)
+        idx, w, yf = check_layer_call(bank, f"decode v{variant}", x, Wr, c["k"], ws=ws)
+        ridx, rw = oracle.route_topk(oracle.router_logits(x, Wr), c["k"])
+        assert np.array_equal(idx, ridx)
+        recs = host_records(c["bank_seed"], np.unique(idx), c["H"], c["I"])
+        ref_f, _ = oracle.moe_forward(recs, c["E"], c["H"], c["I"], x, ridx, rw)
+        check_f32(yf, ref_f, f"layer call decode v{variant}")
+
+
 def test_forward_batched_full_shape_sampled(big_bank):
     bank, _ = big_bank
     c = W.CONFIGS["batched"]

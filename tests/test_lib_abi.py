@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) >= 14, names
+    assert len(names) >= 15, names
     assert sorted(names) == sorted(wq.EXPORTS)
     L = C.CDLL(wq.LIB_PATH)
     for n in names:
@@ -89,6 +89,35 @@ def test_forward_validation_before_launch():
     broken = _bank()
     broken.stride = 4096
     assert call(args(), bank=broken) == wq.MOE_EINVAL
+
+
+def test_layer_validation_before_launch():
+    L = wq.lib()
+    b = _bank()
+    fake = C.c_void_p(1 << 26)
+    ws_need = L.moe_nvfp4_workspace_bytes(1, 2, 256, 128, 16)
+    args = lambda **kw: dict(dict(x=fake, wr=fake, T=1, k=2, res=None, lg=fake, idx=fake, w=fake, y=fake, flags=0,
+                                  ws=fake, wsb=ws_need), **kw)
+
+    def call(a, bank=b):
+        return L.moe_nvfp4_layer(C.byref(bank), a["x"], a["wr"], a["T"], a["k"], a["res"], a["lg"], a["idx"],
+                                 a["w"], a["y"], a["flags"], a["ws"], a["wsb"], None)
+
+    assert call(args(k=0)) == wq.MOE_ESHAPE
+    assert call(args(k=17)) == wq.MOE_ESHAPE
+    assert call(args(T=-1)) == wq.MOE_ESHAPE
+    assert call(args(wr=None)) == wq.MOE_EINVAL
+    assert call(args(lg=None)) == wq.MOE_EINVAL
+    assert call(args(idx=None)) == wq.MOE_EINVAL
+    assert call(args(wsb=ws_need - 1)) == wq.MOE_EWORKSPACE
+    assert call(args(wr=C.c_void_p((1 << 26) + 8))) == wq.MOE_EALIGN
+    assert call(args(lg=C.c_void_p((1 << 26) + 2))) == wq.MOE_EALIGN
+    assert call(args(x=C.c_void_p((1 << 26) + 2))) == wq.MOE_EALIGN
+    assert call(args(flags=wq.MOE_FORCE_DECODE | wq.MOE_FORCE_PREFILL)) == wq.MOE_EINVAL
+    assert call(args(T=0)) == wq.MOE_OK
+    bad = _bank(H=256, I=96)
+    assert call(args(), bank=bad) == wq.MOE_ESHAPE
+    assert b"layer" in L.moe_last_error()
 
 
 def test_route_sort_affine_rmsnorm_validation():

@@ -22,7 +22,7 @@ GATE, UP, DOWN = 0, 1, 2
 EXPORTS = [
     "moe_last_error", "moe_nvfp4_record_bytes", "moe_nvfp4_record_stride", "moe_nvfp4_bank_init",
     "moe_pack_nvfp4_bank", "moe_route_topk", "moe_sort_pairs",
-    "moe_nvfp4_workspace_bytes", "moe_nvfp4_forward", "affine8_g64_linear", "moe_rmsnorm",
+    "moe_nvfp4_workspace_bytes", "moe_nvfp4_forward", "moe_nvfp4_layer", "affine8_g64_linear", "moe_rmsnorm",
     "moe_nvfp4_dequant", "moe_profile_enable", "moe_profile_read",
 ]
 
@@ -69,6 +69,8 @@ def lib():
         L.moe_nvfp4_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.moe_nvfp4_forward.restype = i32
         L.moe_nvfp4_forward.argtypes = [bankp, vp, i32, vp, vp, i32, vp, vp, C.c_uint, vp, sz, vp]
+        L.moe_nvfp4_layer.restype = i32
+        L.moe_nvfp4_layer.argtypes = [bankp, vp, vp, i32, i32, vp, vp, vp, vp, vp, C.c_uint, vp, sz, vp]
         L.affine8_g64_linear.restype = i32
         L.affine8_g64_linear.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp]
         L.moe_rmsnorm.restype = i32
@@ -155,6 +157,12 @@ def moe_nvfp4_forward(bank, x, T, idx, w, k, residual, y, flags, workspace, stre
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().moe_nvfp4_forward(C.byref(bank), _ptr(x), T, _ptr(idx), _ptr(w), k, _ptr(residual), _ptr(y),
                                    flags, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def moe_nvfp4_layer(bank, x, w_router, T, k, residual, logits, idx, w, y, flags, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().moe_nvfp4_layer(C.byref(bank), _ptr(x), _ptr(w_router), T, k, _ptr(residual), _ptr(logits),
+                                 _ptr(idx), _ptr(w), _ptr(y), flags, _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def affine8_g64_linear(x, codes, scales, biases, T, K, N, y, stream=None):

@@ -3,6 +3,10 @@
 // error return means nothing was launched. See include/moe_mi355x.h.
 #include <hip/hip_runtime.h>
 
+#include <unistd.h>
+
+#include <atomic>
+#include <chrono>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -207,9 +211,11 @@ MOE_API int moe_route_topk(const uint16_t* x, const float* w_router, float* logi
 
 // ---- S3 sort ---------------------------------------------------------------------
 struct FwdLayout {
-  size_t counts, offsets, sorted, active, tile_e, tile_r, mid, part, total;
+  size_t counts, offsets, sorted, active, tile_e, tile_r, tags, mid, part, total;
   int max_tiles;
 };
+// counts area (256 bytes): [0] active experts, [1] tiles (pair sort),
+// [2] status word of the layer entry point
 
 static FwdLayout fwd_layout(int T, int k, int H, int I, int E) {
   FwdLayout L{};
@@ -228,6 +234,8 @@ static FwdLayout fwd_layout(int T, int k, int H, int I, int E) {
   o += up256((size_t)L.max_tiles * 4);
   L.tile_r = o;
   o += up256((size_t)L.max_tiles * 4);
+  L.tags = o;
+  o += up256((1024 + kFlatDecodeMaxK) * 8);  // router tags (1024 slots), then the routing record
   L.mid = o;
   o += up256(P * (size_t)I * 2);
   L.part = o;
@@ -266,32 +274,38 @@ static int prefill_min_pairs() {
   return v;
 }
 
-MOE_API int moe_nvfp4_forward(const moe_nvfp4_bank* b, const uint16_t* x, int T, const int32_t* idx,
-                              const float* w, int k, const uint16_t* residual, void* y,
-                              unsigned flags, void* workspace, size_t workspace_bytes,
-                              void* stream) {
-  BankView v;
-  int rc = bank_view(b, &v, "forward");
-  if (rc) return rc;
-  if (v.H % 64 || v.I % 64) return fail(MOE_ESHAPE, "forward: H=%d and I=%d must be multiples of 64", v.H, v.I);
-  if (T < 0) return fail(MOE_ESHAPE, "forward: T=%d < 0", T);
-  if (k < 1 || k > v.E || k > 64) return fail(MOE_ESHAPE, "forward: k=%d outside [1, min(E, 64)]", k);
+// Checks shared by the forward and layer entry points (idx and w are checked
+// by the callers: inputs of one, outputs of the other).
+static int layer_checks(const char* who, const BankView& v, const uint16_t* x, int T, int k,
+                        const uint16_t* residual, void* y, unsigned flags, void* workspace,
+                        size_t workspace_bytes, FwdLayout* L) {
+  if (v.H % 64 || v.I % 64) return fail(MOE_ESHAPE, "%s: H=%d and I=%d must be multiples of 64", who, v.H, v.I);
+  if (T < 0) return fail(MOE_ESHAPE, "%s: T=%d < 0", who, T);
+  if (k < 1 || k > v.E || k > 64) return fail(MOE_ESHAPE, "%s: k=%d outside [1, min(E, 64)]", who, k);
   if ((flags & MOE_FORCE_DECODE) && (flags & MOE_FORCE_PREFILL))
-    return fail(MOE_EINVAL, "forward: both FORCE flags set");
-  if (flags & ~(MOE_F32_OUT | MOE_FORCE_DECODE | MOE_FORCE_PREFILL)) return fail(MOE_EINVAL, "forward: unknown flags");
-  if ((long long)T * k > (1LL << 30)) return fail(MOE_ESHAPE, "forward: too many pairs");
+    return fail(MOE_EINVAL, "%s: both FORCE flags set", who);
+  if (flags & ~(MOE_F32_OUT | MOE_FORCE_DECODE | MOE_FORCE_PREFILL)) return fail(MOE_EINVAL, "%s: unknown flags", who);
+  if ((long long)T * k > (1LL << 30)) return fail(MOE_ESHAPE, "%s: too many pairs", who);
   if (T == 0) return MOE_OK;
-  if (!x || !idx || !w || !y || !workspace) return fail(MOE_EINVAL, "forward: null pointer");
-  if (!aligned(x, 16) || (residual && !aligned(residual, 8)) || !aligned(y, 16) || !aligned(idx, 4) ||
-      !aligned(w, 4))
-    return fail(MOE_EALIGN, "forward: x and y must be 16-byte aligned, residual 8-byte, idx/w 4-byte");
-  if (!aligned(workspace, 256)) return fail(MOE_EALIGN, "forward: workspace not 256-byte aligned");
-  const FwdLayout L = fwd_layout(T, k, v.H, v.I, v.E);
-  if (workspace_bytes < L.total)
-    return fail(MOE_EWORKSPACE, "forward: workspace %zu < %zu bytes", workspace_bytes, L.total);
+  if (!x || !y || !workspace) return fail(MOE_EINVAL, "%s: null pointer", who);
+  if (!aligned(x, 16) || (residual && !aligned(residual, 8)) || !aligned(y, 16))
+    return fail(MOE_EALIGN, "%s: x and y must be 16-byte aligned, residual 8-byte", who);
+  if (!aligned(workspace, 256)) return fail(MOE_EALIGN, "%s: workspace not 256-byte aligned", who);
+  *L = fwd_layout(T, k, v.H, v.I, v.E);
+  if (workspace_bytes < L->total)
+    return fail(MOE_EWORKSPACE, "%s: workspace %zu < %zu bytes", who, workspace_bytes, L->total);
+  return MOE_OK;
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
+// one token and at most kFlatDecodeMaxK pairs whose mids fit in 64 KiB of LDS
+static bool flat_path(const BankView& v, int T, int k, unsigned flags) {
+  return T == 1 && !(flags & MOE_FORCE_PREFILL) && k <= kFlatDecodeMaxK && (size_t)k * v.I * 2 <= 65536;
+}
+
+static int forward_run(const BankView& v, const uint16_t* x, int T, const int32_t* idx, const float* w, int k,
+                       const uint16_t* residual, void* y, unsigned flags, uint8_t* ws, const FwdLayout& L,
+                       hipStream_t s) {
+  int rc;
   RouteTables rt{};
   rt.counts = reinterpret_cast<int32_t*>(ws + L.counts);
   rt.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
@@ -306,7 +320,7 @@ MOE_API int moe_nvfp4_forward(const moe_nvfp4_bank* b, const uint16_t* x, int T,
   if (flags & MOE_FORCE_DECODE) prefill = false;
   if (flags & MOE_FORCE_PREFILL) prefill = true;
   const bool f32_out = (flags & MOE_F32_OUT) != 0;
-  if (!prefill && T == 1 && k <= kFlatDecodeMaxK && (size_t)k * v.I * 2 <= 65536)
+  if (!prefill && flat_path(v, T, k, flags))
     return hip_check(launch_flat_decode(v, x, idx, w, k, residual, mid, y, f32_out, s), "decode");
 
   if (prefill) {
@@ -333,6 +347,66 @@ MOE_API int moe_nvfp4_forward(const moe_nvfp4_bank* b, const uint16_t* x, int T,
   }
   return hip_check(launch_combine(part, idx, v.E, T, v.H, k, residual, y, f32_out, s),
                    "combine");
+}
+
+MOE_API int moe_nvfp4_forward(const moe_nvfp4_bank* b, const uint16_t* x, int T, const int32_t* idx,
+                              const float* w, int k, const uint16_t* residual, void* y,
+                              unsigned flags, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  BankView v;
+  int rc = bank_view(b, &v, "forward");
+  if (rc) return rc;
+  FwdLayout L;
+  rc = layer_checks("forward", v, x, T, k, residual, y, flags, workspace, workspace_bytes, &L);
+  if (rc || T == 0) return rc;
+  if (!idx || !w) return fail(MOE_EINVAL, "forward: null idx/w");
+  if (!aligned(idx, 4) || !aligned(w, 4)) return fail(MOE_EALIGN, "forward: idx/w must be 4-byte aligned");
+  return forward_run(v, x, T, idx, w, k, residual, y, flags, static_cast<uint8_t*>(workspace), L,
+                     static_cast<hipStream_t>(stream));
+}
+
+// ---- S1..S7 in one call ------------------------------------------------------------
+// Call numbers stamp the router tags in the workspace. They start from a
+// clock-derived value per process and skip 0 (the value a zero-filled
+// workspace holds).
+static uint32_t next_call_number() {
+  static std::atomic<uint32_t> counter{(uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() ^
+                                       ((uint32_t)getpid() << 16)};
+  uint32_t c;
+  do {
+    c = counter.fetch_add(1) + 1;
+  } while (c == 0);
+  return c;
+}
+
+MOE_API int moe_nvfp4_layer(const moe_nvfp4_bank* b, const uint16_t* x, const float* w_router, int T, int k,
+                            const uint16_t* residual, float* logits, int32_t* idx, float* w, void* y,
+                            unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
+  BankView v;
+  int rc = bank_view(b, &v, "layer");
+  if (rc) return rc;
+  if (v.E > 1024) return fail(MOE_ESHAPE, "layer: E=%d above 1024", v.E);
+  FwdLayout L;
+  rc = layer_checks("layer", v, x, T, k, residual, y, flags, workspace, workspace_bytes, &L);
+  if (rc || T == 0) return rc;
+  if (!w_router || !logits || !idx || !w) return fail(MOE_EINVAL, "layer: null w_router/logits/idx/w");
+  if (!aligned(w_router, 16) || !aligned(logits, 4) || !aligned(idx, 4) || !aligned(w, 4))
+    return fail(MOE_EALIGN, "layer: w_router must be 16-byte aligned, logits/idx/w 4-byte");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (flat_path(v, T, k, flags)) {
+    uint64_t* tags = reinterpret_cast<uint64_t*>(ws + L.tags);
+    uint32_t* status = reinterpret_cast<uint32_t*>(ws + L.counts) + 2;
+    uint16_t* mid = reinterpret_cast<uint16_t*>(ws + L.mid);
+    return hip_check(launch_flat_layer(v, x, w_router, k, residual, logits, idx, w, mid, tags, status,
+                                       next_call_number(), y, (flags & MOE_F32_OUT) != 0, s),
+                     "layer");
+  }
+  rc = hip_check(launch_router(x, w_router, logits, T, v.H, v.E, s), "router");
+  if (rc) return rc;
+  rc = hip_check(launch_topk(logits, T, v.E, k, idx, w, s), "topk");
+  if (rc) return rc;
+  return forward_run(v, x, T, idx, w, k, residual, y, flags, ws, L, s);
 }
 
 // ---- S8 affine8_g64 --------------------------------------------------------------

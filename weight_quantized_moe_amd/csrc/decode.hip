@@ -24,6 +24,7 @@
 #include "common.h"
 #include "gemv_util.h"
 #include "internal.h"
+#include "route_util.h"
 
 namespace moe {
 
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(kDecThreads) void gemv_kernel(DecodeArgs a) {
   const int nqb = (nquads + G * kQB - 1) / (G * kQB);  // quad batches per row
   const int p0 = (NPROJ == 2) ? 0 : 2;
   const uint8_t* rec = a.bank + (size_t)e * a.stride;
-  extern __shared__ uint32_t xs[];  // [MT][K/2]
+  extern __shared__ __attribute__((aligned(16))) uint32_t xs[];  // [MT][K/2]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rsub = lane / G, sub = lane % G;
   const int rows_per_block = a.passes * kDecWaves * R;
@@ -334,26 +335,25 @@ struct FlatArgs {
   int f32_out;
 };
 
-__global__ __launch_bounds__(kDecThreads) void flat_gateup_kernel(FlatArgs a) {
+// x [H] (bf16) -> LDS, as packed pairs
+__device__ __forceinline__ void flat_stage_x(const FlatArgs& a, uint32_t* xs) {
+  const u32x4* src = reinterpret_cast<const u32x4*>(a.x);
+  u32x4* dst = reinterpret_cast<u32x4*>(xs);
+  for (int i = threadIdx.x; i < a.H / 8; i += kDecThreads) dst[i] = src[i];
+}
+
+// The gate/up items of workgroup `blk` of `nblk`: wave w takes items
+// blk * 4 + w, then every nblk * 4-th; item (pair j, 4-row group), the pair's
+// expert s_idx[j] (-1: none).
+__device__ __forceinline__ void flat_gateup_items(const FlatArgs& a, const uint32_t* xs, const int* s_idx,
+                                                  int blk, int nblk) {
   constexpr int G = 16, R = 64 / G, QB = 5;
-  extern __shared__ uint32_t xs[];  // [H/2]
-  __shared__ int s_idx[kFlatDecodeMaxK];
   const int H = a.H, I = a.I, nquads = H / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rsub = lane / G, sub = lane % G;
-  if (threadIdx.x < a.k) {
-    const int e = a.idx[threadIdx.x];
-    s_idx[threadIdx.x] = (e >= 0 && e < a.E) ? e : -1;
-  }
-  {
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.x);
-    u32x4* dst = reinterpret_cast<u32x4*>(xs);
-    for (int i = threadIdx.x; i < H / 8; i += kDecThreads) dst[i] = src[i];
-  }
-  __syncthreads();
   const int groups = (I + R - 1) / R;
   const int n_items = a.k * groups;
-  for (int it = blockIdx.x * kDecWaves + wave; it < n_items; it += gridDim.x * kDecWaves) {
+  for (int it = blk * kDecWaves + wave; it < n_items; it += nblk * kDecWaves) {
     const int j = it / groups;
     const int r = (it % groups) * R + rsub;
     const int e = s_idx[j];
@@ -398,9 +398,21 @@ __global__ __launch_bounds__(kDecThreads) void flat_gateup_kernel(FlatArgs a) {
   }
 }
 
+__global__ __launch_bounds__(kDecThreads) void flat_gateup_kernel(FlatArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t xs[];  // [H/2]
+  __shared__ int s_idx[kFlatDecodeMaxK];
+  if (threadIdx.x < a.k) {
+    const int e = a.idx[threadIdx.x];
+    s_idx[threadIdx.x] = (e >= 0 && e < a.E) ? e : -1;
+  }
+  flat_stage_x(a, xs);
+  __syncthreads();
+  flat_gateup_items(a, xs, s_idx, blockIdx.x, gridDim.x);
+}
+
 __global__ __launch_bounds__(64 * kFlatDecodeMaxK) void flat_down_kernel(FlatArgs a) {
   constexpr int G = 8, R = 64 / G, QB = 5;
-  extern __shared__ uint32_t ms[];  // [k][I/2]
+  extern __shared__ __attribute__((aligned(16))) uint32_t ms[];  // [k][I/2]
   __shared__ int s_idx[kFlatDecodeMaxK];
   __shared__ float s_w[kFlatDecodeMaxK];
   __shared__ float s_d[kFlatDecodeMaxK][R];
@@ -469,6 +481,180 @@ __global__ __launch_bounds__(64 * kFlatDecodeMaxK) void flat_down_kernel(FlatArg
   }
 }
 
+// ---- one token, router and top-k in the gate/up launch -----------------------
+// A launch costs a few microseconds of start-up and drain, more than the router
+// (5 MB of f32 weights) and the top-k need, so the layer entry point runs both
+// in the gate/up launch. Its first E workgroups are router workgroups: each
+// computes one logit (expert e = blockIdx.x) with the router kernel's
+// arithmetic (thread j sums h = 4j, 4j + 1024, ... by f32 fma, then the wave
+// sums in wave order), publishes it in the workspace as a 64-bit tag (this
+// call's number above the logit's bits, one atomic store) and ends. The other
+// workgroups stage x and then need the routing. A workgroup that finds the
+// routing record of this call (k tagged words: call number above the expert
+// index) takes it from there; one that does not waits for all E tags and
+// selects the top-k itself. The first of these workgroups publishes the
+// record and writes logits, idx and w out (one writer: many stores to the
+// same words from all workgroups would queue behind each other). Tags and
+// records left by earlier
+// calls carry other numbers, so nothing is reset between calls. A router
+// workgroup waits for nothing, and workgroups are dispatched in id order, so
+// the waits end once the router workgroups have run, however few workgroups
+// fit on the GPU at a time. The wait is bounded anyway (about 0.1 s of
+// polling): past the bound the workgroup sets bit 0 of the workspace's status
+// word, writes idx as -1 and skips its items; the call's outputs are then
+// invalid.
+//
+// Selection, with 256 threads: thread t waits for the tags t, t + 256, ...
+// and turns each logit into a key (topk_key: unique, ordered as the
+// selection rule); wave 0 takes the largest key of each lane's stripe (keys
+// l, l + 64, ...); tau, the k-th largest of these 64 maxima, is at most the
+// k-th largest key, since k stripes reach it. So the top-k keys are all
+// >= tau, and the keys >= tau (at most k stripes' worth) are ranked among
+// themselves by counting: a key's rank among them is its rank among all keys.
+// A workgroup that starts once the record is out reads k words instead.
+struct RouteFuse {
+  const float* wr;    // [E][H] router weights, f32
+  float* logits;      // [E] out
+  int32_t* idx;       // [k] out (the down launch reads it as FlatArgs::idx)
+  float* w;           // [k] out (FlatArgs::w)
+  uint64_t* tags;     // [1024] workspace: router logits
+  uint64_t* route;    // [kFlatDecodeMaxK] workspace: the routing record
+  uint32_t* status;   // workspace status word
+  uint32_t call;      // this call's number
+};
+
+constexpr uint32_t kTagSpins = 1u << 20;
+
+__device__ __forceinline__ uint64_t ld_tag(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_tag(uint64_t* p, uint32_t call, uint32_t v) {
+  __hip_atomic_store(p, ((uint64_t)call << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(kDecThreads) void flat_route_gateup_kernel(FlatArgs a, RouteFuse r) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t xs[];  // [H/2]
+  __shared__ uint64_t keys[1024];
+  __shared__ float lv[1024];
+  __shared__ uint64_t lmax[64];
+  __shared__ uint64_t cand[kFlatDecodeMaxK * 16];  // k stripes of at most 1024 / 64 keys
+  __shared__ uint64_t tau;
+  __shared__ int ncand, failed, have_route;
+  __shared__ float red[kDecWaves];
+  __shared__ float sel_v[kFlatDecodeMaxK];
+  __shared__ int s_idx[kFlatDecodeMaxK];
+  const int H = a.H, E = a.E, k = a.k;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (blockIdx.x < (unsigned)E) {
+    const int e = blockIdx.x;
+    const float* row = r.wr + (size_t)e * H;
+    float acc = 0.0f;
+    for (int h = 4 * tid; h < H; h += 4 * kDecThreads) {
+      const f32x4 wv = *reinterpret_cast<const f32x4*>(row + h);
+      const u32x2 xv = *reinterpret_cast<const u32x2*>(a.x + h);
+      acc = fmaf(bf16_to_f32(xv.x & 0xFFFFu), wv.x, acc);
+      acc = fmaf(bf16_to_f32(xv.x >> 16), wv.y, acc);
+      acc = fmaf(bf16_to_f32(xv.y & 0xFFFFu), wv.z, acc);
+      acc = fmaf(bf16_to_f32(xv.y >> 16), wv.w, acc);
+    }
+    const float sw = wave_sum(acc);
+    if (lane == 0) red[wave] = sw;
+    __syncthreads();
+    if (tid == 0) st_tag(r.tags + e, r.call, __float_as_uint(((red[0] + red[1]) + red[2]) + red[3]));
+    return;
+  }
+  const int blk = blockIdx.x - E, nblk = gridDim.x - E;
+  if (tid == 0) {
+    ncand = 0;
+    failed = 0;
+    have_route = 1;
+    tau = ~0ull;
+  }
+  if (tid < kFlatDecodeMaxK) s_idx[tid] = -1;
+  __syncthreads();
+  flat_stage_x(a, xs);
+  // the routing record, if a workgroup has published it already
+  if (tid < k) {
+    const uint64_t v = ld_tag(r.route + tid);
+    if ((uint32_t)(v >> 32) == r.call)
+      s_idx[tid] = (int)(uint32_t)v;
+    else
+      have_route = 0;
+  }
+  __syncthreads();
+  if (!have_route) {
+    for (int e = tid; e < E; e += kDecThreads) {
+      uint64_t v = ld_tag(r.tags + e);
+      uint32_t n = 0;
+      while ((uint32_t)(v >> 32) != r.call) {
+        if (++n > kTagSpins) {
+          failed = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+        v = ld_tag(r.tags + e);
+      }
+      lv[e] = __uint_as_float((uint32_t)v);
+      keys[e] = topk_key(lv[e], e);
+    }
+    __syncthreads();
+    if (failed) {
+      if (tid < k) {
+        r.w[tid] = 0.0f;
+        r.idx[tid] = -1;
+      }
+      if (tid == 0) atomicOr(r.status, 1u);
+      return;
+    }
+    if (wave == 0) {
+      uint64_t m = 0;
+      for (int e = lane; e < E; e += 64) m = max(m, keys[e]);
+      lmax[lane] = m;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const uint64_t m = lmax[lane];
+      int ahead = 0;
+      for (int j = 0; j < 64; j++) ahead += lmax[j] > m ? 1 : 0;
+      if (ahead == k - 1 && m != 0) tau = m;  // exactly one lane
+    }
+    __syncthreads();
+    constexpr int kCand = kFlatDecodeMaxK * 16;
+    for (int e = tid; e < E; e += kDecThreads)
+      if (keys[e] >= tau) {
+        const int pos = atomicAdd(&ncand, 1);
+        if (pos < kCand) cand[pos] = keys[e];
+      }
+    __syncthreads();
+    const int nc = min(ncand, kCand);
+    for (int i = tid; i < nc; i += kDecThreads) {
+      const uint64_t c = cand[i];
+      int rank = 0;
+      for (int j = 0; j < nc; j++) rank += cand[j] > c ? 1 : 0;
+      if (rank < k) {
+        const int e = topk_key_expert(c);
+        s_idx[rank] = e;
+        sel_v[rank] = lv[e];
+      }
+    }
+    __syncthreads();
+    // one workgroup writes the outputs and the record (the first gate/up
+    // workgroup, which always selects: no record exists before it does)
+    if (blk == 0) {
+      if (wave == 0) {
+        const float wl = topk_softmax(sel_v, k, lane);
+        if (lane < k) {
+          r.w[lane] = wl;
+          r.idx[lane] = s_idx[lane];
+          st_tag(r.route + lane, r.call, (uint32_t)s_idx[lane]);
+        }
+      }
+      for (int e = tid; e < E; e += kDecThreads) r.logits[e] = lv[e];
+    }
+  }
+  flat_gateup_items(a, xs, s_idx, blk, nblk);
+}
+
 static int flat_blocks(int n_items) {
   // one item per wave: every wave's loads are issued at once and the hardware
   // starts the next workgroup on a SIMD as soon as one finishes (measured
@@ -478,9 +664,8 @@ static int flat_blocks(int n_items) {
   return b < 1 ? 1 : b;
 }
 
-hipError_t launch_flat_decode(const BankView& b, const uint16_t* x, const int32_t* idx,
-                              const float* w, int k, const uint16_t* residual, uint16_t* mid,
-                              void* y, bool f32_out, hipStream_t s) {
+static FlatArgs flat_args(const BankView& b, const uint16_t* x, const int32_t* idx, const float* w, int k,
+                          const uint16_t* residual, uint16_t* mid, void* y, bool f32_out) {
   FlatArgs a{};
   a.bank = b.base;
   a.stride = b.stride;
@@ -500,14 +685,48 @@ hipError_t launch_flat_decode(const BankView& b, const uint16_t* x, const int32_
   a.mid = mid;
   a.y = y;
   a.f32_out = f32_out ? 1 : 0;
+  return a;
+}
+
+static hipError_t launch_flat_down(const FlatArgs& a, hipStream_t s) {
+  launch_kernel("decode_down", flat_down_kernel, dim3((a.H + 7) / 8), dim3(64 * a.k),
+                (uint32_t)(a.k * a.I * 2), s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_flat_decode(const BankView& b, const uint16_t* x, const int32_t* idx,
+                              const float* w, int k, const uint16_t* residual, uint16_t* mid,
+                              void* y, bool f32_out, hipStream_t s) {
+  const FlatArgs a = flat_args(b, x, idx, w, k, residual, mid, y, f32_out);
   const int groups = (b.I + 3) / 4;
   launch_kernel("decode_gateup", flat_gateup_kernel, dim3(flat_blocks(k * groups)), dim3(kDecThreads),
                 (uint32_t)(b.H * 2), s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  launch_kernel("decode_down", flat_down_kernel, dim3((b.H + 7) / 8), dim3(64 * k),
-                (uint32_t)(k * b.I * 2), s, a);
-  return hipGetLastError();
+  return launch_flat_down(a, s);
+}
+
+hipError_t launch_flat_layer(const BankView& b, const uint16_t* x, const float* wr, int k,
+                             const uint16_t* residual, float* logits, int32_t* idx, float* w,
+                             uint16_t* mid, uint64_t* tags, uint32_t* status, uint32_t call, void* y,
+                             bool f32_out, hipStream_t s) {
+  const FlatArgs a = flat_args(b, x, idx, w, k, residual, mid, y, f32_out);
+  RouteFuse r{};
+  r.wr = wr;
+  r.logits = logits;
+  r.idx = idx;
+  r.w = w;
+  r.tags = tags;
+  r.route = tags + 1024;
+  r.status = status;
+  r.call = call;
+  const int groups = (b.I + 3) / 4;
+  const dim3 grid(b.E + flat_blocks(k * groups)), block(kDecThreads);
+  const uint32_t lds = b.H * 2;
+  launch_kernel("decode_route_gateup", flat_route_gateup_kernel, grid, block, lds, s, a, r);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_flat_down(a, s);
 }
 
 // ---- S7: weighted combine (the routing weight is already in `part`) -----------

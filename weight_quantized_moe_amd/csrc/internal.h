@@ -56,6 +56,15 @@ constexpr int kFlatDecodeMaxK = 16;
 hipError_t launch_flat_decode(const BankView& b, const uint16_t* x, const int32_t* idx,
                               const float* w, int k, const uint16_t* residual, uint16_t* mid,
                               void* y, bool f32_out, hipStream_t s);
+// router + top-k + gate/up in one launch, then down (T = 1, the same limits
+// as launch_flat_decode, E <= 1024): logits [E], idx [k] and w [k] are
+// written; tags [E] and status live in the workspace; call is this call's
+// number (tags carrying it are this call's logits); tags spans 1024 router
+// tags followed by kFlatDecodeMaxK routing-record words
+hipError_t launch_flat_layer(const BankView& b, const uint16_t* x, const float* wr, int k,
+                             const uint16_t* residual, float* logits, int32_t* idx, float* w,
+                             uint16_t* mid, uint64_t* tags, uint32_t* status, uint32_t call, void* y,
+                             bool f32_out, hipStream_t s);
 // y[t] = residual[t] + sum_j part[t*k+j] (j ascending); pairs with idx
 // outside [0, E) contribute nothing
 hipError_t launch_combine(const float* part, const int32_t* idx, int E, int T, int H, int k,

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void affine8_kernel(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ scales,
                                                       const uint16_t* __restrict__ biases, int T,
                                                       int K, int N, uint16_t* __restrict__ y) {
-  extern __shared__ uint32_t lds[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   uint32_t* xs = lds;                                          // [kAffTok][K/2] bf16 pairs
   float* xc = reinterpret_cast<float*>(lds + kAffTok * (K / 2));  // [kAffTok][K/16]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

@@ -9,6 +9,7 @@
 // the readings the C header states.
 #include "common.h"
 #include "internal.h"
+#include "route_util.h"
 
 namespace moe {
 
@@ -71,7 +72,7 @@ hipError_t launch_router(const uint16_t* x, const float* Wr, float* logits, int 
 // quarter q) counts the candidates of quarter q that are ahead of the
 // candidates c, c+256, ...; the four partial counts are added in LDS. The k
 // candidates with rank < k are the top-k in order; the softmax over them is
-// f32, summed in slot order.
+// f32, summed in slot order (topk_softmax).
 
 __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ logits, int T, int E,
                                                     int k, int32_t* __restrict__ idx,
@@ -106,13 +107,10 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ lo
   __syncthreads();
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    const float top0 = sel_v[0];
-    const float a = (lane < k) ? expf(sel_v[lane] - top0) : 0.0f;
-    float sum = 0.0f;
-    for (int j = 0; j < k; j++) sum += __shfl(a, j, 64);
+    const float wl = topk_softmax(sel_v, k, lane);
     if (lane < k) {
       idx[(size_t)t * k + lane] = sel_e[lane];
-      w[(size_t)t * k + lane] = a / sum;
+      w[(size_t)t * k + lane] = wl;
     }
   }
 }
