@@ -335,11 +335,27 @@ struct FlatArgs {
   int f32_out;
 };
 
+// n 16-byte pieces global -> LDS by the workgroup: the first U rounds of
+// loads are all issued before any store, so they cost one round trip
+template <int U>
+__device__ __forceinline__ void stage_lds(const u32x4* src, u32x4* dst, int n) {
+  u32x4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    const int i = threadIdx.x + u * blockDim.x;
+    if (i < n) v[u] = src[i];
+  }
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    const int i = threadIdx.x + u * blockDim.x;
+    if (i < n) dst[i] = v[u];
+  }
+  for (int i = threadIdx.x + U * blockDim.x; i < n; i += blockDim.x) dst[i] = src[i];
+}
+
 // x [H] (bf16) -> LDS, as packed pairs
 __device__ __forceinline__ void flat_stage_x(const FlatArgs& a, uint32_t* xs) {
-  const u32x4* src = reinterpret_cast<const u32x4*>(a.x);
-  u32x4* dst = reinterpret_cast<u32x4*>(xs);
-  for (int i = threadIdx.x; i < a.H / 8; i += kDecThreads) dst[i] = src[i];
+  stage_lds<3>(reinterpret_cast<const u32x4*>(a.x), reinterpret_cast<u32x4*>(xs), a.H / 8);
 }
 
 // The gate/up items of workgroup `blk` of `nblk`: wave w takes items
