@@ -275,12 +275,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a)
   __shared__ __attribute__((aligned(16))) uint8_t lds_s0[NW * kSGroup];
   __shared__ __attribute__((aligned(16))) uint8_t lds_s1[NW * kSGroup];
   __shared__ int src_row[kPM];
+  __shared__ int out_pair[NPROJ == 1 ? kPM : 1];   // down: pair id of each tile row
+  __shared__ float out_w[NPROJ == 1 ? kPM : 1];    // down: its routing weight
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (tid < kPM) {
     // rows past the tile's end read a valid stand-in row; their outputs are not stored
     const int r = min(tid, rows - 1);
-    src_row[tid] = (NPROJ == 2) ? a.rt.sorted[row0 + r] / a.k : row0 + r;
+    if (NPROJ == 2) {
+      src_row[tid] = a.rt.sorted[row0 + r] / a.k;
+    } else {
+      src_row[tid] = row0 + r;
+      const int pair = a.rt.sorted[row0 + r];
+      out_pair[tid] = pair;
+      out_w[tid] = a.w[pair];
+    }
   }
   TileCtx<NW> c;
   c.in = uniform_ptr(a.in);
@@ -365,8 +374,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a)
           a.mid[(size_t)(row0 + row) * N + n] = f32_to_bf16(silu_mul(g, u));
         }
       } else {
-        const int pair = a.rt.sorted[row0 + row];
-        const float wp = a.w[pair] * t_p[0];
+        const int pair = out_pair[row];
+        const float wp = out_w[row] * t_p[0];
 #pragma unroll
         for (int f = 0; f < 2; f++) {
           const int n = n0 + kWR * wave + 32 * f + (lane & 31);
