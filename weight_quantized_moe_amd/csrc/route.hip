@@ -66,58 +66,95 @@ hipError_t launch_router(const uint16_t* x, const float* Wr, float* logits, int 
 
 // ---- S2: top-k + softmax ------------------------------------------------------
 // Order: larger logit first, then lower expert index; -0 and +0 are equal; a
-// NaN ranks below every number. Each logit becomes an unsigned key that
-// preserves that order, and candidate e's rank is the number of candidates
-// ahead of it. One block of 1024 threads per token: thread (candidate slot c,
-// quarter q) counts the candidates of quarter q that are ahead of the
-// candidates c, c+256, ...; the four partial counts are added in LDS. The k
-// candidates with rank < k are the top-k in order; the softmax over them is
-// f32, summed in slot order (topk_softmax).
+// NaN ranks below every number (topk_key turns a logit and its index into one
+// unique 64-bit key with that order). One wave per token, four tokens per
+// workgroup. Lane l owns the stripe of experts l, l + 64, ... (NS stripes,
+// 64 NS >= E). tau, the k-th largest of the 64 stripe maxima, is at most the
+// k-th largest key (k stripes reach it), so every top-k key is >= tau, and
+// the keys >= tau (at most k NS) are ranked among themselves by counting:
+// a key's rank among them is its rank among all keys. The softmax over the
+// k selected logits is f32, summed in slot order (topk_softmax).
+constexpr int kTopkWaves = 4;
 
-__global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ logits, int T, int E,
-                                                    int k, int32_t* __restrict__ idx,
-                                                    float* __restrict__ w) {
-  const int t = blockIdx.x;
-  __shared__ uint32_t key[1024];
-  __shared__ uint16_t prank[4][1024];
-  __shared__ float sel_v[64];
-  __shared__ int sel_e[64];
+template <int NS>
+__global__ __launch_bounds__(64 * kTopkWaves) void topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                              int k, int32_t* __restrict__ idx,
+                                                              float* __restrict__ w) {
+  __shared__ uint64_t lmax_all[kTopkWaves][64];
+  __shared__ uint64_t cand_all[kTopkWaves][64 * NS];
+  __shared__ float sel_v_all[kTopkWaves][64];
+  __shared__ int sel_e_all[kTopkWaves][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * kTopkWaves + wave;
+  if (t >= T) return;
+  uint64_t* lmax = lmax_all[wave];
+  uint64_t* cand = cand_all[wave];
+  float* sel_v = sel_v_all[wave];
+  int* sel_e = sel_e_all[wave];
   const float* lt = logits + (size_t)t * E;
-  for (int e = threadIdx.x; e < E; e += 1024) key[e] = order_key(lt[e]);
-  __syncthreads();
-  const int c = threadIdx.x & 255, q = threadIdx.x >> 8;
-  const int j0 = q * E / 4, j1 = (q + 1) * E / 4;
-  for (int e = c; e < E; e += 256) {
-    const uint32_t ke = key[e];
-    int n = 0;
-    for (int j = j0; j < j1; j++) {
-      const uint32_t kj = key[j];
-      n += (kj > ke || (kj == ke && j < e)) ? 1 : 0;
-    }
-    prank[q][e] = (uint16_t)n;
+  uint64_t key[NS];
+  uint64_t m = 0;
+#pragma unroll
+  for (int i = 0; i < NS; i++) {
+    const int e = lane + 64 * i;
+    key[i] = (e < E) ? topk_key(lt[e], e) : 0;
+    m = max(m, key[i]);
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 1024) {
-    const int rank = prank[0][e] + prank[1][e] + prank[2][e] + prank[3][e];
-    if (rank < k) {
-      sel_v[rank] = lt[e];
+  lmax[lane] = m;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  int ahead = 0;
+#pragma unroll
+  for (int j = 0; j < 64; j++) ahead += lmax[j] > m ? 1 : 0;
+  // the lane whose stripe maximum has k - 1 larger ones (keys are unique and
+  // non-zero; lanes without a key hold 0 and never qualify)
+  const uint64_t hit = __ballot(ahead == k - 1 && m != 0);
+  const int src = hit ? __builtin_ctzll(hit) : 0;
+  const uint64_t tau = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(m >> 32), src) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)m, src);
+  int nc = 0;
+#pragma unroll
+  for (int i = 0; i < NS; i++) {
+    const bool c = key[i] != 0 && key[i] >= tau;
+    const uint64_t mask = __ballot(c);
+    const int pos = nc + __popcll(mask & ((1ull << lane) - 1ull));
+    if (c && pos < 64 * NS) cand[pos] = key[i];
+    nc += __popcll(mask);
+  }
+  nc = min(nc, 64 * NS);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  for (int i0 = 0; i0 < nc; i0 += 64) {
+    const int i = i0 + lane;
+    const uint64_t c = (i < nc) ? cand[i] : 0;
+    int rank = 0;
+    for (int j = 0; j < nc; j++) rank += cand[j] > c ? 1 : 0;
+    if (i < nc && rank < k) {
+      const int e = topk_key_expert(c);
       sel_e[rank] = e;
+      sel_v[rank] = lt[e];
     }
   }
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const float wl = topk_softmax(sel_v, k, lane);
-    if (lane < k) {
-      idx[(size_t)t * k + lane] = sel_e[lane];
-      w[(size_t)t * k + lane] = wl;
-    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  const float wl = topk_softmax(sel_v, k, lane);
+  if (lane < k) {
+    idx[(size_t)t * k + lane] = sel_e[lane];
+    w[(size_t)t * k + lane] = wl;
   }
 }
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                        hipStream_t s) {
-  launch_kernel("topk", topk_kernel, dim3(T), dim3(1024), 0, s, logits, T, E, k, idx, w);
+  const dim3 grid((T + kTopkWaves - 1) / kTopkWaves), block(64 * kTopkWaves);
+  const int ns = (E + 63) / 64;
+  if (ns <= 1)
+    launch_kernel("topk", topk_kernel<1>, grid, block, 0, s, logits, T, E, k, idx, w);
+  else if (ns <= 2)
+    launch_kernel("topk", topk_kernel<2>, grid, block, 0, s, logits, T, E, k, idx, w);
+  else if (ns <= 4)
+    launch_kernel("topk", topk_kernel<4>, grid, block, 0, s, logits, T, E, k, idx, w);
+  else if (ns <= 8)
+    launch_kernel("topk", topk_kernel<8>, grid, block, 0, s, logits, T, E, k, idx, w);
+  else
+    launch_kernel("topk", topk_kernel<16>, grid, block, 0, s, logits, T, E, k, idx, w);
   return hipGetLastError();
 }
 
