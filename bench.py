@@ -235,7 +235,7 @@ def prefill_leg(bank, P):
     for _ in range(P):
         pre.step()
     torch.cuda.synchronize()
-    pk = {n_: kernel_avg_ms(n_) for n_ in ["topk", "sort", "prefill_gateup", "prefill_down", "combine"]}
+    pk = {n_: kernel_avg_ms(n_) for n_ in ["topk", "sort", "sort_count", "sort_scan", "sort_place", "prefill_gateup", "prefill_down", "combine"]}
     pk = {n_: v for n_, v in pk.items() if v[1]}
     wq.moe_profile_enable(False)
     for n_, (avg, cnt) in pk.items():

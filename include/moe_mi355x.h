@@ -109,6 +109,16 @@ int moe_route_topk(const uint16_t* x, const float* w_router, float* logits, int 
 int moe_sort_pairs(const int32_t* idx, int T, int k, int E, int32_t* offsets, int32_t* sorted,
                    void* stream);
 
+/* The same sort with a caller scratch buffer, the form moe_nvfp4_forward uses
+ * internally: above 2048 pairs it runs on many workgroups (per-chunk counts,
+ * a scan, per-chunk placement) instead of one. Same results as
+ * moe_sort_pairs, bit for bit. workspace: device, 4-byte aligned, at least
+ * moe_sort_workspace_bytes(T, k, E) bytes (0 on bad arguments), not shared
+ * with a concurrent call. */
+size_t moe_sort_workspace_bytes(int T, int k, int E);
+int moe_sort_pairs_ws(const int32_t* idx, int T, int k, int E, int32_t* offsets, int32_t* sorted,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* S3..S7, the layer (shape rules: H and I multiples of 64, T >= 0,
  * 1 <= k <= min(E, 64)):
  *   y[t] = residual[t] + sum_j w[t][j] * down_e( bf16( silu(gate_e x[t]) * up_e x[t] ) )

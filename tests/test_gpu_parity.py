@@ -257,6 +257,32 @@ def test_sort_bit_exact(T, k, E):
     assert np.array_equal(srt.cpu().numpy(), rsrt)
 
 
+@pytest.mark.parametrize("T,k,E", [(8192, 8, 256), (300, 8, 256), (257, 8, 16), (5000, 3, 1024), (2000, 64, 1000)])
+def test_sort_multi_workgroup_bit_exact(T, k, E):
+    """moe_sort_pairs_ws: above 2048 pairs the count / scan / place launches;
+    the same stable order and offsets as the oracle (ragged last chunks, E up
+    to 1024, a Zipf-skewed case with large groups)."""
+    rng = np.random.default_rng(T * 13 + k)
+    if T == 8192:
+        _, _, logits = W.inputs("prefill")
+        idx, _ = oracle.route_topk(logits, k)
+    else:
+        idx = rng.integers(0, E, (T, k)).astype(np.int32)
+    idx[0, 0] = -1 if T == 5000 else idx[0, 0]  # one dropped pair
+    offs = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    srt = torch.full((T * k,), -7, dtype=torch.int32, device=DEV)
+    ws = torch.empty(wq.moe_sort_workspace_bytes(T, k, E) // 4 + 1, dtype=torch.int32, device=DEV)
+    wq.moe_sort_pairs_ws(torch.from_numpy(idx).to(DEV), T, k, E, offs, srt, ws)
+    torch.cuda.synchronize()
+    flat = idx.ravel()
+    keep = np.nonzero((flat >= 0) & (flat < E))[0]  # the oracle takes valid pairs only
+    roff, rsrt = oracle.sort_pairs(flat[keep], E)
+    assert np.array_equal(offs.cpu().numpy(), roff)
+    n = int(roff[-1])
+    assert n == keep.size
+    assert np.array_equal(srt.cpu().numpy()[:n], keep[rsrt])
+
+
 def test_sort_drops_invalid_indices():
     idx = np.array([[3, -1], [7, 3], [16, 0]], np.int32)
     offs = torch.empty(17, dtype=torch.int32, device=DEV)

@@ -21,7 +21,7 @@ GATE, UP, DOWN = 0, 1, 2
 
 EXPORTS = [
     "moe_last_error", "moe_nvfp4_record_bytes", "moe_nvfp4_record_stride", "moe_nvfp4_bank_init",
-    "moe_pack_nvfp4_bank", "moe_route_topk", "moe_sort_pairs",
+    "moe_pack_nvfp4_bank", "moe_route_topk", "moe_sort_pairs", "moe_sort_workspace_bytes", "moe_sort_pairs_ws",
     "moe_nvfp4_workspace_bytes", "moe_nvfp4_forward", "moe_nvfp4_layer", "affine8_g64_linear", "moe_rmsnorm",
     "moe_nvfp4_dequant", "moe_profile_enable", "moe_profile_read",
 ]
@@ -65,6 +65,10 @@ def lib():
         L.moe_route_topk.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
         L.moe_sort_pairs.restype = i32
         L.moe_sort_pairs.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+        L.moe_sort_workspace_bytes.restype = sz
+        L.moe_sort_workspace_bytes.argtypes = [i32, i32, i32]
+        L.moe_sort_pairs_ws.restype = i32
+        L.moe_sort_pairs_ws.argtypes = [vp, i32, i32, i32, vp, vp, vp, sz, vp]
         L.moe_nvfp4_workspace_bytes.restype = sz
         L.moe_nvfp4_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.moe_nvfp4_forward.restype = i32
@@ -146,6 +150,16 @@ def moe_route_topk(x, w_router, logits, T, H, E, k, idx, w, stream=None):
 
 def moe_sort_pairs(idx, T, k, E, offsets, sorted_, stream=None):
     _check(lib().moe_sort_pairs(_ptr(idx), T, k, E, _ptr(offsets), _ptr(sorted_), _stream(stream)))
+
+
+def moe_sort_workspace_bytes(T, k, E):
+    return lib().moe_sort_workspace_bytes(T, k, E)
+
+
+def moe_sort_pairs_ws(idx, T, k, E, offsets, sorted_, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().moe_sort_pairs_ws(_ptr(idx), T, k, E, _ptr(offsets), _ptr(sorted_), _ptr(workspace), ws_bytes,
+                                   _stream(stream)))
 
 
 # ---- the layer ----------------------------------------------------------------------

@@ -211,7 +211,7 @@ MOE_API int moe_route_topk(const uint16_t* x, const float* w_router, float* logi
 
 // ---- S3 sort ---------------------------------------------------------------------
 struct FwdLayout {
-  size_t counts, offsets, sorted, active, tile_e, tile_r, tags, mid, part, total;
+  size_t counts, offsets, sorted, active, tile_e, tile_r, hist, tags, mid, part, total;
   int max_tiles;
 };
 // counts area (256 bytes): [0] active experts, [1] tiles (pair sort),
@@ -234,6 +234,8 @@ static FwdLayout fwd_layout(int T, int k, int H, int I, int E) {
   o += up256((size_t)L.max_tiles * 4);
   L.tile_r = o;
   o += up256((size_t)L.max_tiles * 4);
+  L.hist = o;
+  o += up256((size_t)sort_hist_ints((int)(P < (1u << 30) ? P : 0), E) * 4);
   L.tags = o;
   o += up256((1024 + kFlatDecodeMaxK) * 8);  // router tags (1024 slots), then the routing record
   L.mid = o;
@@ -256,6 +258,30 @@ MOE_API int moe_sort_pairs(const int32_t* idx, int T, int k, int E, int32_t* off
   rt.offsets = offsets;
   rt.sorted = sorted;
   return hip_check(launch_sort(idx, (int)P, E, rt, 0, 0, s), "sort");
+}
+
+MOE_API size_t moe_sort_workspace_bytes(int T, int k, int E) {
+  if (T < 0 || k < 1 || k > 64 || E < 1 || E > 1024) return 0;
+  const long long P = (long long)T * k;
+  if (P > (1LL << 30)) return 0;
+  return (size_t)sort_hist_ints((int)P, E) * 4 + 4;
+}
+
+MOE_API int moe_sort_pairs_ws(const int32_t* idx, int T, int k, int E, int32_t* offsets, int32_t* sorted,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (T < 0 || k < 1 || k > 64) return fail(MOE_ESHAPE, "sort: T=%d k=%d", T, k);
+  if (E < 1 || E > 1024) return fail(MOE_ESHAPE, "sort: E=%d outside [1, 1024]", E);
+  if (!idx || !offsets || !sorted || !workspace) return fail(MOE_EINVAL, "sort: null pointer");
+  const long long P = (long long)T * k;
+  if (P > (1LL << 30)) return fail(MOE_ESHAPE, "sort: too many pairs");
+  if (!aligned(workspace, 4)) return fail(MOE_EALIGN, "sort: workspace not 4-byte aligned");
+  if (workspace_bytes < moe_sort_workspace_bytes(T, k, E))
+    return fail(MOE_EWORKSPACE, "sort: workspace %zu < %zu bytes", workspace_bytes, moe_sort_workspace_bytes(T, k, E));
+  RouteTables rt{};
+  rt.offsets = offsets;
+  rt.sorted = sorted;
+  rt.hist = static_cast<int32_t*>(workspace);
+  return hip_check(launch_sort(idx, (int)P, E, rt, 0, 0, static_cast<hipStream_t>(stream)), "sort");
 }
 
 // ---- S3..S7 forward --------------------------------------------------------------
@@ -313,6 +339,7 @@ static int forward_run(const BankView& v, const uint16_t* x, int T, const int32_
   rt.active = reinterpret_cast<int32_t*>(ws + L.active);
   rt.tile_expert = reinterpret_cast<int32_t*>(ws + L.tile_e);
   rt.tile_row0 = reinterpret_cast<int32_t*>(ws + L.tile_r);
+  rt.hist = reinterpret_cast<int32_t*>(ws + L.hist);
   uint16_t* mid = reinterpret_cast<uint16_t*>(ws + L.mid);
   float* part = reinterpret_cast<float*>(ws + L.part);
   const int P = T * k;

@@ -22,6 +22,7 @@ struct RouteTables {
   int32_t* counts;      // [0] n_active, [1] n_tiles
   int32_t* tile_expert; // [max_tiles] grouped-GEMM tiles: expert
   int32_t* tile_row0;   // [max_tiles] first sorted slot of the tile
+  int32_t* hist;        // [sort_hist_ints(P, E)] scratch of the multi-workgroup sort, or null
 };
 
 // router: logits = x . Wr^T with Wr f32 [E][H]; one block per (expert, 8 tokens)
@@ -32,7 +33,10 @@ hipError_t launch_router(const uint16_t* x, const float* Wr, float* logits, int 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                        hipStream_t s);
 // stable counting sort of the T*k pairs; also the active list and, when
-// mtile > 0, the grouped-GEMM tile table (tiles of mtile sorted slots)
+// mtile > 0, the grouped-GEMM tile table (tiles of mtile sorted slots). With
+// rt.hist set and more than 2048 pairs it runs as three multi-workgroup
+// launches (same order).
+int sort_hist_ints(int P, int E);
 hipError_t launch_sort(const int32_t* idx, int P, int E, RouteTables rt, int mtile, int max_tiles,
                        hipStream_t s);
 

@@ -159,34 +159,31 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, f
 }
 
 // ---- S3: stable counting sort of the pairs -----------------------------------
-// One workgroup of 1024 threads (16 waves). Pass 1 counts pairs per expert
-// (integer LDS atomics: order-independent). Pass 2 scans the counts. Pass 3
-// places chunks of 1024 pairs in order: inside a wave, lanes with the same
-// expert find each other by matching the expert id bit by bit with ballots;
-// a pair's slot is the expert's running cursor + the same-expert pairs of the
-// earlier waves of the chunk + its rank among the earlier lanes of its wave.
+// Pairs are placed in chunks of 1024 (one per 16-wave workgroup pass): inside
+// a wave, lanes with the same expert find each other by matching the expert
+// id bit by bit with ballots; a pair's slot is the expert's cursor at the
+// chunk's start + the same-expert pairs of the earlier waves of the chunk +
+// its rank among the earlier lanes of its wave. Counts use integer LDS
+// atomics (order-independent). Pairs with an expert outside [0, E) are
+// dropped.
+//
+// Few pairs: one workgroup counts, scans and places every chunk in order.
+// Many pairs (with a histogram buffer): three launches. sort_count_kernel
+// counts each chunk's pairs per expert; sort_scan_kernel turns the counts
+// into each chunk's starting cursor per expert (the expert's first slot +
+// the pairs of the earlier chunks) and builds the tables; sort_place_kernel
+// places each chunk from its cursors. Both give the same stable order.
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / 64;
 constexpr int kMaxE = 1024;
 
-__global__ __launch_bounds__(kSortThreads) void sort_kernel(const int32_t* __restrict__ idx, int P,
-                                                            int E, RouteTables rt, int mtile,
-                                                            int max_tiles) {
-  __shared__ int cnt[kMaxE];
-  __shared__ int cursor[kMaxE];
-  __shared__ uint16_t wcnt[kSortWaves][kMaxE];
-  __shared__ int scan_tmp[kSortThreads / 64];
+// From per-expert counts cnt[0..E) (LDS): offsets, and when asked the active
+// list and the grouped-GEMM tile table; cursor[e] (LDS) = first slot of e.
+// Called by all kSortThreads threads of one workgroup.
+__device__ void sort_tables(const int* cnt, int* cursor, int E, const RouteTables& rt, int mtile, int max_tiles) {
+  __shared__ int scan_tmp[kSortWaves];
+  __shared__ int fsum[kSortWaves], tsum[kSortWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < E; e += kSortThreads) {
-    cnt[e] = 0;
-    for (int wv = 0; wv < kSortWaves; wv++) wcnt[wv][e] = 0;
-  }
-  __syncthreads();
-  for (int p = tid; p < P; p += kSortThreads) {
-    int e = idx[p];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
-  }
-  __syncthreads();
   // exclusive scan of cnt[0..E) -> cursor, one expert per thread (E <= 1024)
   int my = (tid < E) ? cnt[tid] : 0;
   int incl = my;
@@ -210,82 +207,173 @@ __global__ __launch_bounds__(kSortThreads) void sort_kernel(const int32_t* __res
     rt.offsets[E] = total;
   }
   // active experts (count > 0) in ascending order, and the grouped-GEMM tiles
-  {
-    int flag = (tid < E && my > 0) ? 1 : 0;
-    int ntile = (flag && mtile > 0) ? (my + mtile - 1) / mtile : 0;
-    unsigned long long fb = __ballot(flag);
-    int fpos = __popcll(fb & ((1ull << lane) - 1ull));
-    int tincl = ntile;
+  int flag = (tid < E && my > 0) ? 1 : 0;
+  int ntile = (flag && mtile > 0) ? (my + mtile - 1) / mtile : 0;
+  unsigned long long fb = __ballot(flag);
+  int fpos = __popcll(fb & ((1ull << lane) - 1ull));
+  int tincl = ntile;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      int n = __shfl_up(tincl, o, 64);
-      if (lane >= o) tincl += n;
-    }
-    __shared__ int fsum[kSortWaves], tsum[kSortWaves];
-    if (lane == 63) {
-      fsum[wave] = __popcll(fb);
-      tsum[wave] = tincl;
-    }
-    __syncthreads();
-    int fbase = 0, tbase = 0;
-    for (int wv = 0; wv < wave; wv++) {
-      fbase += fsum[wv];
-      tbase += tsum[wv];
-    }
-    if (flag && rt.active) rt.active[fbase + fpos] = tid;
-    int t0 = tbase + tincl - ntile;
-    for (int q = 0; q < ntile; q++) {
-      if (t0 + q < max_tiles && rt.tile_expert) {
-        rt.tile_expert[t0 + q] = tid;
-        rt.tile_row0[t0 + q] = excl + q * mtile;
-      }
-    }
-    if (tid == kSortThreads - 1 && rt.counts) {
-      int na = 0, nt = 0;
-      for (int wv = 0; wv < kSortWaves; wv++) {
-        na += fsum[wv];
-        nt += tsum[wv];
-      }
-      rt.counts[0] = na;
-      rt.counts[1] = nt < max_tiles ? nt : max_tiles;
-    }
+  for (int o = 1; o < 64; o <<= 1) {
+    int n = __shfl_up(tincl, o, 64);
+    if (lane >= o) tincl += n;
+  }
+  if (lane == 63) {
+    fsum[wave] = __popcll(fb);
+    tsum[wave] = tincl;
   }
   __syncthreads();
-  // placement, chunk by chunk
-  for (int p0 = 0; p0 < P; p0 += kSortThreads) {
-    int p = p0 + tid;
-    int e = (p < P) ? idx[p] : -1;
-    bool valid = e >= 0 && e < E;
-    int key = valid ? e : kMaxE;  // 11-bit key; invalid pairs group together
-    unsigned long long peers = __ballot(1);
-#pragma unroll
-    for (int b = 0; b < 11; b++) {
-      unsigned long long bb = __ballot((key >> b) & 1);
-      peers &= ((key >> b) & 1) ? bb : ~bb;
-    }
-    int rank = __popcll(peers & ((1ull << lane) - 1ull));
-    bool leader = rank == 0;
-    if (valid && leader) wcnt[wave][e] = (uint16_t)__popcll(peers);
-    __syncthreads();
-    int slot = 0;
-    if (valid) {
-      int before = 0;
-      for (int wv = 0; wv < wave; wv++) before += wcnt[wv][e];
-      slot = cursor[e] + before + rank;
-      rt.sorted[slot] = p;
-    }
-    __syncthreads();
-    if (valid && leader) {
-      atomicAdd(&cursor[e], (int)wcnt[wave][e]);
-    }
-    __syncthreads();
-    if (valid && leader) wcnt[wave][e] = 0;
+  int fbase = 0, tbase = 0;
+  for (int wv = 0; wv < wave; wv++) {
+    fbase += fsum[wv];
+    tbase += tsum[wv];
   }
+  if (flag && rt.active) rt.active[fbase + fpos] = tid;
+  int t0 = tbase + tincl - ntile;
+  for (int q = 0; q < ntile; q++) {
+    if (t0 + q < max_tiles && rt.tile_expert) {
+      rt.tile_expert[t0 + q] = tid;
+      rt.tile_row0[t0 + q] = excl + q * mtile;
+    }
+  }
+  if (tid == kSortThreads - 1 && rt.counts) {
+    int na = 0, nt = 0;
+    for (int wv = 0; wv < kSortWaves; wv++) {
+      na += fsum[wv];
+      nt += tsum[wv];
+    }
+    rt.counts[0] = na;
+    rt.counts[1] = nt < max_tiles ? nt : max_tiles;
+  }
+  __syncthreads();
 }
+
+// Place the chunk of pairs p0 .. p0 + 1023 from the per-expert cursors (LDS);
+// the cursors advance past the chunk's pairs. wcnt [kSortWaves][E] must be 0
+// and is left 0. Called by all kSortThreads threads.
+__device__ void sort_place_chunk(const int32_t* __restrict__ idx, int p0, int P, int E, int* cursor,
+                                 uint16_t (*wcnt)[kMaxE], int32_t* __restrict__ sorted) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int p = p0 + tid;
+  const int e = (p < P) ? idx[p] : -1;
+  const bool valid = e >= 0 && e < E;
+  const int key = valid ? e : kMaxE;  // 11-bit key; invalid pairs group together
+  unsigned long long peers = __ballot(1);
+#pragma unroll
+  for (int b = 0; b < 11; b++) {
+    unsigned long long bb = __ballot((key >> b) & 1);
+    peers &= ((key >> b) & 1) ? bb : ~bb;
+  }
+  const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+  const bool leader = rank == 0;
+  if (valid && leader) wcnt[wave][e] = (uint16_t)__popcll(peers);
+  __syncthreads();
+  if (valid) {
+    int before = 0;
+    for (int wv = 0; wv < wave; wv++) before += wcnt[wv][e];
+    sorted[cursor[e] + before + rank] = p;
+  }
+  __syncthreads();
+  if (valid && leader) atomicAdd(&cursor[e], (int)wcnt[wave][e]);
+  __syncthreads();
+  if (valid && leader) wcnt[wave][e] = 0;
+}
+
+__global__ __launch_bounds__(kSortThreads) void sort_kernel(const int32_t* __restrict__ idx, int P,
+                                                            int E, RouteTables rt, int mtile,
+                                                            int max_tiles) {
+  __shared__ int cnt[kMaxE];
+  __shared__ int cursor[kMaxE];
+  __shared__ uint16_t wcnt[kSortWaves][kMaxE];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kSortThreads) {
+    cnt[e] = 0;
+    for (int wv = 0; wv < kSortWaves; wv++) wcnt[wv][e] = 0;
+  }
+  __syncthreads();
+  for (int p = tid; p < P; p += kSortThreads) {
+    int e = idx[p];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  sort_tables(cnt, cursor, E, rt, mtile, max_tiles);
+  for (int p0 = 0; p0 < P; p0 += kSortThreads) sort_place_chunk(idx, p0, P, E, cursor, wcnt, rt.sorted);
+}
+
+// chunk b's count per expert -> hist[b][e]
+__global__ __launch_bounds__(kSortThreads) void sort_count_kernel(const int32_t* __restrict__ idx, int P, int E,
+                                                                  int32_t* __restrict__ hist) {
+  __shared__ int cnt[kMaxE];
+  const int tid = threadIdx.x, b = blockIdx.x;
+  for (int e = tid; e < E; e += kSortThreads) cnt[e] = 0;
+  __syncthreads();
+  const int p = b * kSortThreads + tid;
+  if (p < P) {
+    const int e = idx[p];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kSortThreads) hist[(size_t)b * E + e] = cnt[e];
+}
+
+// hist[b][e] -> the number of expert e's pairs in chunks before b; the tables
+__global__ __launch_bounds__(kSortThreads) void sort_scan_kernel(int nb, int E, int32_t* __restrict__ hist,
+                                                                 RouteTables rt, int mtile, int max_tiles) {
+  __shared__ int cnt[kMaxE];
+  __shared__ int cursor[kMaxE];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kSortThreads) {
+    int run = 0;
+    int b = 0;
+    // 16 loads in flight per pass over the chunks
+    for (; b + 16 <= nb; b += 16) {
+      int v[16];
+#pragma unroll
+      for (int u = 0; u < 16; u++) v[u] = hist[(size_t)(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 16; u++) {
+        hist[(size_t)(b + u) * E + e] = run;
+        run += v[u];
+      }
+    }
+    for (; b < nb; b++) {
+      const int v = hist[(size_t)b * E + e];
+      hist[(size_t)b * E + e] = run;
+      run += v;
+    }
+    cnt[e] = run;
+  }
+  __syncthreads();
+  sort_tables(cnt, cursor, E, rt, mtile, max_tiles);
+}
+
+// chunk b placed from its cursors: the expert's first slot + hist[b][e]
+__global__ __launch_bounds__(kSortThreads) void sort_place_kernel(const int32_t* __restrict__ idx, int P, int E,
+                                                                  const int32_t* __restrict__ hist, RouteTables rt) {
+  __shared__ int cursor[kMaxE];
+  __shared__ uint16_t wcnt[kSortWaves][kMaxE];
+  const int tid = threadIdx.x, b = blockIdx.x;
+  for (int e = tid; e < E; e += kSortThreads) {
+    cursor[e] = rt.offsets[e] + hist[(size_t)b * E + e];
+    for (int wv = 0; wv < kSortWaves; wv++) wcnt[wv][e] = 0;
+  }
+  __syncthreads();
+  sort_place_chunk(idx, b * kSortThreads, P, E, cursor, wcnt, rt.sorted);
+}
+
+int sort_hist_ints(int P, int E) { return (P + kSortThreads - 1) / kSortThreads * E; }
 
 hipError_t launch_sort(const int32_t* idx, int P, int E, RouteTables rt, int mtile, int max_tiles,
                        hipStream_t s) {
-  launch_kernel("sort", sort_kernel, dim3(1), dim3(kSortThreads), 0, s, idx, P, E, rt, mtile, max_tiles);
+  const int nb = (P + kSortThreads - 1) / kSortThreads;
+  if (!rt.hist || nb <= 2) {
+    launch_kernel("sort", sort_kernel, dim3(1), dim3(kSortThreads), 0, s, idx, P, E, rt, mtile, max_tiles);
+    return hipGetLastError();
+  }
+  launch_kernel("sort_count", sort_count_kernel, dim3(nb), dim3(kSortThreads), 0, s, idx, P, E, rt.hist);
+  launch_kernel("sort_scan", sort_scan_kernel, dim3(1), dim3(kSortThreads), 0, s, nb, E, rt.hist, rt, mtile,
+                max_tiles);
+  launch_kernel("sort_place", sort_place_kernel, dim3(nb), dim3(kSortThreads), 0, s, idx, P, E,
+                (const int32_t*)rt.hist, rt);
   return hipGetLastError();
 }
 
