@@ -29,7 +29,7 @@ struct RouteTables {
 constexpr int kRouterTok = 8;
 hipError_t launch_router(const uint16_t* x, const float* Wr, float* logits, int T, int H, int E,
                          hipStream_t s);
-// top-k + softmax over given logits, one block per token
+// top-k + softmax over given logits, one wave per token
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                        hipStream_t s);
 // stable counting sort of the T*k pairs; also the active list and, when
