@@ -563,17 +563,7 @@ __global__ __launch_bounds__(kDecThreads) void flat_route_gateup_kernel(FlatArgs
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (blockIdx.x < (unsigned)E) {
     const int e = blockIdx.x;
-    const float* row = r.wr + (size_t)e * H;
-    float acc = 0.0f;
-    for (int h = 4 * tid; h < H; h += 4 * kDecThreads) {
-      const f32x4 wv = *reinterpret_cast<const f32x4*>(row + h);
-      const u32x2 xv = *reinterpret_cast<const u32x2*>(a.x + h);
-      acc = fmaf(bf16_to_f32(xv.x & 0xFFFFu), wv.x, acc);
-      acc = fmaf(bf16_to_f32(xv.x >> 16), wv.y, acc);
-      acc = fmaf(bf16_to_f32(xv.y & 0xFFFFu), wv.z, acc);
-      acc = fmaf(bf16_to_f32(xv.y >> 16), wv.w, acc);
-    }
-    const float sw = wave_sum(acc);
+    const float sw = wave_sum(router_thread_sum<kDecThreads>(r.wr + (size_t)e * H, a.x, H, tid));
     if (lane == 0) red[wave] = sw;
     __syncthreads();
     if (tid == 0) st_tag(r.tags + e, r.call, __float_as_uint(((red[0] + red[1]) + red[2]) + red[3]));

@@ -16,38 +16,21 @@ namespace moe {
 // ---- S1: router logits --------------------------------------------------------
 // Router weights are f32 [E][H], one contiguous row per expert. Block
 // (expert e, token group) computes the whole dot product of that row with up
-// to 8 token rows: thread j reads 16-byte pieces h = 4j, 4j + 1024, ... of the
-// row (coalesced) and the matching x values; the sum is reduced in the wave,
-// then over the 4 waves in wave order. One block per expert keeps every CU
-// busy at E = 256 without partial sums across blocks.
-__global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict__ x,
-                                                     const float* __restrict__ Wr,
-                                                     float* __restrict__ logits, int T, int H,
-                                                     int E) {
+// to 8 token rows: thread j sums 16-byte pieces h = 4j, 4j + 1024, ... of the
+// row (coalesced) against the matching x values (router_thread_sum, the
+// arithmetic the one-token layer kernel uses too); the sum is reduced in the
+// wave, then over the 4 waves in wave order. The row is read once per token
+// (the token's pass hits it in the cache after the first). One block per
+// expert keeps every CU busy at E = 256 without partial sums across blocks.
+__global__ __launch_bounds__(256) void router_kernel(const uint16_t* x, const float* Wr, float* logits, int T,
+                                                     int H, int E) {
   const int e = blockIdx.x, t0 = blockIdx.y * kRouterTok;
   const int nt = min(kRouterTok, T - t0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ float red[4][kRouterTok];
-  float acc[kRouterTok];
-#pragma unroll
-  for (int tt = 0; tt < kRouterTok; tt++) acc[tt] = 0.0f;
   const float* row = Wr + (size_t)e * H;
-  for (int h = 4 * threadIdx.x; h < H; h += 1024) {
-    const f32x4 wv = *reinterpret_cast<const f32x4*>(row + h);
-#pragma unroll
-    for (int tt = 0; tt < kRouterTok; tt++) {
-      if (tt < nt) {
-        const u32x2 xv = *reinterpret_cast<const u32x2*>(x + (size_t)(t0 + tt) * H + h);
-        acc[tt] = fmaf(bf16_to_f32(xv.x & 0xFFFFu), wv.x, acc[tt]);
-        acc[tt] = fmaf(bf16_to_f32(xv.x >> 16), wv.y, acc[tt]);
-        acc[tt] = fmaf(bf16_to_f32(xv.y & 0xFFFFu), wv.z, acc[tt]);
-        acc[tt] = fmaf(bf16_to_f32(xv.y >> 16), wv.w, acc[tt]);
-      }
-    }
-  }
-#pragma unroll
-  for (int tt = 0; tt < kRouterTok; tt++) {
-    const float s = wave_sum(acc[tt]);
+  for (int tt = 0; tt < nt; tt++) {
+    const float s = wave_sum(router_thread_sum<256>(row, x + (size_t)(t0 + tt) * H, H, threadIdx.x));
     if (lane == 0) red[wave][tt] = s;
   }
   __syncthreads();

@@ -1,5 +1,6 @@
-// Routing helpers shared by the top-k kernel and the one-token layer kernel,
-// so that both select the same experts and produce bit-identical weights.
+// Routing helpers shared by the router and top-k kernels and the one-token
+// layer kernel, so that both paths compute bit-identical logits, select the
+// same experts and produce bit-identical weights.
 //
 // Selection rule (the C header states it): the k largest router logits, ties
 // to the lower expert index, -0 == +0, a NaN below every number; the weights
@@ -26,6 +27,40 @@ __device__ __forceinline__ float topk_softmax(const float* sel_v, int k, int lan
   float sum = 0.0f;
   for (int j = 0; j < k; j++) sum += __shfl(a, j, 64);
   return (lane < k) ? a / sum : 0.0f;
+}
+
+// One thread's part of a router logit, for a workgroup of NT threads: the
+// f32 fma chain over h = 4j, 4j + 4 NT, ... (h ascending; the four inputs of
+// a piece in order). Each pass issues the loads of up to 8 pieces before its
+// FMAs, so a row costs one memory round trip per 32 NT inputs, not one per
+// piece. row: f32 [H] (16-byte aligned); x: bf16 [H] (8-byte aligned).
+template <int NT>
+__device__ __forceinline__ float router_thread_sum(const float* __restrict__ row, const uint16_t* __restrict__ x,
+                                                   int H, int j) {
+  constexpr int U = 8;
+  float acc = 0.0f;
+  for (int h0 = 4 * j; h0 < H; h0 += 4 * NT * U) {
+    f32x4 wv[U];
+    u32x2 xv[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int h = h0 + 4 * NT * u;
+      if (h < H) {
+        wv[u] = *reinterpret_cast<const f32x4*>(row + h);
+        xv[u] = *reinterpret_cast<const u32x2*>(x + h);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      if (h0 + 4 * NT * u < H) {
+        acc = fmaf(bf16_to_f32(xv[u].x & 0xFFFFu), wv[u].x, acc);
+        acc = fmaf(bf16_to_f32(xv[u].x >> 16), wv[u].y, acc);
+        acc = fmaf(bf16_to_f32(xv[u].y & 0xFFFFu), wv[u].z, acc);
+        acc = fmaf(bf16_to_f32(xv[u].y >> 16), wv[u].w, acc);
+      }
+    }
+  }
+  return acc;
 }
 
 }  // namespace moe
