@@ -22,6 +22,7 @@
 #include <cstdlib>
 
 #include "common.h"
+#include "dma.h"
 #include "gemv_util.h"
 #include "internal.h"
 #include "route_util.h"
@@ -442,11 +443,8 @@ __global__ __launch_bounds__(64 * kFlatDecodeMaxK) void flat_down_kernel(FlatArg
     s_idx[threadIdx.x] = (e >= 0 && e < a.E) ? e : -1;
     s_w[threadIdx.x] = a.w[threadIdx.x];
   }
-  {
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.mid);
-    u32x4* dst = reinterpret_cast<u32x4*>(ms);
-    for (int i = threadIdx.x; i < k * I / 8; i += blockDim.x) dst[i] = src[i];
-  }
+  dma_copy_lds(a.mid, ms, (uint32_t)(k * I * 2), k);  // the k waves copy the mids, all chunks at once
+  wait_vmcnt<0>();
   __syncthreads();
   {
     const int j = wave;  // one wave per pair

@@ -27,6 +27,22 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const void* p) {
   return reinterpret_cast<const uint8_t*>((uintptr_t)(((uint64_t)hi << 32) | lo));
 }
 
+// A linear copy of nbytes (a multiple of 16; src and dst 16-byte aligned)
+// from global memory to LDS by the nwaves waves of a workgroup: wave w copies
+// the 1 KiB chunks w, w + nwaves, ... with one wave-wide load each, all in
+// flight together. The caller waits (wait_vmcnt<0>, then a barrier) before any
+// wave reads the copy.
+__device__ __forceinline__ void dma_copy_lds(const void* src, void* dst, uint32_t nbytes, int nwaves) {
+  const uint8_t* base = uniform_ptr(src);
+  const uint32_t l0 = lds_addr(dst);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (uint32_t c = wave; c * 1024 < nbytes; c += nwaves) {
+    const uint32_t off = c * 1024 + 16 * lane;
+    if (off < nbytes) dma16(base, off, __builtin_amdgcn_readfirstlane(l0 + c * 1024));
+  }
+}
+
 // s_waitcnt vmcnt(n) alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
 // expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
 template <int N>
