@@ -86,6 +86,26 @@ int moe_nvfp4_bank_init(moe_nvfp4_bank* b, void* base, int H, int I, int E);
 int moe_pack_nvfp4_bank(const moe_nvfp4_bank* b, const uint32_t* const codes[3],
                         const uint8_t* const scales[3], const float* const g[3], void* stream);
 
+/* Pack side, [PACK] global-scales bullet: the release gives per projection an
+ * f32 weight_scale_2 (ws2); the bank stores g with f32(g / 2688) == ws2. For
+ * each of the n values (host arrays): g[i] is the f32 whose f32(g / 2688) is
+ * nearest to ws2[i] (equal to it when such a g exists); among several, the
+ * one nearest to the exact product ws2[i] * 2688, then the one with an even
+ * significand. inexact (nullable) u8 [n]: 1 where no g gives ws2[i] exactly
+ * (the manifest's global_scale_inexact list), else 0. Runs on the host, no
+ * GPU needed. Errors: MOE_EINVAL for n < 0, null ws2/g (n > 0), or a ws2 that
+ * is not a positive f32 whose g = ws2 * 2688 is finite; nothing is written
+ * then. */
+int moe_nvfp4_global_from_ws2(const float* ws2, int64_t n, float* g, uint8_t* inexact);
+
+/* Manifest digests, [PACK] routed-experts bullet (each record's sha256): the
+ * SHA-256 (FIPS 180-4) of records e0 .. e0+n-1 of the bank over their
+ * record_bytes bytes (not the pad), computed on the device from the records
+ * as they sit in memory. digests: device u8 [n][32], 4-byte aligned. Errors:
+ * MOE_EINVAL for a range outside [0, E) or null digests (n > 0), MOE_EALIGN;
+ * bank errors as for the pack. Stream-ordered like the other calls. */
+int moe_nvfp4_record_sha256(const moe_nvfp4_bank* b, int e0, int n, uint8_t* digests, void* stream);
+
 /* S1 + S2, routing ([PACK] intro: 8 of 256 experts per token; [VQ] "What
  * stays native": FP32 router logits).
  *   If x and w_router are both non-null: logits[t][e] = sum_h x[t][h]*Wr[e][h]
@@ -184,7 +204,7 @@ int moe_nvfp4_dequant(const moe_nvfp4_bank* b, int expert, int proj, float* out_
  * starts collection; moe_profile_read(name, ...) synchronizes the events and
  * returns the summed duration and count of the kernel family `name` since the
  * last enable. Names: "router", "topk", "sort", "decode_gateup", "decode_down",
- * "combine", "prefill_gateup", "prefill_down", "affine8", "rmsnorm". */
+ * "combine", "prefill_gateup", "prefill_down", "affine8", "rmsnorm", "sha256". */
 int moe_profile_enable(int on);
 int moe_profile_read(const char* name, double* total_ms, int64_t* launches);
 

@@ -126,6 +126,64 @@ def pack_record(H, I, codes, scales, g):
     return out
 
 
+def global_from_ws2(ws2):
+    """The stored global g for each f32 weight_scale_2 value ("Beam 1.0 501B-A23B,
+    streaming pack, NVFP4 experts / MLX 8-bit residents", "What this pack holds",
+    global-scales bullet: the g with f32(g / 2688) equal to weight_scale_2, else
+    the nearest g). Returns (g f32, inexact u8).
+
+    Plainly: positive f32 values are ordered like their bit patterns and
+    g -> f32(g / 2688) is monotone, so two bisections over the bit patterns find
+    lo, the first g whose image is >= ws2, and hi, the first whose image is
+    > ws2. The exact solutions are [lo, hi). If there are any, the pick is the one
+    nearest to the exact product ws2 * 2688; if there are none, lo - 1 and lo
+    (images below and above ws2) compete on the distance of their images to ws2,
+    then on the distance to ws2 * 2688. Remaining ties go to the even bit
+    pattern. Readings: "nearest" is taken on the image, and the tie rules are ours.
+    """
+    ws2 = np.ascontiguousarray(ws2, dtype=np.float32).ravel()
+    n = ws2.size
+    div = np.float32(2688.0)
+
+    def image(bits):
+        return (bits.astype(np.uint32).view(np.float32) / div).astype(np.float32)
+
+    def first_at_least(strict):
+        lo = np.ones(n, dtype=np.int64)              # smallest positive subnormal
+        hi = np.full(n, 0x7F800000, dtype=np.int64)  # +inf: image compares as larger
+        while np.any(lo < hi):
+            mid = (lo + hi) // 2
+            img = image(mid)
+            ok = img > ws2 if strict else img >= ws2
+            hi = np.where(ok & (lo < hi), mid, hi)
+            lo = np.where(~ok & (lo < hi), mid + 1, lo)
+        return lo
+
+    lo = first_at_least(False)
+    hi = first_at_least(True)
+    target = ws2.astype(np.float64) * 2688.0
+    g = np.empty(n, dtype=np.float32)
+    inexact = np.zeros(n, dtype=np.uint8)
+    for i in range(n):
+        if hi[i] > lo[i]:
+            cands = list(range(int(lo[i]), int(hi[i])))
+        else:
+            cands = [int(lo[i]) - 1, int(lo[i])]
+            inexact[i] = 1
+        best = None
+        for c in cands:
+            gv = np.array([c], dtype=np.uint32).view(np.float32)[0]
+            if not np.isfinite(gv) or gv <= 0:
+                continue
+            err = abs(float(np.float32(gv / div)) - float(ws2[i]))
+            dist = abs(float(gv) - float(target[i]))
+            key = (err, dist, c & 1)
+            if best is None or key < best[0]:
+                best = (key, gv)
+        g[i] = best[1]
+    return g, inexact
+
+
 def proj_shape(H, I, proj):
     return (H, I) if proj == DOWN else (I, H)
 

@@ -144,6 +144,70 @@ def test_pack_bytes_match_oracle_sampled_full_shape(big_bank):
         assert np.array_equal(dev, rec), e
 
 
+# ---- pack side: record digests and the manifest --------------------------------------
+def device_digests(bank, e0, n):
+    d = torch.empty((n, 32), dtype=torch.uint8, device=DEV)
+    wq.moe_nvfp4_record_sha256(bank, e0, n, d)
+    torch.cuda.synchronize()
+    return [bytes(r) for r in d.cpu().numpy()]
+
+
+@pytest.mark.parametrize("H,I,E", [(256, 128, 16), (16, 16, 5), (16, 32, 3)])
+def test_record_sha256_small_banks(H, I, E):
+    # record sizes end 12, 60 and 44 bytes into a 64-byte block: one and two
+    # padding blocks
+    import hashlib
+    seed = 11
+    say(f"sha256 of {E} records at H={H} I={I}")
+    bank, base = W.build_bank(seed, H, I, E)
+    _, nbytes, _ = oracle.record_layout(H, I)
+    recs = host_records(seed, range(E), H, I)
+    want = [hashlib.sha256(recs[e][:nbytes].tobytes()).digest() for e in range(E)]
+    assert device_digests(bank, 0, E) == want
+    assert device_digests(bank, 1, E - 2) == want[1:E - 1]
+
+
+def test_record_sha256_full_shape_sampled(big_bank):
+    import hashlib
+    bank, base = big_bank
+    c = W.CONFIGS["decode"]
+    _, nbytes, _ = oracle.record_layout(c["H"], c["I"])
+    got = device_digests(bank, 96, 2) + device_digests(bank, 255, 1)
+    recs = host_records(c["bank_seed"], [96, 97, 255], c["H"], c["I"])
+    want = [hashlib.sha256(recs[e][:nbytes].tobytes()).digest() for e in (96, 97, 255)]
+    assert got == want
+
+
+def test_manifest_with_recovered_global_scales():
+    # the pack-side flow: weight_scale_2 values -> g (library, host) -> records
+    # holding those g -> manifest; the oracle repacks the same parts with the
+    # oracle's own g and hashes them
+    import hashlib
+    from weight_quantized_moe_amd import manifest
+    H, I, E, seed = 256, 128, 8, 12
+    bank, base = W.build_bank(seed, H, I, E)
+    rng = np.random.default_rng(7)
+    ws2 = np.exp(rng.uniform(np.log(1e-4), np.log(1e-1), (E, 3))).astype(np.float32)
+    g, inexact = wq.moe_nvfp4_global_from_ws2(ws2.ravel())
+    g_ref, inexact_ref = oracle.global_from_ws2(ws2.ravel())
+    assert np.array_equal(g.view(np.uint32), g_ref.view(np.uint32)) and np.array_equal(inexact, inexact_ref)
+    g, inexact = g.reshape(E, 3), inexact.reshape(E, 3)
+    for e in range(E):
+        for p in range(3):
+            off = e * bank.stride + int(bank.part_off[6 + p])
+            base[off:off + 4] = torch.from_numpy(g[e, p:p + 1].view(np.uint8).copy()).to(DEV)
+    torch.cuda.synchronize()
+    m = manifest.bank_manifest(bank, inexact)
+    _, nbytes, stride = oracle.record_layout(H, I)
+    want_inexact = [(e, manifest.PROJECTIONS[p]) for e in range(E) for p in range(3) if inexact_ref[e * 3 + p]]
+    assert [(r["record"], r["projection"]) for r in m["global_scale_inexact"]] == want_inexact
+    for e in range(E):
+        c_, s_, _ = W.host_parts(seed, e, H, I)
+        rec = oracle.pack_record(H, I, c_, s_, g_ref[3 * e:3 * e + 3])
+        assert m["records"][e] == {"offset": e * stride, "length": nbytes,
+                                   "sha256": hashlib.sha256(rec[:nbytes].tobytes()).hexdigest()}, e
+
+
 @pytest.mark.parametrize("proj", [0, 1, 2])
 def test_dequant_bit_exact_tiny(tiny_bank, proj):
     bank, base = tiny_bank

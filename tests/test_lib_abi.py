@@ -149,3 +149,29 @@ def test_workspace_sizes_grow_with_pairs():
     assert 0 < a < b
     # mids (bf16) and per-pair f32 rows dominate: P*(2I + 4H) bytes
     assert b >= 65536 * (2 * 2560 + 4 * 5120)
+
+
+def test_pack_side_validation():
+    L = wq.lib()
+    b = _bank()
+    fake = C.c_void_p(1 << 26)
+    assert L.moe_nvfp4_record_sha256(C.byref(b), 15, 2, fake, None) == wq.MOE_EINVAL
+    assert L.moe_nvfp4_record_sha256(C.byref(b), -1, 1, fake, None) == wq.MOE_EINVAL
+    assert L.moe_nvfp4_record_sha256(C.byref(b), 0, 1, None, None) == wq.MOE_EINVAL
+    assert L.moe_nvfp4_record_sha256(C.byref(b), 0, 1, C.c_void_p((1 << 26) + 2), None) == wq.MOE_EALIGN
+    assert L.moe_nvfp4_record_sha256(None, 0, 1, fake, None) == wq.MOE_EINVAL
+    assert L.moe_nvfp4_record_sha256(C.byref(b), 3, 0, None, None) == wq.MOE_OK
+
+
+def test_manifest_part_table():
+    from weight_quantized_moe_amd import manifest
+    b = _bank(5120, 2560, 256)
+    parts = manifest.part_table(b)
+    assert [p[0] for p in parts] == ["gate.codes", "gate.scales", "up.codes", "up.scales", "down.codes",
+                                     "down.scales", "gate.global", "up.global", "down.global"]
+    # contiguous, ending at the record size
+    end = 0
+    for _, off, length in parts:
+        assert off == end
+        end = off + length
+    assert end == b.record_bytes == 22118412

@@ -23,7 +23,8 @@ EXPORTS = [
     "moe_last_error", "moe_nvfp4_record_bytes", "moe_nvfp4_record_stride", "moe_nvfp4_bank_init",
     "moe_pack_nvfp4_bank", "moe_route_topk", "moe_sort_pairs", "moe_sort_workspace_bytes", "moe_sort_pairs_ws",
     "moe_nvfp4_workspace_bytes", "moe_nvfp4_forward", "moe_nvfp4_layer", "affine8_g64_linear", "moe_rmsnorm",
-    "moe_nvfp4_dequant", "moe_profile_enable", "moe_profile_read",
+    "moe_nvfp4_dequant", "moe_profile_enable", "moe_profile_read", "moe_nvfp4_global_from_ws2",
+    "moe_nvfp4_record_sha256",
 ]
 
 
@@ -81,6 +82,10 @@ def lib():
         L.moe_rmsnorm.argtypes = [vp, i32, i32, C.c_float, vp, vp]
         L.moe_nvfp4_dequant.restype = i32
         L.moe_nvfp4_dequant.argtypes = [bankp, i32, i32, vp, vp, vp]
+        L.moe_nvfp4_global_from_ws2.restype = i32
+        L.moe_nvfp4_global_from_ws2.argtypes = [vp, C.c_int64, vp, vp]
+        L.moe_nvfp4_record_sha256.restype = i32
+        L.moe_nvfp4_record_sha256.argtypes = [bankp, i32, i32, vp, vp]
         L.moe_profile_enable.restype = i32
         L.moe_profile_enable.argtypes = [i32]
         L.moe_profile_read.restype = i32
@@ -190,6 +195,22 @@ def moe_rmsnorm(x, T, H, eps, y, stream=None):
 
 def moe_nvfp4_dequant(bank, expert, proj, out_f32, out_unit, stream=None):
     _check(lib().moe_nvfp4_dequant(C.byref(bank), expert, proj, _ptr(out_f32), _ptr(out_unit), _stream(stream)))
+
+
+def moe_nvfp4_global_from_ws2(ws2):
+    """g (f32) and the inexact flags (u8) for host f32 values ws2 (numpy)."""
+    import numpy as np
+    ws2 = np.ascontiguousarray(ws2, dtype=np.float32)
+    g = np.empty_like(ws2)
+    inexact = np.empty(ws2.shape, dtype=np.uint8)
+    _check(lib().moe_nvfp4_global_from_ws2(ws2.ctypes.data_as(C.c_void_p), ws2.size,
+                                           g.ctypes.data_as(C.c_void_p), inexact.ctypes.data_as(C.c_void_p)))
+    return g, inexact
+
+
+def moe_nvfp4_record_sha256(bank, e0, n, digests, stream=None):
+    """digests: device uint8 [n][32]."""
+    _check(lib().moe_nvfp4_record_sha256(C.byref(bank), e0, n, _ptr(digests), _stream(stream)))
 
 
 def moe_profile_enable(on):

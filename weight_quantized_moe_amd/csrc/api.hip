@@ -186,6 +186,35 @@ MOE_API int moe_pack_nvfp4_bank(const moe_nvfp4_bank* b, const uint32_t* const c
   return hip_check(launch_zero_tails(base, b->stride, b->record_bytes, b->E, s), "pack zero pad");
 }
 
+// ---- pack side: global scales and record digests --------------------------------
+MOE_API int moe_nvfp4_global_from_ws2(const float* ws2, int64_t n, float* g, uint8_t* inexact) {
+  if (n < 0) return fail(MOE_EINVAL, "global_from_ws2: n=%lld < 0", (long long)n);
+  if (n > 0 && (!ws2 || !g)) return fail(MOE_EINVAL, "global_from_ws2: null ws2/g");
+  for (int64_t i = 0; i < n; i++)
+    if (!(ws2[i] > 0.0f) || !((double)ws2[i] * 2688.0 <= 3.4028234663852886e38))
+      return fail(MOE_EINVAL, "global_from_ws2: ws2[%lld] = %g is not a positive f32 with a finite g",
+                  (long long)i, (double)ws2[i]);
+  for (int64_t i = 0; i < n; i++) {
+    const bool exact = global_from_ws2_one(ws2[i], &g[i]);
+    if (inexact) inexact[i] = exact ? 0 : 1;
+  }
+  return MOE_OK;
+}
+
+MOE_API int moe_nvfp4_record_sha256(const moe_nvfp4_bank* b, int e0, int n, uint8_t* digests, void* stream) {
+  BankView v;
+  int rc = bank_view(b, &v, "record_sha256");
+  if (rc) return rc;
+  if (e0 < 0 || n < 0 || (int64_t)e0 + n > b->E)
+    return fail(MOE_EINVAL, "record_sha256: records [%d, %d) outside [0, %d)", e0, e0 + n, b->E);
+  if (n == 0) return MOE_OK;
+  if (!digests) return fail(MOE_EINVAL, "record_sha256: null digests");
+  if (!aligned(digests, 4)) return fail(MOE_EALIGN, "record_sha256: digests not 4-byte aligned");
+  return hip_check(launch_record_sha256(v.base, v.stride, b->record_bytes, e0, n, digests,
+                                        static_cast<hipStream_t>(stream)),
+                   "record_sha256");
+}
+
 // ---- S1 + S2 routing -----------------------------------------------------------
 MOE_API int moe_route_topk(const uint16_t* x, const float* w_router, float* logits, int T, int H,
                            int E, int k, int32_t* idx, float* w, void* stream) {

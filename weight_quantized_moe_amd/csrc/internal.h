@@ -40,6 +40,13 @@ int sort_hist_ints(int P, int E);
 hipError_t launch_sort(const int32_t* idx, int P, int E, RouteTables rt, int mtile, int max_tiles,
                        hipStream_t s);
 
+// pack side: g with f32(g / 2688) == ws2 if one exists, else the nearest
+// (returns whether it is exact); SHA-256 of records e0 .. e0 + n - 1 over
+// their first nbytes bytes, digests [n][32] (device, 4-byte aligned)
+bool global_from_ws2_one(float ws2, float* g);
+hipError_t launch_record_sha256(const uint8_t* base, uint64_t stride, uint64_t nbytes, int e0, int n,
+                                uint8_t* digests, hipStream_t s);
+
 // expert-streaming (GEMV) kernels. rt == nullptr: each block finds its
 // expert (the slot-th smallest present in idx) and that expert's pairs itself,
 // which needs P <= kDecInblockMaxP; else the sorted tables are used. mid and part
