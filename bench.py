@@ -25,8 +25,14 @@ counters read for a plain device copy of known size; read from
 profiles/traffic_decode_gateup.txt and reported only while the kernel source
 it was measured on is unchanged (its SHA-1 is recorded there), else null.
 
+Expert cache leg (--only cache, not part of the default run): the bank in
+pinned host memory, a bounded pool of HBM slots (moe_cache_*), single-token
+decode steps on Zipf(1.1)-skewed routing; reports the host-to-HBM copy rate
+on an all-miss pattern against PCIe 5.0 x16 (64 GB/s per direction), and per
+pool size the hit rate and the time per step (prepare + forward).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--prefill-steps P]
-       [--only decode|prefill] [--no-cpu-baseline] [--two-call]
+       [--only decode|prefill|cache] [--no-cpu-baseline] [--two-call]
 Profiling helpers: --copy-calibration (device copies of 1 GiB, for the
 counter scale factor); --summarize-pmc DIR (per-kernel mean counter values
 per dispatch from a rocprofv3 --pmc output directory; no GPU needed).
@@ -52,6 +58,7 @@ from synth import workloads as W  # noqa: E402
 
 METRIC = "NVFP4 MoE layer: decode HBM GB/s (T=1) + prefill TFLOP/s (T=8192), 1 GPU"
 HBM_PEAK_GBS = 8000.0
+PCIE_PEAK_GBS = 64.0
 BF16_PEAK_TFLOPS = 2500.0
 ROTATE = 64
 
@@ -254,6 +261,89 @@ def prefill_leg(bank, P):
             "kernels_us": {n_: round(v[0] * 1e3, 2) for n_, v in pk.items()}}
 
 
+def cache_leg(bank, base, pools=(32, 64, 128, 192), steps=256, warm=64):
+    c = W.CONFIGS["decode"]
+    E, k, H = c["E"], c["k"], c["H"]
+    host_mem = torch.empty(base.numel(), dtype=torch.uint8, pin_memory=True)
+    host_mem.copy_(base)
+    hb = wq.moe_nvfp4_bank()
+    hb.H, hb.I, hb.E, hb.record_bytes, hb.stride = bank.H, bank.I, bank.E, bank.record_bytes, bank.stride
+    for i in range(9):
+        hb.part_off[i] = bank.part_off[i]
+    hb.base = host_mem.data_ptr()
+    stride = bank.stride
+    # routing of `steps + warm` single-token steps on Zipf-skewed logits (the
+    # library's top-k)
+    n_tok = steps + warm
+    logits = torch.from_numpy(synth.skewed_logits(77, n_tok, E, rank_seed=c["seed"])).cuda()
+    idx_d = torch.empty((n_tok, k), dtype=torch.int32, device="cuda")
+    w_d = torch.empty((n_tok, k), dtype=torch.float32, device="cuda")
+    wq.moe_route_topk(None, None, logits, n_tok, H, E, k, idx_d, w_d)
+    idx_h = idx_d.cpu().numpy()
+    xs = bf16_dev(np.stack([W.inputs("decode", v)[0] for v in range(8)]))
+    y = torch.empty((1, H), dtype=torch.int16, device="cuda")
+
+    def pool(n):
+        mem = torch.empty(n * stride + 4096, dtype=torch.uint8, device="cuda")
+        off = (-mem.data_ptr()) % 4096
+        return mem, mem[off:off + n * stride]
+
+    out = {"workload": "single-token decode steps, top-8 of 256 on Zipf(1.1)-skewed logits, the 256-record bank "
+                       "in pinned host memory, a pool of HBM slots"}
+    # host -> HBM rate: 8 slots, every step names 8 experts not resident
+    mem, sb = pool(8)
+    cache = wq.moe_cache_create(hb, sb, 8)
+    reps = 64
+    torch.cuda.synchronize()
+    t0 = time.time()
+    for r in range(reps):
+        wq.moe_cache_prepare(cache, [(8 * r + j) % E for j in range(8)])
+    torch.cuda.synchronize()
+    dt = time.time() - t0
+    _, _, nbytes = wq.moe_cache_stats(cache)
+    wq.moe_cache_destroy(cache)
+    del mem, sb
+    gbs = nbytes / dt / 1e9
+    out["h2d"] = {"GBps": round(gbs, 2), "peak": PCIE_PEAK_GBS, "frac": round(gbs / PCIE_PEAK_GBS, 4),
+                  "bytes": int(nbytes), "records": reps * 8}
+    log(f"cache: host->HBM {gbs:.1f} GB/s over {reps * 8} records")
+    # decode through pools of several sizes
+    ws = wq.workspace(wq.moe_nvfp4_workspace_bytes(1, k, H, c["I"], E))
+    rows = []
+    for n in pools:
+        mem, sb = pool(n)
+        cache = wq.moe_cache_create(hb, sb, n)
+        cb = wq.moe_cache_bank(cache)
+        sidx = torch.empty((1, k), dtype=torch.int32, device="cuda")
+
+        def step(t):
+            ids = list(dict.fromkeys(int(e) for e in idx_h[t]))
+            slot_of = wq.moe_cache_prepare(cache, ids)
+            remap = dict(zip(ids, slot_of.tolist()))
+            sidx.copy_(torch.tensor([[remap[int(e)] for e in idx_h[t]]], dtype=torch.int32), non_blocking=False)
+            wq.moe_nvfp4_forward(cb, xs[t % 8], 1, sidx, w_d[t:t + 1], k, None, y, 0, ws)
+
+        for t in range(warm):
+            step(t)
+        torch.cuda.synchronize()
+        h0, m0, b0 = wq.moe_cache_stats(cache)
+        t0 = time.time()
+        for t in range(warm, warm + steps):
+            step(t)
+        torch.cuda.synchronize()
+        dt = time.time() - t0
+        h1, m1, b1 = wq.moe_cache_stats(cache)
+        wq.moe_cache_destroy(cache)
+        del mem, sb
+        hit = (h1 - h0) / max(1, (h1 - h0) + (m1 - m0))
+        row = {"slots": n, "hit_rate": round(hit, 4), "ms_per_step": round(dt / steps * 1e3, 4),
+               "copied_MB_per_step": round((b1 - b0) / steps / 1e6, 2)}
+        rows.append(row)
+        log(f"cache: {n} slots, hit rate {hit:.3f}, {dt / steps * 1e3:.3f} ms/step")
+    out["decode"] = rows
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -262,7 +352,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill"])
+    ap.add_argument("--only", choices=["decode", "prefill", "cache"])
     ap.add_argument("--two-call", action="store_true",
                     help="decode step as moe_route_topk + moe_nvfp4_forward instead of moe_nvfp4_layer")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -290,6 +380,9 @@ def main():
     log(f"bank ready in {time.time() - t0:.1f} s")
     if args.only == "prefill":
         print(json.dumps({"prefill": prefill_leg(bank, args.prefill_steps)}), flush=True)
+        return
+    if args.only == "cache":
+        print(json.dumps({"expert_cache": cache_leg(bank, base)}), flush=True)
         return
 
     # ---- decode leg

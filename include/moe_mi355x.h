@@ -106,6 +106,39 @@ int moe_nvfp4_global_from_ws2(const float* ws2, int64_t n, float* g, uint8_t* in
  * bank errors as for the pack. Stream-ordered like the other calls. */
 int moe_nvfp4_record_sha256(const moe_nvfp4_bank* b, int e0, int n, uint8_t* digests, void* stream);
 
+/* Expert cache: a bounded set of expert records in HBM fed from host memory
+ * ([PACK] "What it is for": the selected experts stream into a bounded cache
+ * of expert rows on the GPU; "Beam-1.0-501B-A23B, EXL3 3-bit, for 2x RTX PRO
+ * 6000 Blackwell", "How it fits": cold experts in pinned host RAM, moved over
+ * PCIe on a side stream).
+ * moe_cache_create: host_bank describes the full bank in HOST memory (base
+ * pinned by the caller, e.g. hipHostMalloc; stride a multiple of 4096; any E
+ * >= 1), slot_base is DEVICE memory of nslots * stride bytes (4096-byte
+ * aligned, 1 <= nslots <= min(E, 1024)). The cache keeps both pointers until
+ * moe_cache_destroy; it creates one copy stream (default priority) and two
+ * events. Errors: MOE_EINVAL, MOE_ESHAPE, MOE_EALIGN, MOE_EHIP.
+ * moe_cache_prepare: makes experts ids[0..n) (host i32, in [0, E), at most
+ * nslots distinct; duplicates allowed) resident and writes their slots into
+ * slot_of (host i32 [n]). A resident expert is a hit; a miss takes the least
+ * recently used slot that this call does not name (empty slots first, then
+ * the lowest slot) and is copied (stride bytes) on the copy stream, which first
+ * waits for the work already on `stream`; `stream` then waits for the copies.
+ * So a forward enqueued on `stream` after the call, over moe_cache_bank's
+ * descriptor with idx mapped through slot_of, reads the right records, and no
+ * slot is overwritten while earlier work on `stream` may read it. Calls on one
+ * cache must not overlap (the cache has no lock). Errors are returned before
+ * any state changes.
+ * moe_cache_bank: the slot pool as a bank descriptor (E = nslots) for
+ * moe_nvfp4_forward / moe_nvfp4_layer.
+ * moe_cache_stats: hits and misses counted per id since creation, and bytes
+ * copied (nullable outputs). */
+typedef struct moe_expert_cache moe_expert_cache;
+int moe_cache_create(const moe_nvfp4_bank* host_bank, void* slot_base, int nslots, moe_expert_cache** out);
+int moe_cache_destroy(moe_expert_cache* c);
+int moe_cache_prepare(moe_expert_cache* c, const int32_t* ids, int n, int32_t* slot_of, void* stream);
+int moe_cache_bank(const moe_expert_cache* c, moe_nvfp4_bank* out);
+int moe_cache_stats(const moe_expert_cache* c, int64_t* hits, int64_t* misses, int64_t* bytes_copied);
+
 /* S1 + S2, routing ([PACK] intro: 8 of 256 experts per token; [VQ] "What
  * stays native": FP32 router logits).
  *   If x and w_router are both non-null: logits[t][e] = sum_h x[t][h]*Wr[e][h]

@@ -184,6 +184,40 @@ def global_from_ws2(ws2):
     return g, inexact
 
 
+def lru_slots(nslots, calls):
+    """The expert cache's placement rule, step by step in plain Python: for each
+    call (a list of expert ids) the slot of every id and the call's hits and
+    misses. A resident id is a hit (also an id placed earlier in the same call);
+    a miss takes, among the slots this call does not name, the one used longest
+    ago (never-used slots first), the lowest slot on a tie. Returns
+    [(slots, hits, misses)] per call. (The pages fix only that the cache is
+    bounded and fed on demand; least-recently-used eviction is our reading.)"""
+    holder = [None] * nslots       # expert in each slot
+    last = [0] * nslots            # call number of each slot's last use
+    where = {}
+    out = []
+    for t, ids in enumerate(calls, start=1):
+        named = {where[e] for e in ids if e in where}
+        slots, hits, misses = [], 0, 0
+        for e in ids:
+            if e in where:
+                hits += 1
+            else:
+                free = [s for s in range(nslots) if s not in named]
+                s = min(free, key=lambda q: (last[q], q))
+                if holder[s] is not None:
+                    del where[holder[s]]
+                holder[s] = e
+                where[e] = s
+                named.add(s)
+                misses += 1
+            slots.append(where[e])
+        for s in slots:
+            last[s] = t
+        out.append((slots, hits, misses))
+    return out
+
+
 def proj_shape(H, I, proj):
     return (H, I) if proj == DOWN else (I, H)
 

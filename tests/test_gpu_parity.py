@@ -208,6 +208,84 @@ def test_manifest_with_recovered_global_scales():
                                    "sha256": hashlib.sha256(rec[:nbytes].tobytes()).hexdigest()}, e
 
 
+# ---- expert cache: records in HBM slots, fed from pinned host memory ------------------
+def run_through_cache(dev_bank, dev_base, nslots, steps):
+    """steps: [(x_bits [T][H], idx [T][k], w [T][k])]. Each step prepares the
+    step's distinct experts (first-appearance order) in a cache over a pinned
+    host copy of the bank, runs the forward on the slot pool with idx mapped to
+    slots, and the same forward on the full device bank. Returns the outputs of
+    both, the slots and the per-step counts."""
+    host_mem = torch.empty(dev_base.numel(), dtype=torch.uint8, pin_memory=True)
+    host_mem.copy_(dev_base)
+    host_bank = wq.moe_nvfp4_bank()
+    host_bank.H, host_bank.I, host_bank.E = dev_bank.H, dev_bank.I, dev_bank.E
+    host_bank.record_bytes, host_bank.stride = dev_bank.record_bytes, dev_bank.stride
+    for i in range(9):
+        host_bank.part_off[i] = dev_bank.part_off[i]
+    host_bank.base = host_mem.data_ptr()
+    slots_mem = torch.empty(nslots * dev_bank.stride + 4096, dtype=torch.uint8, device=DEV)
+    off = (-slots_mem.data_ptr()) % 4096
+    slot_base = slots_mem[off:off + nslots * dev_bank.stride]
+    cache = wq.moe_cache_create(host_bank, slot_base, nslots)
+    try:
+        cb = wq.moe_cache_bank(cache)
+        cache_out, full_out, slots, counts = [], [], [], []
+        for x, idx, w in steps:
+            ids = list(dict.fromkeys(int(e) for e in np.asarray(idx).ravel()))
+            h0, m0, _ = wq.moe_cache_stats(cache)
+            slot_of = wq.moe_cache_prepare(cache, ids)
+            h1, m1, _ = wq.moe_cache_stats(cache)
+            remap = dict(zip(ids, slot_of.tolist()))
+            sidx = np.vectorize(remap.get)(np.asarray(idx)).astype(np.int32)
+            k = idx.shape[1]
+            cache_out.append(gpu_forward(cb, x, sidx, w, k))
+            full_out.append(gpu_forward(dev_bank, x, idx, w, k))
+            slots.append(slot_of.tolist())
+            counts.append((h1 - h0, m1 - m0))
+        return cache_out, full_out, slots, counts, wq.moe_cache_stats(cache)
+    finally:
+        wq.moe_cache_destroy(cache)
+
+
+def check_cache_run(nslots, steps, result, stride):
+    cache_out, full_out, slots, counts, (hits, misses, nbytes) = result
+    calls = [list(dict.fromkeys(int(e) for e in np.asarray(idx).ravel())) for _, idx, _ in steps]
+    want = oracle.lru_slots(nslots, calls)
+    for t in range(len(steps)):
+        assert slots[t] == want[t][0], t
+        assert counts[t] == (want[t][1], want[t][2]), t
+        # the same kernels on the same record bytes: identical outputs
+        assert np.array_equal(cache_out[t][0].view(np.uint32), full_out[t][0].view(np.uint32)), t
+        assert np.array_equal(cache_out[t][1], full_out[t][1]), t
+    assert misses == sum(m for _, _, m in want) and hits == sum(h for _, h, _ in want)
+    assert nbytes == misses * stride
+    say(f"cache of {nslots}: {hits} hits, {misses} misses over {len(steps)} steps")
+
+
+def test_expert_cache_tiny(tiny_bank):
+    bank, base = tiny_bank
+    c = W.CONFIGS["tiny"]
+    rng = np.random.default_rng(21)
+    x, _, _ = W.inputs("tiny")
+    steps = []
+    for t in range(40):
+        idx = np.stack([rng.choice(c["E"], size=c["k"], replace=False) for _ in range(2)]).astype(np.int32)
+        w = rng.uniform(0.1, 1.0, idx.shape).astype(np.float32)
+        steps.append((x[:2], idx, w))
+    check_cache_run(5, steps, run_through_cache(bank, base, 5, steps), bank.stride)
+
+
+def test_expert_cache_decode_full_shape(big_bank):
+    # single-token decode steps with Zipf-skewed routing (the batched config's
+    # 32 tokens, one per step), 64 slots of 256
+    bank, base = big_bank
+    c = W.CONFIGS["batched"]
+    x, _, logits = W.inputs("batched")
+    idx, w = oracle.route_topk(logits, c["k"])
+    steps = [(x[t:t + 1], idx[t:t + 1], w[t:t + 1]) for t in range(16)]
+    check_cache_run(64, steps, run_through_cache(bank, base, 64, steps), bank.stride)
+
+
 @pytest.mark.parametrize("proj", [0, 1, 2])
 def test_dequant_bit_exact_tiny(tiny_bank, proj):
     bank, base = tiny_bank

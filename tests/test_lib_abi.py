@@ -175,3 +175,20 @@ def test_manifest_part_table():
         assert off == end
         end = off + length
     assert end == b.record_bytes == 22118412
+
+
+def test_cache_validation_before_any_hip_call():
+    L = wq.lib()
+    host = _bank(256, 128, 16)
+    fake = C.c_void_p(1 << 26)
+    h = C.c_void_p()
+    assert L.moe_cache_create(C.byref(host), fake, 5, None) == wq.MOE_EINVAL
+    assert L.moe_cache_create(C.byref(host), fake, 0, C.byref(h)) == wq.MOE_ESHAPE
+    assert L.moe_cache_create(C.byref(host), fake, 17, C.byref(h)) == wq.MOE_ESHAPE
+    assert L.moe_cache_create(C.byref(host), None, 5, C.byref(h)) == wq.MOE_EINVAL
+    assert L.moe_cache_create(C.byref(host), C.c_void_p((1 << 26) + 256), 5, C.byref(h)) == wq.MOE_EALIGN
+    assert L.moe_cache_create(None, fake, 5, C.byref(h)) == wq.MOE_EINVAL
+    assert h.value is None
+    assert L.moe_cache_prepare(None, None, 0, None, None) == wq.MOE_EINVAL
+    assert L.moe_cache_bank(None, C.byref(host)) == wq.MOE_EINVAL
+    assert L.moe_cache_stats(None, None, None, None) == wq.MOE_EINVAL

@@ -2,7 +2,9 @@
 ("Beam 1.0 501B-A23B, streaming pack, NVFP4 experts / MLX 8-bit residents",
 "What this pack holds", global-scales bullet), and the library's host
 implementation against it (no GPU needed: the library's function runs on the
-host). The record digests are checked on the GPU in test_gpu_parity.py."""
+host). The record digests are checked on the GPU in test_gpu_parity.py. Also
+the expert cache's placement rule (oracle.lru_slots), pinned by a hand-worked
+example and invariants."""
 import ctypes as C
 
 import numpy as np
@@ -109,3 +111,38 @@ def test_library_rejects_bad_scales(bad):
     assert np.all(g == 7.0)  # nothing written
     assert L.moe_nvfp4_global_from_ws2(None, -1, None, None) == wq.MOE_EINVAL
     assert L.moe_nvfp4_global_from_ws2(None, 0, None, None) == wq.MOE_OK
+
+
+# ---- the expert cache's placement rule (oracle.lru_slots) ------------------------------
+def test_lru_slots_hand_worked():
+    # 3 slots. call 1 fills 0, 1 with experts 7, 8; call 2: 8 hits, 9 takes the
+    # empty slot 2; call 3: 7 hits (slot 0), 10 evicts the slot used longest ago
+    # among those not named: slot 1 (8, last used in call 2) and slot 2 (9,
+    # call 2) tie, the lower slot wins -> slot 1; call 4: 8 misses and takes
+    # slot 2 (9, call 2: older than slots 0 and 1, used in call 3)
+    got = oracle.lru_slots(3, [[7, 8], [8, 9], [7, 10], [8]])
+    assert got == [([0, 1], 0, 2), ([1, 2], 1, 1), ([0, 1], 1, 1), ([2], 0, 1)]
+
+
+def test_lru_slots_invariants():
+    rng = np.random.default_rng(8)
+    calls = [list(rng.choice(40, size=rng.integers(1, 6), replace=False)) for _ in range(300)]
+    # enough slots for everything: each expert misses exactly once
+    out = oracle.lru_slots(40, calls)
+    assert sum(m for _, _, m in out) == len({e for c in calls for e in c})
+    # a call's experts sit in distinct slots, and a hit keeps its slot
+    out = oracle.lru_slots(6, calls)
+    where = {}
+    for c, (slots, hits, misses) in zip(calls, out):
+        assert len(set(slots)) == len(c) and hits + misses == len(c)
+        assert hits == sum(1 for e in c if e in where)
+        for e, s in zip(c, slots):
+            if e in where:
+                assert where[e] == s
+        for e in list(where):
+            if where[e] in slots and e not in c:
+                del where[e]
+        for e, s in zip(c, slots):
+            where[e] = s
+    # duplicates inside a call count as hits after the first
+    assert oracle.lru_slots(2, [[3, 3, 4]]) == [([0, 0, 1], 1, 2)]

@@ -24,7 +24,8 @@ EXPORTS = [
     "moe_pack_nvfp4_bank", "moe_route_topk", "moe_sort_pairs", "moe_sort_workspace_bytes", "moe_sort_pairs_ws",
     "moe_nvfp4_workspace_bytes", "moe_nvfp4_forward", "moe_nvfp4_layer", "affine8_g64_linear", "moe_rmsnorm",
     "moe_nvfp4_dequant", "moe_profile_enable", "moe_profile_read", "moe_nvfp4_global_from_ws2",
-    "moe_nvfp4_record_sha256",
+    "moe_nvfp4_record_sha256", "moe_cache_create", "moe_cache_destroy", "moe_cache_prepare", "moe_cache_bank",
+    "moe_cache_stats",
 ]
 
 
@@ -86,6 +87,16 @@ def lib():
         L.moe_nvfp4_global_from_ws2.argtypes = [vp, C.c_int64, vp, vp]
         L.moe_nvfp4_record_sha256.restype = i32
         L.moe_nvfp4_record_sha256.argtypes = [bankp, i32, i32, vp, vp]
+        L.moe_cache_create.restype = i32
+        L.moe_cache_create.argtypes = [bankp, vp, i32, C.POINTER(vp)]
+        L.moe_cache_destroy.restype = i32
+        L.moe_cache_destroy.argtypes = [vp]
+        L.moe_cache_prepare.restype = i32
+        L.moe_cache_prepare.argtypes = [vp, vp, i32, vp, vp]
+        L.moe_cache_bank.restype = i32
+        L.moe_cache_bank.argtypes = [vp, bankp]
+        L.moe_cache_stats.restype = i32
+        L.moe_cache_stats.argtypes = [vp, C.POINTER(C.c_int64), C.POINTER(C.c_int64), C.POINTER(C.c_int64)]
         L.moe_profile_enable.restype = i32
         L.moe_profile_enable.argtypes = [i32]
         L.moe_profile_read.restype = i32
@@ -211,6 +222,40 @@ def moe_nvfp4_global_from_ws2(ws2):
 def moe_nvfp4_record_sha256(bank, e0, n, digests, stream=None):
     """digests: device uint8 [n][32]."""
     _check(lib().moe_nvfp4_record_sha256(C.byref(bank), e0, n, _ptr(digests), _stream(stream)))
+
+
+def moe_cache_create(host_bank, slot_base, nslots):
+    """host_bank: descriptor over pinned host memory; slot_base: device uint8
+    tensor of nslots * stride bytes (4096-aligned). Returns the handle."""
+    h = C.c_void_p()
+    _check(lib().moe_cache_create(C.byref(host_bank), _ptr(slot_base), nslots, C.byref(h)))
+    return h
+
+
+def moe_cache_destroy(handle):
+    _check(lib().moe_cache_destroy(handle))
+
+
+def moe_cache_prepare(handle, ids, stream=None):
+    """ids: host int sequence; returns the slots (numpy int32)."""
+    import numpy as np
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    slot_of = np.empty_like(ids)
+    _check(lib().moe_cache_prepare(handle, ids.ctypes.data_as(C.c_void_p), ids.size,
+                                   slot_of.ctypes.data_as(C.c_void_p), _stream(stream)))
+    return slot_of
+
+
+def moe_cache_bank(handle):
+    b = moe_nvfp4_bank()
+    _check(lib().moe_cache_bank(handle, C.byref(b)))
+    return b
+
+
+def moe_cache_stats(handle):
+    h, m, n = C.c_int64(), C.c_int64(), C.c_int64()
+    _check(lib().moe_cache_stats(handle, C.byref(h), C.byref(m), C.byref(n)))
+    return h.value, m.value, n.value
 
 
 def moe_profile_enable(on):

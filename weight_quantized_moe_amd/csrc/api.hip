@@ -215,6 +215,71 @@ MOE_API int moe_nvfp4_record_sha256(const moe_nvfp4_bank* b, int e0, int n, uint
                    "record_sha256");
 }
 
+// ---- expert cache (host bank, HBM slots) ------------------------------------------
+// The host bank's checks are the device bank's, without the device alignment
+// of its base (host memory from the caller's pinned allocation).
+static int host_bank_ok(const moe_nvfp4_bank* b, const char* who) {
+  if (!b || !b->base) return fail(MOE_EINVAL, "%s: null bank", who);
+  if (!record_shape_ok(b->H, b->I) || b->E < 1)
+    return fail(MOE_ESHAPE, "%s: bank shape H=%d I=%d E=%d", who, b->H, b->I, b->E);
+  if (b->stride < b->record_bytes || b->record_bytes != moe_nvfp4_record_bytes(b->H, b->I) || b->stride % 4096)
+    return fail(MOE_EINVAL, "%s: record size/stride inconsistent with H, I", who);
+  return MOE_OK;
+}
+
+MOE_API int moe_cache_create(const moe_nvfp4_bank* host_bank, void* slot_base, int nslots, moe_expert_cache** out) {
+  int rc = host_bank_ok(host_bank, "cache_create");
+  if (rc) return rc;
+  if (!out) return fail(MOE_EINVAL, "cache_create: null out");
+  if (nslots < 1 || nslots > 1024 || nslots > host_bank->E)
+    return fail(MOE_ESHAPE, "cache_create: nslots=%d outside [1, min(E, 1024)]", nslots);
+  if (!slot_base) return fail(MOE_EINVAL, "cache_create: null slot_base");
+  if (!aligned(slot_base, 4096)) return fail(MOE_EALIGN, "cache_create: slot_base not 4096-byte aligned");
+  rc = cache_create(host_bank, slot_base, nslots, out);
+  if (rc == MOE_EHIP) return fail(MOE_EHIP, "cache_create: stream or event creation failed");
+  if (rc) return fail(rc, "cache_create: out of host memory");
+  return MOE_OK;
+}
+
+MOE_API int moe_cache_destroy(moe_expert_cache* c) {
+  cache_destroy(c);
+  return MOE_OK;
+}
+
+MOE_API int moe_cache_prepare(moe_expert_cache* c, const int32_t* ids, int n, int32_t* slot_of, void* stream) {
+  if (!c) return fail(MOE_EINVAL, "cache_prepare: null cache");
+  if (n < 0) return fail(MOE_EINVAL, "cache_prepare: n=%d < 0", n);
+  if (n > 0 && (!ids || !slot_of)) return fail(MOE_EINVAL, "cache_prepare: null ids/slot_of");
+  const int E = cache_experts(c);
+  moe_nvfp4_bank view;
+  cache_view(c, &view);
+  std::vector<uint8_t> mark(E, 0);
+  int distinct = 0;
+  for (int i = 0; i < n; i++) {
+    if (ids[i] < 0 || ids[i] >= E) return fail(MOE_EINVAL, "cache_prepare: ids[%d] = %d outside [0, %d)", i, ids[i], E);
+    if (!mark[ids[i]]) {
+      mark[ids[i]] = 1;
+      distinct++;
+    }
+  }
+  if (distinct > view.E) return fail(MOE_EINVAL, "cache_prepare: %d distinct experts do not fit %d slots", distinct, view.E);
+  char err[256] = "";
+  const int rc = cache_prepare(c, ids, n, slot_of, static_cast<hipStream_t>(stream), err, sizeof(err));
+  if (rc) return fail(rc, "%s", err);
+  return MOE_OK;
+}
+
+MOE_API int moe_cache_bank(const moe_expert_cache* c, moe_nvfp4_bank* out) {
+  if (!c || !out) return fail(MOE_EINVAL, "cache_bank: null argument");
+  return cache_view(c, out);
+}
+
+MOE_API int moe_cache_stats(const moe_expert_cache* c, int64_t* hits, int64_t* misses, int64_t* bytes_copied) {
+  if (!c) return fail(MOE_EINVAL, "cache_stats: null cache");
+  cache_stats(c, hits, misses, bytes_copied);
+  return MOE_OK;
+}
+
 // ---- S1 + S2 routing -----------------------------------------------------------
 MOE_API int moe_route_topk(const uint16_t* x, const float* w_router, float* logits, int T, int H,
                            int E, int k, int32_t* idx, float* w, void* stream) {

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+struct moe_nvfp4_bank;
+struct moe_expert_cache;
+
 namespace moe {
 
 // Where one bank's parts live: byte offsets inside every record.
@@ -44,6 +47,15 @@ hipError_t launch_sort(const int32_t* idx, int P, int E, RouteTables rt, int mti
 // (returns whether it is exact); SHA-256 of records e0 .. e0 + n - 1 over
 // their first nbytes bytes, digests [n][32] (device, 4-byte aligned)
 bool global_from_ws2_one(float ws2, float* g);
+// the expert cache's host logic and copies (arguments checked by the caller;
+// prepare's ids are in [0, E) with at most nslots distinct)
+int cache_create(const moe_nvfp4_bank* host, void* slot_base, int nslots, moe_expert_cache** out);
+void cache_destroy(moe_expert_cache* c);
+int cache_prepare(moe_expert_cache* c, const int32_t* ids, int n, int32_t* slot_of, hipStream_t stream, char* err,
+                  size_t errlen);
+int cache_view(const moe_expert_cache* c, moe_nvfp4_bank* out);
+int cache_experts(const moe_expert_cache* c);
+void cache_stats(const moe_expert_cache* c, int64_t* hits, int64_t* misses, int64_t* bytes);
 hipError_t launch_record_sha256(const uint8_t* base, uint64_t stride, uint64_t nbytes, int e0, int n,
                                 uint8_t* digests, hipStream_t s);
 
