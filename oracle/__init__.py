@@ -54,6 +54,19 @@ def lib():
         L.orc_moe_forward.restype = C.c_int
         L.orc_moe_forward.argtypes = [C.POINTER(u8p), C.c_int, C.c_int, C.c_int, u16p, C.c_int,
                                       i32p, f32p, C.c_int, u16p, C.c_int, f32p, u16p, u16p]
+        L.orc_f16_value.restype = C.c_double
+        L.orc_f16_value.argtypes = [C.c_uint16]
+        L.orc_vq_index.restype = C.c_uint
+        L.orc_vq_index.argtypes = [u8p, C.c_uint64]
+        L.orc_vq_layout.restype = C.c_int
+        L.orc_vq_layout.argtypes = [C.c_int, C.c_int, u64p, u64p, u64p]
+        L.orc_vq_pack_record.restype = None
+        L.orc_vq_pack_record.argtypes = [C.c_int, C.c_int, C.POINTER(u8p), C.POINTER(u16p), u8p]
+        L.orc_vq_dequant_projection.restype = None
+        L.orc_vq_dequant_projection.argtypes = [u8p, u8p, C.c_int, C.c_int, C.c_int, f32p]
+        L.orc_vq_moe_forward.restype = C.c_int
+        L.orc_vq_moe_forward.argtypes = [C.POINTER(u8p), u8p, C.c_int, C.c_int, C.c_int, u16p, C.c_int,
+                                         i32p, f32p, C.c_int, u16p, C.c_int, f32p, u16p]
         L.orc_q8_quantize.restype = C.c_int
         L.orc_q8_quantize.argtypes = [u16p, C.c_int, C.c_int, u32p, u16p, u16p]
         L.orc_affine8_linear.restype = C.c_int
@@ -292,6 +305,73 @@ def moe_forward(records, E, H, I, x_bf16, idx, w, residual=None, acc=ACC_F64, wa
     if rc != 0:
         raise ValueError("moe_forward: bad argument or missing record")
     return (yf, yb, mid) if want_mid else (yf, yb)
+
+
+# ---- 8-dim VQ experts ([VQ] "Recipe", routed-experts bullet) -----------------
+def f16_value(bits):
+    return lib().orc_f16_value(int(bits))
+
+
+def vq_index(row_bytes, j):
+    r = np.ascontiguousarray(row_bytes, dtype=np.uint8)
+    return lib().orc_vq_index(_p(r, C.c_uint8), j)
+
+
+def vq_layout(H, I):
+    off = (C.c_uint64 * 6)()
+    nb, st = C.c_uint64(), C.c_uint64()
+    if lib().orc_vq_layout(H, I, off, C.byref(nb), C.byref(st)) != 0:
+        raise ValueError("bad shape")
+    return [int(o) for o in off], int(nb.value), int(st.value)
+
+
+def vq_pack_record(H, I, idx, gains):
+    """idx[p]: uint8 packed index rows [out][in*3/16]; gains[p]: f16 bits [out]."""
+    _, _, stride = vq_layout(H, I)
+    idx = [np.ascontiguousarray(a, dtype=np.uint8) for a in idx]
+    gains = [np.ascontiguousarray(g, dtype=np.uint16) for g in gains]
+    ip = (C.POINTER(C.c_uint8) * 3)(*[_p(a, C.c_uint8) for a in idx])
+    gp = (C.POINTER(C.c_uint16) * 3)(*[_p(g, C.c_uint16) for g in gains])
+    out = np.empty(stride, dtype=np.uint8)
+    lib().orc_vq_pack_record(H, I, ip, gp, _p(out, C.c_uint8))
+    return out
+
+
+def vq_dequant_projection(record, codebook, H, I, proj):
+    out, inn = proj_shape(H, I, proj)
+    w = np.empty((out, inn), dtype=np.float32)
+    r = np.ascontiguousarray(record, dtype=np.uint8)
+    cb = np.ascontiguousarray(codebook, dtype=np.uint8).ravel()
+    lib().orc_vq_dequant_projection(_p(r, C.c_uint8), _p(cb, C.c_uint8), H, I, proj, _p(w, C.c_float))
+    return w
+
+
+def vq_moe_forward(records, codebook, E, H, I, x_bf16, idx, w, residual=None, acc=ACC_F64):
+    """moe_forward over VQ records (dict or list expert -> record bytes)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    T = x.shape[0]
+    ix = np.ascontiguousarray(idx, dtype=np.int32)
+    wv = np.ascontiguousarray(w, dtype=np.float32)
+    k = ix.shape[1]
+    keep = []
+    ptrs = (C.POINTER(C.c_uint8) * E)()
+    items = records.items() if isinstance(records, dict) else enumerate(records)
+    for e, r in items:
+        if r is None:
+            continue
+        r = np.ascontiguousarray(r, dtype=np.uint8)
+        keep.append(r)
+        ptrs[int(e)] = _p(r, C.c_uint8)
+    cb = np.ascontiguousarray(codebook, dtype=np.uint8).ravel()
+    res = None if residual is None else np.ascontiguousarray(residual, dtype=np.uint16)
+    yf = np.empty((T, H), dtype=np.float32)
+    yb = np.empty((T, H), dtype=np.uint16)
+    rc = lib().orc_vq_moe_forward(ptrs, _p(cb, C.c_uint8), E, H, I, _p(x, C.c_uint16), T, _p(ix, C.c_int32),
+                                  _p(wv, C.c_float), k, _p(res, C.c_uint16), acc, _p(yf, C.c_float),
+                                  _p(yb, C.c_uint16))
+    if rc != 0:
+        raise ValueError("vq_moe_forward: bad argument or missing record")
+    return yf, yb
 
 
 # ---- residents -----------------------------------------------------------

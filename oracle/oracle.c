@@ -265,10 +265,14 @@ static void matvec(const float* A, int rows, int cols, const float* xv, int acc,
   }
 }
 
-int orc_moe_forward(const uint8_t* const* records, int E, int H, int I, const uint16_t* x,
-                    int T, const int32_t* idx, const float* w, int k,
-                    const uint16_t* residual, int acc, float* y_f32, uint16_t* y_bf16,
-                    uint16_t* mid_bf16) {
+/* The layer over any expert format: deq(ctx, e, proj, W) writes expert e's
+ * dense f32 matrix of projection proj ([out][in]). */
+typedef void (*orc_deq_fn)(const void* ctx, int e, int H, int I, int proj, float* W);
+
+static int moe_forward_core(const uint8_t* const* records, orc_deq_fn deq, const void* ctx, int E, int H,
+                            int I, const uint16_t* x, int T, const int32_t* idx, const float* w, int k,
+                            const uint16_t* residual, int acc, float* y_f32, uint16_t* y_bf16,
+                            uint16_t* mid_bf16) {
   if (H <= 0 || I <= 0 || H % 16 || I % 16 || T < 0 || k < 1 || k > E) return -1;
   size_t P = (size_t)T * (size_t)k;
   for (size_t p = 0; p < P; p++)
@@ -293,9 +297,9 @@ int orc_moe_forward(const uint8_t* const* records, int E, int H, int I, const ui
     int used = 0;
     for (size_t p = 0; p < P && !used; p++) used = (idx[p] == e);
     if (!used) continue;
-    orc_dequant_projection(records[e], H, I, ORC_GATE, Wg, NULL);
-    orc_dequant_projection(records[e], H, I, ORC_UP, Wu, NULL);
-    orc_dequant_projection(records[e], H, I, ORC_DOWN, Wd, NULL);
+    deq(ctx, e, H, I, ORC_GATE, Wg);
+    deq(ctx, e, H, I, ORC_UP, Wu);
+    deq(ctx, e, H, I, ORC_DOWN, Wd);
     for (size_t p = 0; p < P; p++) {
       if (idx[p] != e) continue;
       size_t t = p / (size_t)k;
@@ -354,6 +358,115 @@ done:
   free(uv);
   free(d_all);
   return rc;
+}
+
+static void nvfp4_deq(const void* ctx, int e, int H, int I, int proj, float* W) {
+  const uint8_t* const* records = (const uint8_t* const*)ctx;
+  orc_dequant_projection(records[e], H, I, proj, W, NULL);
+}
+
+int orc_moe_forward(const uint8_t* const* records, int E, int H, int I, const uint16_t* x,
+                    int T, const int32_t* idx, const float* w, int k,
+                    const uint16_t* residual, int acc, float* y_f32, uint16_t* y_bf16,
+                    uint16_t* mid_bf16) {
+  return moe_forward_core(records, nvfp4_deq, records, E, H, I, x, T, idx, w, k, residual, acc, y_f32,
+                          y_bf16, mid_bf16);
+}
+
+/* ------------------------------------------------------------------------ */
+/* 8-dim VQ experts ([VQ] "Recipe", routed-experts bullet)                   */
+/* ------------------------------------------------------------------------ */
+
+double orc_f16_value(uint16_t h) {
+  int s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24); /* subnormal: m * 2^-14 / 1024 */
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp(1.0 + (double)m / 1024.0, e - 15);
+  return s ? -v : v;
+}
+
+unsigned orc_vq_index(const uint8_t* row, uint64_t j) {
+  /* bits 12j .. 12j+11 of the row's little-endian bit stream */
+  uint64_t bit = 12 * j;
+  unsigned lo = row[bit / 8], hi = row[bit / 8 + 1];
+  return ((lo | (hi << 8)) >> (bit % 8)) & 0xFFFu;
+}
+
+static uint64_t up16(uint64_t n) { return (n + 15) / 16 * 16; }
+
+int orc_vq_layout(int H, int I, uint64_t part_off[6], uint64_t* record_bytes, uint64_t* stride) {
+  if (H <= 0 || I <= 0 || H % 64 || I % 64) return -1;
+  uint64_t off = 0;
+  for (int p = 0; p < 3; p++) {
+    int out, in;
+    proj_shape(H, I, p, &out, &in);
+    part_off[2 * p] = off;
+    off = up16(off + (uint64_t)out * ((uint64_t)in / 8 * 12 / 8)); /* 12 bits per 8 weights */
+    part_off[2 * p + 1] = off;
+    off = up16(off + (uint64_t)out * 2); /* one f16 gain per row */
+  }
+  *record_bytes = off;
+  *stride = (off + 4095) / 4096 * 4096;
+  return 0;
+}
+
+void orc_vq_pack_record(int H, int I, const uint8_t* const idx[3], const uint16_t* const gain[3],
+                        uint8_t* dst) {
+  uint64_t off[6], bytes, stride;
+  orc_vq_layout(H, I, off, &bytes, &stride);
+  memset(dst, 0, stride);
+  for (int p = 0; p < 3; p++) {
+    int out, in;
+    proj_shape(H, I, p, &out, &in);
+    memcpy(dst + off[2 * p], idx[p], (uint64_t)out * ((uint64_t)in / 8 * 12 / 8));
+    for (int r = 0; r < out; r++) {
+      dst[off[2 * p + 1] + 2 * (uint64_t)r] = (uint8_t)(gain[p][r] & 0xFF);
+      dst[off[2 * p + 1] + 2 * (uint64_t)r + 1] = (uint8_t)(gain[p][r] >> 8);
+    }
+  }
+}
+
+void orc_vq_dequant_projection(const uint8_t* record, const uint8_t* codebook, int H, int I, int proj,
+                               float* w_out) {
+  uint64_t off[6], bytes, stride;
+  orc_vq_layout(H, I, off, &bytes, &stride);
+  int out, in;
+  proj_shape(H, I, proj, &out, &in);
+  const uint64_t row_bytes = (uint64_t)in / 8 * 12 / 8;
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < out; r++) {
+    const uint8_t* row = record + off[2 * proj] + (uint64_t)r * row_bytes;
+    uint16_t gb = (uint16_t)(record[off[2 * proj + 1] + 2 * (uint64_t)r] |
+                             (record[off[2 * proj + 1] + 2 * (uint64_t)r + 1] << 8));
+    double gain = orc_f16_value(gb);
+    for (int j = 0; j < in / 8; j++) {
+      unsigned c = orc_vq_index(row, (uint64_t)j);
+      for (int i = 0; i < 8; i++) /* exact: 11 x 4 significant bits */
+        w_out[(uint64_t)r * in + 8 * j + i] = (float)(gain * orc_e4m3_value(codebook[8 * c + i]));
+    }
+  }
+}
+
+typedef struct {
+  const uint8_t* const* records;
+  const uint8_t* codebook;
+} vq_ctx;
+
+static void vq_deq(const void* ctx, int e, int H, int I, int proj, float* W) {
+  const vq_ctx* c = (const vq_ctx*)ctx;
+  orc_vq_dequant_projection(c->records[e], c->codebook, H, I, proj, W);
+}
+
+int orc_vq_moe_forward(const uint8_t* const* records, const uint8_t* codebook, int E, int H, int I,
+                       const uint16_t* x, int T, const int32_t* idx, const float* w, int k,
+                       const uint16_t* residual, int acc, float* y_f32, uint16_t* y_bf16) {
+  vq_ctx c = {records, codebook};
+  if (H % 64 || I % 64) return -1;
+  return moe_forward_core(records, vq_deq, &c, E, H, I, x, T, idx, w, k, residual, acc, y_f32, y_bf16, NULL);
 }
 
 /* ------------------------------------------------------------------------ */

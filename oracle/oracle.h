@@ -76,6 +76,31 @@ void orc_pack_record(int H, int I, const uint32_t* const codes[3],
 void orc_dequant_projection(const uint8_t* record, int H, int I, int proj,
                             float* w_out, uint16_t* unit_out);
 
+/* ---- 8-dim VQ experts, [VQ] "Recipe" routed-experts bullet ------------------
+ * Every 8 consecutive weights of an expert row are one index into a codebook
+ * of 8-dim E4M3 codewords (one book per layer, shared by all experts and by
+ * gate/up/down), times one F16 gain per row. 12-bit indices: 4,096 codewords
+ * of 8 bytes, 32 KiB (the [VQ] kernel budget leaves 27 KiB of 99 KiB beside
+ * 40 KiB of mids at 12 bits). Readings: index j of a row is bits 12j..12j+11 of
+ * the row's little-endian bit stream; codeword c is bytes 8c..8c+7, element i
+ * at byte 8c+i; a record holds gate.idx, gate.gain, up.idx, up.gain,
+ * down.idx, down.gain, each part starting on 16 bytes, records on 4 KiB; the
+ * weight is gain * e4m3(codeword element), exact in f32. */
+double orc_f16_value(uint16_t h);
+unsigned orc_vq_index(const uint8_t* row, uint64_t j);
+/* part_off[2p] = index rows of projection p, part_off[2p+1] = its gains;
+ * H and I multiples of 64; returns 0 or -1 */
+int orc_vq_layout(int H, int I, uint64_t part_off[6], uint64_t* record_bytes, uint64_t* stride);
+/* idx[p]: packed index rows [out_p][in_p * 3 / 16] bytes; gain[p]: f16 bits [out_p] */
+void orc_vq_pack_record(int H, int I, const uint8_t* const idx[3], const uint16_t* const gain[3],
+                        uint8_t* dst);
+void orc_vq_dequant_projection(const uint8_t* record, const uint8_t* codebook, int H, int I, int proj,
+                               float* w_out);
+/* the layer of orc_moe_forward over VQ records (codebook: 4096 x 8 bytes) */
+int orc_vq_moe_forward(const uint8_t* const* records, const uint8_t* codebook, int E, int H, int I,
+                       const uint16_t* x, int T, const int32_t* idx, const float* w, int k,
+                       const uint16_t* residual, int acc, float* y_f32, uint16_t* y_bf16);
+
 /* ---- routing ------------------------------------------------------------ */
 /* logits[t][e] = f32( sum_h x[t][h] * Wr[e][h] ), sum in f64; [VQ] "What stays
  * native" keeps router logits in FP32. x bf16 [T][H], Wr f32 [E][H] (one row

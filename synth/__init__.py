@@ -35,6 +35,8 @@ MASK64 = (1 << 64) - 1
 S_X, S_WR, S_LOGIT, S_PERM, S_G, S_AFF = 1, 2, 3, 4, 5, 6
 S_CODES = 1 << 20
 S_SCALES = 2 << 20
+S_VQIDX = 3 << 20
+S_VQGAIN, S_CB = 7, 8
 
 
 def _signed(v: int) -> int:
@@ -202,3 +204,27 @@ def expert_globals(seed, expert):
     """g (gate, up, down) of one expert: entries 3e..3e+2 of the globals stream"""
     u = uniform01_np(seed, S_G, 3, start=3 * expert)
     return (2688.0 * (0.5 + 1.5 * u)).astype(np.float32)
+
+
+# ---- 8-dim VQ experts -------------------------------------------------------
+def vq_codebook(seed, n=4096):
+    """n codewords of 8 E4M3 bytes [n][8]: N(0,1) values rounded f32 -> f16 ->
+    E4M3 (round to nearest even at each step)"""
+    z = normal_np(seed, S_CB, 8 * n).astype(np.float32)
+    h = z.astype(np.float16).astype(np.float32)
+    return torch.from_numpy(h).to(torch.float8_e4m3fn).view(torch.uint8).numpy().reshape(n, 8)
+
+
+def vq_expert_parts(seed, expert, H, I, device="cpu"):
+    """idx[p]: uint8 packed 12-bit index rows [out][in * 3 / 16] (uniform
+    indices: uniform bytes), gains[p]: f16 bits [out] of 0.02 * U(0.5, 2);
+    p = gate, up, down (gate and up [I][H], down [H][I])."""
+    idx, gains = [], []
+    for p in range(3):
+        out, inn = (H, I) if p == 2 else (I, H)
+        nbytes = out * inn * 3 // 16
+        w = code_words(seed, S_VQIDX + 3 * expert + p, nbytes // 4, device)
+        idx.append(w.view(torch.uint8).reshape(out, inn * 3 // 16))
+        u = uniform01_np(seed, S_VQGAIN, out, start=(3 * expert + p) << 16)
+        gains.append((0.02 * (0.5 + 1.5 * u)).astype(np.float16).view(np.uint16))
+    return idx, gains
