@@ -31,8 +31,14 @@ decode steps on Zipf(1.1)-skewed routing; reports the host-to-HBM copy rate
 on an all-miss pattern against PCIe 5.0 x16 (64 GB/s per direction), and per
 pool size the hit rate and the time per step (prepare + forward).
 
+VQ leg (--only vq, not part of the default run): the same single-token decode
+step over the 8-dim VQ expert format (256 records of 7,393,280 B, 12-bit
+indices, a 32 KiB E4M3 codebook): moe_route_topk (router + top-k) then
+moe_vq_forward, as GB/s of algorithmic bytes (8 VQ records + the f32 router +
+the codebook + x and y).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--prefill-steps P]
-       [--only decode|prefill|cache] [--no-cpu-baseline] [--two-call]
+       [--only decode|prefill|cache|vq] [--no-cpu-baseline] [--two-call]
 Profiling helpers: --copy-calibration (device copies of 1 GiB, for the
 counter scale factor); --summarize-pmc DIR (per-kernel mean counter values
 per dispatch from a rocprofv3 --pmc output directory; no GPU needed).
@@ -261,6 +267,55 @@ def prefill_leg(bank, P):
             "kernels_us": {n_: round(v[0] * 1e3, 2) for n_, v in pk.items()}}
 
 
+def vq_leg(K, Wm):
+    c = W.CONFIGS["decode"]
+    H, I, E, k = c["H"], c["I"], c["E"], c["k"]
+    bank, base, cb = W.build_vq_bank(32, H, I, E)
+    xs = bf16_dev(np.stack([W.inputs("decode", v)[0] for v in range(ROTATE)]))
+    _, Wr, _ = W.inputs("decode")
+    Wr = torch.from_numpy(Wr).cuda()
+    logits = torch.empty((1, E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((ROTATE, 1, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((ROTATE, 1, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((1, H), dtype=torch.int16, device="cuda")
+    ws = wq.workspace(wq.moe_vq_workspace_bytes(1, k, H, I))
+    state = {"i": 0}
+
+    def step():
+        r = state["i"] % ROTATE
+        state["i"] += 1
+        wq.moe_route_topk(xs[r], Wr, logits, 1, H, E, k, idx[r], w[r])
+        wq.moe_vq_forward(bank, xs[r], 1, idx[r], w[r], k, None, y, 0, ws)
+
+    ms_total, _ = timed(step, K, Wm)
+    idx_h = idx.cpu().numpy()
+    rs = [(Wm + i) % ROTATE for i in range(K)]
+    rec = wq.moe_vq_record_bytes(H, I)
+    nb = np.array([len(np.unique(idx_h[r])) * rec + H * E * 4 + 32768 + 2 * H * 2 for r in rs], dtype=np.float64)
+    gbs = nb.sum() / (ms_total * 1e-3) / 1e9
+    wq.moe_profile_enable(True)
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    kern = {}
+    for name in ["router", "topk", "vq_gateup", "vq_down"]:
+        avg, cnt = kernel_avg_ms(name)
+        if cnt:
+            kern[name] = round(avg * 1e3, 2)
+    wq.moe_profile_enable(False)
+    gu_bytes = np.mean([len(np.unique(idx_h[r])) * 2 * I * (H * 3 // 16 + 2) for r in rs]) + 32768 + H * 2 + k * I * 2
+    gu_gbs = gu_bytes / (kern["vq_gateup"] * 1e-6) / 1e9
+    log(f"vq decode: {ms_total / K * 1e3:.1f} us/step, {gbs:.1f} GB/s; kernels {kern}")
+    return {"value": round(gbs, 2), "unit": "GB/s", "steps": K, "us_per_step": round(ms_total / K * 1e3, 2),
+            "workload": "decode T=1 over 8-dim VQ records (12-bit indices, 32 KiB E4M3 codebook), H=5120, I=2560, "
+                        "256 experts, top-8; router f32; 64 rotating activations",
+            "bytes_per_step": int(nb.mean()),
+            "roofline": {"kernel": "vq_gateup", "bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": int(gu_bytes),
+                         "avg_launch_us": kern["vq_gateup"]},
+            "kernels_us": kern}
+
+
 def cache_leg(bank, base, pools=(32, 64, 128, 192), steps=256, warm=64):
     c = W.CONFIGS["decode"]
     E, k, H = c["E"], c["k"], c["H"]
@@ -352,7 +407,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "cache"])
+    ap.add_argument("--only", choices=["decode", "prefill", "cache", "vq"])
     ap.add_argument("--two-call", action="store_true",
                     help="decode step as moe_route_topk + moe_nvfp4_forward instead of moe_nvfp4_layer")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -372,6 +427,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.only == "vq":
+        print(json.dumps({"vq": vq_leg(args.steps, args.warmup)}), flush=True)
         return
     c = W.CONFIGS["decode"]
     log(f"building the bank: {c['E']} records of {wq.moe_nvfp4_record_bytes(c['H'], c['I'])} B")

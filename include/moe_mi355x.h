@@ -232,12 +232,57 @@ int moe_rmsnorm(const uint16_t* x, int T, int H, float eps, uint16_t* y, void* s
 int moe_nvfp4_dequant(const moe_nvfp4_bank* b, int expert, int proj, float* out_f32,
                       uint16_t* out_unit, void* stream);
 
+/* ---- 8-dim VQ experts, a second record format for the same layer ----------
+ * "Beam-1.0-501B-A23B VQ GGUF", "Recipe", routed-experts bullet: every 8
+ * consecutive weights of an expert row are one 12-bit index into a codebook
+ * of 4,096 codewords of 8 E4M3 bytes (one codebook per layer, shared by all
+ * experts and by gate/up/down), times one F16 gain per row: weight =
+ * gain * e4m3(codeword[index][i]), exact in f32. Index j of a row is bits
+ * 12j..12j+11 of the row's little-endian bit stream (8 indices in 12 bytes).
+ * Record: gate.idx [I][H*3/16] bytes, gate.gain f16 [I], up.idx, up.gain,
+ * down.idx [H][I*3/16], down.gain [H], each part on 16 bytes; records every
+ * `stride` bytes (record size rounded up to 4 KiB). At H = 5120, I = 2560:
+ * 7,393,280 B per record, 1.5 bits per weight. H and I multiples of 64. */
+size_t moe_vq_record_bytes(int H, int I);  /* 0 on bad shape */
+size_t moe_vq_record_stride(int H, int I);
+
+typedef struct moe_vq_bank {
+  int32_t H, I, E, reserved;
+  uint64_t record_bytes, stride;
+  uint64_t part_off[6]; /* part_off[2p] index rows, part_off[2p+1] gains of projection p */
+  void* base;           /* device, E * stride bytes, 4096-byte aligned */
+  const void* codebook; /* device, 4096 * 8 bytes (E4M3), 16-byte aligned */
+} moe_vq_bank;
+
+/* Fills *b with the default layout. Errors: MOE_EINVAL (null), MOE_ESHAPE
+ * (H, I not positive multiples of 64; E outside [1, 1024]), MOE_EALIGN. */
+int moe_vq_bank_init(moe_vq_bank* b, void* base, const void* codebook, int H, int I, int E);
+/* Copies each expert's parts into its record and zeroes the pad:
+ * idx[p] bytes [E][out_p][in_p*3/16], gain[p] f16 bits [E][out_p], host or
+ * device memory (host sources must stay valid until the stream reaches the
+ * copies). */
+int moe_vq_pack_bank(const moe_vq_bank* b, const uint8_t* const idx[3], const uint16_t* const gain[3],
+                     void* stream);
+/* Test export: f32 [out][in] weights of one projection of one record, through
+ * the kernels' own conversion path. */
+int moe_vq_dequant(const moe_vq_bank* b, int expert, int proj, float* out_f32, void* stream);
+/* The layer of moe_nvfp4_forward over VQ records (same arguments, flags
+ * MOE_F32_OUT only; expert-streaming kernels for any T, k <= 16, and
+ * 32 KiB + k*I*2 bytes of codebook and mids must fit the LDS). workspace:
+ * device, 256-byte aligned, >= moe_vq_workspace_bytes(T, k, H, I) (0 on bad
+ * arguments). idx values outside [0, E) contribute nothing. */
+size_t moe_vq_workspace_bytes(int T, int k, int H, int I);
+int moe_vq_forward(const moe_vq_bank* b, const uint16_t* x, int T, const int32_t* idx, const float* w, int k,
+                   const uint16_t* residual, void* y, unsigned flags, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
 /* Kernel timing with HIP events that hipExtLaunchKernel records at each
  * kernel's own start and end on its stream. moe_profile_enable(1) clears and
  * starts collection; moe_profile_read(name, ...) synchronizes the events and
  * returns the summed duration and count of the kernel family `name` since the
  * last enable. Names: "router", "topk", "sort", "decode_gateup", "decode_down",
- * "combine", "prefill_gateup", "prefill_down", "affine8", "rmsnorm", "sha256". */
+ * "combine", "prefill_gateup", "prefill_down", "affine8", "rmsnorm", "sha256",
+ * "vq_gateup", "vq_down", "vq_dequant". */
 int moe_profile_enable(int on);
 int moe_profile_read(const char* name, double* total_ms, int64_t* launches);
 

@@ -13,7 +13,7 @@ Banks are packed through the library's own pack entry point.
 import numpy as np
 import torch
 
-from . import activations, expert_parts, router_weights, skewed_logits
+from . import activations, expert_parts, router_weights, skewed_logits, vq_codebook, vq_expert_parts
 
 CONFIGS = {
     "tiny": dict(H=256, I=128, E=16, k=2, T=4, routing="router", seed=0, bank_seed=0),
@@ -42,6 +42,26 @@ def build_bank(seed, H, I, E, device="cuda", chunk=16, expert0=0):
         del parts, codes, scales, g
     torch.cuda.synchronize()
     return bank, base
+
+
+def build_vq_bank(seed, H, I, E, device="cuda", chunk=16):
+    """A packed bank of E 8-dim VQ records (expert e holds the seeded parts of
+    expert e) over the seeded codebook. Returns (descriptor, base, codebook)."""
+    import weight_quantized_moe_amd as wq
+
+    cb = torch.from_numpy(vq_codebook(seed).reshape(-1).copy()).to(device)
+    bank, base = wq.alloc_vq_bank(cb, H, I, E, device)
+    stride = bank.stride
+    for e0 in range(0, E, chunk):
+        n = min(chunk, E - e0)
+        parts = [vq_expert_parts(seed, e0 + j, H, I, device) for j in range(n)]
+        idx = [torch.stack([p[0][q] for p in parts]).contiguous() for q in range(3)]
+        gains = [torch.from_numpy(np.stack([p[1][q] for p in parts]).view(np.int16)).to(device) for q in range(3)]
+        sub = wq.moe_vq_bank_init(base[e0 * stride:(e0 + n) * stride], cb, H, I, n)
+        wq.moe_vq_pack_bank(sub, idx, gains)
+        del parts, idx, gains
+    torch.cuda.synchronize()
+    return bank, base, cb
 
 
 def host_parts(seed, expert, H, I):

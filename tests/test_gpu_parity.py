@@ -144,6 +144,88 @@ def test_pack_bytes_match_oracle_sampled_full_shape(big_bank):
         assert np.array_equal(dev, rec), e
 
 
+# ---- 8-dim VQ experts -------------------------------------------------------------------
+def vq_host_records(seed, experts, H, I):
+    recs = {}
+    for e in experts:
+        idx, gains = synth.vq_expert_parts(seed, int(e), H, I)
+        recs[int(e)] = oracle.vq_pack_record(H, I, [a.numpy() for a in idx], gains)
+    return recs
+
+
+@pytest.fixture(scope="module")
+def vq_tiny():
+    say("building the tiny VQ bank")
+    return W.build_vq_bank(31, 256, 128, 16)
+
+
+@pytest.fixture(scope="module")
+def vq_big():
+    say("building the 256-record VQ bank (1.89 GB)")
+    return W.build_vq_bank(32, 5120, 2560, 256)
+
+
+def test_vq_pack_and_dequant_bit_exact(vq_tiny, vq_big):
+    for (bank, base, cb), H, I, seed, experts in [(vq_tiny, 256, 128, 31, range(16)), (vq_big, 5120, 2560, 32, [0, 201])]:
+        recs = vq_host_records(seed, experts, H, I)
+        cbh = cb.cpu().numpy()
+        for e in experts:
+            assert np.array_equal(base[e * bank.stride:(e + 1) * bank.stride].cpu().numpy(), recs[e]), e
+            for p in range(3):
+                out, inn = oracle.proj_shape(H, I, p)
+                d = torch.empty((out, inn), dtype=torch.float32, device=DEV)
+                wq.moe_vq_dequant(bank, e, p, d)
+                torch.cuda.synchronize()
+                ref = oracle.vq_dequant_projection(recs[e], cbh, H, I, p)
+                assert np.array_equal(d.cpu().numpy().view(np.uint32), ref.view(np.uint32)), (e, p)
+
+
+def gpu_vq_forward(bank, x_bits, idx, w, k, residual=None):
+    T, H = x_bits.shape
+    ws = wq.workspace(wq.moe_vq_workspace_bytes(T, k, bank.H, bank.I))
+    xd = bf16_tensor(x_bits)
+    idd = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).to(DEV)
+    wd = torch.from_numpy(np.ascontiguousarray(w, np.float32)).to(DEV)
+    rd = None if residual is None else bf16_tensor(residual)
+    yf = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    yb = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    wq.moe_vq_forward(bank, xd, T, idd, wd, k, rd, yf, wq.MOE_F32_OUT, ws)
+    wq.moe_vq_forward(bank, xd, T, idd, wd, k, rd, yb, 0, ws)
+    torch.cuda.synchronize()
+    return yf.cpu().numpy(), to_np_bits(yb)
+
+
+def test_vq_forward_tiny(vq_tiny):
+    bank, base, cb = vq_tiny
+    H, I, E, k, T = 256, 128, 16, 2, 5
+    x = synth.activations(33, T, H)
+    lg = np.random.default_rng(33).normal(size=(T, E)).astype(np.float32)
+    idx, w = oracle.route_topk(lg, k)
+    res = synth.activations(34, T, H)
+    recs = vq_host_records(31, np.unique(idx), H, I)
+    for residual in (None, res):
+        yf, yb = gpu_vq_forward(bank, x, idx, w, k, residual)
+        rf, _ = oracle.vq_moe_forward(recs, cb.cpu().numpy(), E, H, I, x, idx, w, residual=residual)
+        check_f32(yf, rf, "vq tiny")
+        check_bf16_of(yb, yf, "vq tiny bf16")
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_vq_forward_full_shape(vq_big, T):
+    # T = 1: single-token decode; T = 3: a short verify pass of a few tokens
+    bank, base, cb = vq_big
+    H, I, E, k = 5120, 2560, 256, 8
+    x = synth.activations(35 + T, T, H)
+    _, Wr, _ = W.inputs("decode")
+    lg = oracle.router_logits(x, Wr)
+    idx, w = oracle.route_topk(lg, k)
+    recs = vq_host_records(32, np.unique(idx), H, I)
+    yf, yb = gpu_vq_forward(bank, x, idx, w, k)
+    rf, _ = oracle.vq_moe_forward(recs, cb.cpu().numpy(), E, H, I, x, idx, w)
+    check_f32(yf, rf, f"vq T={T}")
+    check_bf16_of(yb, yf, f"vq T={T} bf16")
+
+
 # ---- pack side: record digests and the manifest --------------------------------------
 def device_digests(bank, e0, n):
     d = torch.empty((n, 32), dtype=torch.uint8, device=DEV)

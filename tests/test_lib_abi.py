@@ -192,3 +192,32 @@ def test_cache_validation_before_any_hip_call():
     assert L.moe_cache_prepare(None, None, 0, None, None) == wq.MOE_EINVAL
     assert L.moe_cache_bank(None, C.byref(host)) == wq.MOE_EINVAL
     assert L.moe_cache_stats(None, None, None, None) == wq.MOE_EINVAL
+
+
+def test_vq_sizes_and_validation():
+    L = wq.lib()
+    for H, I in [(5120, 2560), (256, 128), (128, 64)]:
+        _, nbytes, stride = oracle.vq_layout(H, I)
+        assert wq.moe_vq_record_bytes(H, I) == nbytes and wq.moe_vq_record_stride(H, I) == stride
+    assert wq.moe_vq_record_bytes(5120, 2576) == 0
+    b = wq.moe_vq_bank()
+    fake, cb = C.c_void_p(1 << 26), C.c_void_p(1 << 22)
+    assert L.moe_vq_bank_init(C.byref(b), fake, cb, 5120, 2560, 256) == wq.MOE_OK
+    off, nbytes, _ = oracle.vq_layout(5120, 2560)
+    assert list(b.part_off) == off and b.record_bytes == nbytes
+    assert L.moe_vq_bank_init(C.byref(b), fake, None, 5120, 2560, 256) == wq.MOE_EINVAL
+    assert L.moe_vq_bank_init(C.byref(b), fake, C.c_void_p((1 << 22) + 8), 5120, 2560, 256) == wq.MOE_EALIGN
+    assert L.moe_vq_bank_init(C.byref(b), fake, cb, 5120, 2560 + 16, 256) == wq.MOE_ESHAPE
+    assert L.moe_vq_bank_init(C.byref(b), fake, cb, 5120, 2560, 256) == wq.MOE_OK
+    ws = wq.moe_vq_workspace_bytes(1, 8, 5120, 2560)
+    assert ws >= 8 * 2560 * 2 and wq.moe_vq_workspace_bytes(1, 17, 5120, 2560) == 0
+    f = lambda **kw: L.moe_vq_forward(C.byref(b), kw.get("x", fake), kw.get("T", 1), fake, fake, kw.get("k", 8),
+                                      None, fake, 0, fake, kw.get("wsb", ws), None)
+    assert f(k=0) == wq.MOE_ESHAPE and f(k=17) == wq.MOE_ESHAPE
+    assert f(T=-1) == wq.MOE_ESHAPE
+    assert f(x=None) == wq.MOE_EINVAL
+    assert f(x=C.c_void_p((1 << 26) + 8)) == wq.MOE_EALIGN
+    assert f(wsb=ws - 1) == wq.MOE_EWORKSPACE
+    assert f(T=0) == wq.MOE_OK
+    assert L.moe_vq_dequant(C.byref(b), 256, 0, fake, None) == wq.MOE_EINVAL
+    assert L.moe_vq_dequant(C.byref(b), 0, 3, fake, None) == wq.MOE_EINVAL

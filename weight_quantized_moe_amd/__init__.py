@@ -25,7 +25,8 @@ EXPORTS = [
     "moe_nvfp4_workspace_bytes", "moe_nvfp4_forward", "moe_nvfp4_layer", "affine8_g64_linear", "moe_rmsnorm",
     "moe_nvfp4_dequant", "moe_profile_enable", "moe_profile_read", "moe_nvfp4_global_from_ws2",
     "moe_nvfp4_record_sha256", "moe_cache_create", "moe_cache_destroy", "moe_cache_prepare", "moe_cache_bank",
-    "moe_cache_stats",
+    "moe_cache_stats", "moe_vq_record_bytes", "moe_vq_record_stride", "moe_vq_bank_init", "moe_vq_pack_bank",
+    "moe_vq_dequant", "moe_vq_workspace_bytes", "moe_vq_forward",
 ]
 
 
@@ -33,6 +34,12 @@ class MoeError(RuntimeError):
     def __init__(self, code, msg):
         super().__init__(f"[{code}] {msg}")
         self.code = code
+
+
+class moe_vq_bank(C.Structure):
+    _fields_ = [("H", C.c_int32), ("I", C.c_int32), ("E", C.c_int32), ("reserved", C.c_int32),
+                ("record_bytes", C.c_uint64), ("stride", C.c_uint64),
+                ("part_off", C.c_uint64 * 6), ("base", C.c_void_p), ("codebook", C.c_void_p)]
 
 
 class moe_nvfp4_bank(C.Structure):
@@ -97,6 +104,21 @@ def lib():
         L.moe_cache_bank.argtypes = [vp, bankp]
         L.moe_cache_stats.restype = i32
         L.moe_cache_stats.argtypes = [vp, C.POINTER(C.c_int64), C.POINTER(C.c_int64), C.POINTER(C.c_int64)]
+        vqp = C.POINTER(moe_vq_bank)
+        L.moe_vq_record_bytes.restype = sz
+        L.moe_vq_record_bytes.argtypes = [i32, i32]
+        L.moe_vq_record_stride.restype = sz
+        L.moe_vq_record_stride.argtypes = [i32, i32]
+        L.moe_vq_bank_init.restype = i32
+        L.moe_vq_bank_init.argtypes = [vqp, vp, vp, i32, i32, i32]
+        L.moe_vq_pack_bank.restype = i32
+        L.moe_vq_pack_bank.argtypes = [vqp, C.POINTER(vp), C.POINTER(vp), vp]
+        L.moe_vq_dequant.restype = i32
+        L.moe_vq_dequant.argtypes = [vqp, i32, i32, vp, vp]
+        L.moe_vq_workspace_bytes.restype = sz
+        L.moe_vq_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        L.moe_vq_forward.restype = i32
+        L.moe_vq_forward.argtypes = [vqp, vp, i32, vp, vp, i32, vp, vp, C.c_uint, vp, sz, vp]
         L.moe_profile_enable.restype = i32
         L.moe_profile_enable.argtypes = [i32]
         L.moe_profile_read.restype = i32
@@ -256,6 +278,53 @@ def moe_cache_stats(handle):
     h, m, n = C.c_int64(), C.c_int64(), C.c_int64()
     _check(lib().moe_cache_stats(handle, C.byref(h), C.byref(m), C.byref(n)))
     return h.value, m.value, n.value
+
+
+# ---- 8-dim VQ experts ---------------------------------------------------------------
+def moe_vq_record_bytes(H, I):
+    return lib().moe_vq_record_bytes(H, I)
+
+
+def moe_vq_record_stride(H, I):
+    return lib().moe_vq_record_stride(H, I)
+
+
+def moe_vq_bank_init(base, codebook, H, I, E):
+    b = moe_vq_bank()
+    _check(lib().moe_vq_bank_init(C.byref(b), _ptr(base), _ptr(codebook), H, I, E))
+    b._keep = (base, codebook)
+    return b
+
+
+def alloc_vq_bank(codebook, H, I, E, device="cuda"):
+    """A 4 KiB-aligned bank of E VQ records on `device` over the device codebook
+    (uint8 [4096][8]) and its descriptor."""
+    stride = moe_vq_record_stride(H, I)
+    raw = torch.empty(E * stride + 4096, dtype=torch.uint8, device=device)
+    off = (-raw.data_ptr()) % 4096
+    base = raw[off:off + E * stride]
+    b = moe_vq_bank_init(base, codebook, H, I, E)
+    b._raw = raw
+    return b, base
+
+
+def moe_vq_pack_bank(bank, idx, gains, stream=None):
+    ip = (C.c_void_p * 3)(*[t.data_ptr() for t in idx])
+    gp = (C.c_void_p * 3)(*[t.data_ptr() for t in gains])
+    _check(lib().moe_vq_pack_bank(C.byref(bank), ip, gp, _stream(stream)))
+
+
+def moe_vq_dequant(bank, expert, proj, out_f32, stream=None):
+    _check(lib().moe_vq_dequant(C.byref(bank), expert, proj, _ptr(out_f32), _stream(stream)))
+
+
+def moe_vq_workspace_bytes(T, k, H, I):
+    return lib().moe_vq_workspace_bytes(T, k, H, I)
+
+
+def moe_vq_forward(bank, x, T, idx, w, k, residual, y, flags, ws, stream=None):
+    _check(lib().moe_vq_forward(C.byref(bank), _ptr(x), T, _ptr(idx), _ptr(w), k, _ptr(residual), _ptr(y), flags,
+                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def moe_profile_enable(on):

@@ -280,6 +280,146 @@ MOE_API int moe_cache_stats(const moe_expert_cache* c, int64_t* hits, int64_t* m
   return MOE_OK;
 }
 
+// ---- 8-dim VQ experts --------------------------------------------------------------
+static bool vq_shape_ok(int H, int I) { return H > 0 && I > 0 && H % 64 == 0 && I % 64 == 0; }
+
+MOE_API size_t moe_vq_record_bytes(int H, int I) {
+  if (!vq_shape_ok(H, I)) return 0;
+  size_t off = 0;
+  for (int p = 0; p < 3; p++) {
+    const size_t out = p == 2 ? H : I, in = p == 2 ? I : H;
+    off = (off + out * in * 3 / 16 + 15) / 16 * 16;
+    off = (off + out * 2 + 15) / 16 * 16;
+  }
+  return off;
+}
+
+MOE_API size_t moe_vq_record_stride(int H, int I) { return (moe_vq_record_bytes(H, I) + 4095) / 4096 * 4096; }
+
+MOE_API int moe_vq_bank_init(moe_vq_bank* b, void* base, const void* codebook, int H, int I, int E) {
+  if (!b || !base || !codebook) return fail(MOE_EINVAL, "vq_bank_init: null pointer");
+  if (!vq_shape_ok(H, I)) return fail(MOE_ESHAPE, "vq_bank_init: H=%d I=%d must be positive multiples of 64", H, I);
+  if (E < 1 || E > 1024) return fail(MOE_ESHAPE, "vq_bank_init: E=%d outside [1, 1024]", E);
+  if (!aligned(base, 4096)) return fail(MOE_EALIGN, "vq_bank_init: base not 4096-byte aligned");
+  if (!aligned(codebook, 16)) return fail(MOE_EALIGN, "vq_bank_init: codebook not 16-byte aligned");
+  b->H = H;
+  b->I = I;
+  b->E = E;
+  b->reserved = 0;
+  size_t off = 0;
+  for (int p = 0; p < 3; p++) {
+    const size_t out = p == 2 ? H : I, in = p == 2 ? I : H;
+    b->part_off[2 * p] = off;
+    off = (off + out * in * 3 / 16 + 15) / 16 * 16;
+    b->part_off[2 * p + 1] = off;
+    off = (off + out * 2 + 15) / 16 * 16;
+  }
+  b->record_bytes = off;
+  b->stride = moe_vq_record_stride(H, I);
+  b->base = base;
+  b->codebook = codebook;
+  return MOE_OK;
+}
+
+static int vq_args(const moe_vq_bank* b, VqArgs* a, const char* who) {
+  if (!b || !b->base || !b->codebook) return fail(MOE_EINVAL, "%s: null bank", who);
+  if (!vq_shape_ok(b->H, b->I) || b->E < 1 || b->E > 1024)
+    return fail(MOE_ESHAPE, "%s: bank shape H=%d I=%d E=%d", who, b->H, b->I, b->E);
+  if (b->record_bytes != moe_vq_record_bytes(b->H, b->I) || b->stride < b->record_bytes || b->stride % 256)
+    return fail(MOE_EINVAL, "%s: record size/stride inconsistent with H, I", who);
+  if (!aligned(b->base, 256) || !aligned(b->codebook, 16)) return fail(MOE_EALIGN, "%s: base/codebook alignment", who);
+  for (int p = 0; p < 3; p++) {
+    const uint64_t out = p == 2 ? b->H : b->I, in = p == 2 ? b->I : b->H;
+    if (b->part_off[2 * p] % 16 || b->part_off[2 * p + 1] % 16)
+      return fail(MOE_EALIGN, "%s: part offsets of projection %d not 16-byte aligned", who, p);
+    if (b->part_off[2 * p] + out * in * 3 / 16 > b->record_bytes || b->part_off[2 * p + 1] + out * 2 > b->record_bytes)
+      return fail(MOE_EINVAL, "%s: part of projection %d outside the record", who, p);
+  }
+  *a = VqArgs{};
+  a->bank = static_cast<const uint8_t*>(b->base);
+  a->stride = b->stride;
+  for (int p = 0; p < 3; p++) {
+    a->idx_off[p] = b->part_off[2 * p];
+    a->gain_off[p] = b->part_off[2 * p + 1];
+  }
+  a->codebook = static_cast<const uint8_t*>(b->codebook);
+  a->H = b->H;
+  a->I = b->I;
+  a->E = b->E;
+  return MOE_OK;
+}
+
+MOE_API int moe_vq_pack_bank(const moe_vq_bank* b, const uint8_t* const idx[3], const uint16_t* const gain[3],
+                             void* stream) {
+  VqArgs a;
+  int rc = vq_args(b, &a, "vq_pack");
+  if (rc) return rc;
+  if (!idx || !gain) return fail(MOE_EINVAL, "vq_pack: null part arrays");
+  for (int p = 0; p < 3; p++)
+    if (!idx[p] || !gain[p]) return fail(MOE_EINVAL, "vq_pack: null part of projection %d", p);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* base = static_cast<uint8_t*>(b->base);
+  for (int e = 0; e < b->E; e++) {
+    uint8_t* rec = base + (size_t)e * b->stride;
+    for (int p = 0; p < 3; p++) {
+      const size_t out = p == 2 ? b->H : b->I, in = p == 2 ? b->I : b->H;
+      const size_t nb = out * in * 3 / 16;
+      rc = hip_check(hipMemcpyAsync(rec + b->part_off[2 * p], idx[p] + e * nb, nb, hipMemcpyDefault, s), "vq_pack idx");
+      if (rc) return rc;
+      rc = hip_check(hipMemcpyAsync(rec + b->part_off[2 * p + 1], gain[p] + e * out, out * 2, hipMemcpyDefault, s),
+                     "vq_pack gains");
+      if (rc) return rc;
+    }
+  }
+  return hip_check(launch_zero_tails(base, b->stride, b->record_bytes, b->E, s), "vq_pack zero pad");
+}
+
+MOE_API int moe_vq_dequant(const moe_vq_bank* b, int expert, int proj, float* out_f32, void* stream) {
+  VqArgs a;
+  int rc = vq_args(b, &a, "vq_dequant");
+  if (rc) return rc;
+  if (expert < 0 || expert >= b->E || proj < 0 || proj > 2 || !out_f32)
+    return fail(MOE_EINVAL, "vq_dequant: expert/proj out of range or null output");
+  return hip_check(launch_vq_dequant(a, expert, proj, out_f32, static_cast<hipStream_t>(stream)), "vq_dequant");
+}
+
+MOE_API size_t moe_vq_workspace_bytes(int T, int k, int H, int I) {
+  if (T < 0 || k < 1 || k > kFlatDecodeMaxK || !vq_shape_ok(H, I)) return 0;
+  return up256((size_t)T * k * I * 2) + 256;
+}
+
+MOE_API int moe_vq_forward(const moe_vq_bank* b, const uint16_t* x, int T, const int32_t* idx, const float* w, int k,
+                           const uint16_t* residual, void* y, unsigned flags, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  VqArgs a;
+  int rc = vq_args(b, &a, "vq_forward");
+  if (rc) return rc;
+  if (T < 0) return fail(MOE_ESHAPE, "vq_forward: T=%d < 0", T);
+  if (k < 1 || k > kFlatDecodeMaxK || k > b->E)
+    return fail(MOE_ESHAPE, "vq_forward: k=%d outside [1, min(E, %d)]", k, kFlatDecodeMaxK);
+  if (32768 + (size_t)k * b->I * 2 > 160 * 1024 - 2048)
+    return fail(MOE_ESHAPE, "vq_forward: k*I*2 = %zu bytes of mids do not fit LDS beside the codebook",
+                (size_t)k * b->I * 2);
+  if (T == 0) return MOE_OK;
+  if (!x || !idx || !w || !y || !workspace) return fail(MOE_EINVAL, "vq_forward: null pointer");
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(idx, 4) || !aligned(w, 4) || (residual && !aligned(residual, 8)) ||
+      !aligned(workspace, 256))
+    return fail(MOE_EALIGN, "vq_forward: x, y 16 B; idx, w 4 B; residual 8 B; workspace 256 B");
+  if (workspace_bytes < moe_vq_workspace_bytes(T, k, b->H, b->I))
+    return fail(MOE_EWORKSPACE, "vq_forward: workspace %zu < %zu bytes", workspace_bytes,
+                moe_vq_workspace_bytes(T, k, b->H, b->I));
+  a.k = k;
+  a.T = T;
+  a.idx = idx;
+  a.w = w;
+  a.x = x;
+  a.residual = residual;
+  a.mid = static_cast<uint16_t*>(workspace);
+  a.y = y;
+  a.f32_out = (flags & MOE_F32_OUT) ? 1 : 0;
+  return hip_check(launch_vq_forward(a, static_cast<hipStream_t>(stream)), "vq_forward");
+}
+
 // ---- S1 + S2 routing -----------------------------------------------------------
 MOE_API int moe_route_topk(const uint16_t* x, const float* w_router, float* logits, int T, int H,
                            int E, int k, int32_t* idx, float* w, void* stream) {

@@ -47,6 +47,24 @@ hipError_t launch_sort(const int32_t* idx, int P, int E, RouteTables rt, int mti
 // (returns whether it is exact); SHA-256 of records e0 .. e0 + n - 1 over
 // their first nbytes bytes, digests [n][32] (device, 4-byte aligned)
 bool global_from_ws2_one(float ws2, float* g);
+// 8-dim VQ records (vq.hip): byte offsets of each projection's index rows and
+// gains inside a record; the codebook is 4096 x 8 E4M3 bytes
+struct VqArgs {
+  const uint8_t* bank;
+  uint64_t stride;
+  uint64_t idx_off[3], gain_off[3];
+  const uint8_t* codebook;
+  int H, I, E, k, T;
+  const int32_t* idx;       // [T][k]
+  const float* w;           // [T][k]
+  const uint16_t* x;        // [T][H]
+  const uint16_t* residual; // [T][H] or null
+  uint16_t* mid;            // [T*k][I] scratch
+  void* y;                  // [T][H] bf16 or f32
+  int f32_out;
+};
+hipError_t launch_vq_forward(const VqArgs& a, hipStream_t s);
+hipError_t launch_vq_dequant(const VqArgs& a, int expert, int proj, float* out, hipStream_t s);
 // the expert cache's host logic and copies (arguments checked by the caller;
 // prepare's ids are in [0, E) with at most nslots distinct)
 int cache_create(const moe_nvfp4_bank* host, void* slot_base, int nslots, moe_expert_cache** out);
