@@ -37,8 +37,12 @@ indices, a 32 KiB E4M3 codebook): moe_route_topk (router + top-k) then
 moe_vq_forward, as GB/s of algorithmic bytes (8 VQ records + the f32 router +
 the codebook + x and y).
 
+Verify leg (--only verify, not part of the default run): the one-call layer
+(moe_nvfp4_layer: router, top-k, experts, combine) on T = 1..4 tokens, the
+draft-verify shape; GB/s over the distinct selected records + W_r + x, y.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--prefill-steps P]
-       [--only decode|prefill|cache|vq] [--no-cpu-baseline] [--two-call]
+       [--only decode|prefill|cache|vq|verify] [--no-cpu-baseline] [--two-call]
 Profiling helpers: --copy-calibration (device copies of 1 GiB, for the
 counter scale factor); --summarize-pmc DIR (per-kernel mean counter values
 per dispatch from a rocprofv3 --pmc output directory; no GPU needed).
@@ -267,6 +271,40 @@ def prefill_leg(bank, P):
             "kernels_us": {n_: round(v[0] * 1e3, 2) for n_, v in pk.items()}}
 
 
+def verify_leg(bank, K, Wm):
+    c = W.CONFIGS["decode"]
+    H, I, E, k = c["H"], c["I"], c["E"], c["k"]
+    _, Wr, _ = W.inputs("decode")
+    Wr = torch.from_numpy(Wr).cuda()
+    rec = wq.moe_nvfp4_record_bytes(H, I)
+    rows = []
+    for T in (1, 2, 3, 4):
+        xs = bf16_dev(np.stack([synth.activations(100 + v, T, H) for v in range(ROTATE)]))
+        logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+        idx = torch.empty((ROTATE, T, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((ROTATE, T, k), dtype=torch.float32, device="cuda")
+        y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+        ws = wq.workspace(wq.moe_nvfp4_workspace_bytes(T, k, H, I, E))
+        state = {"i": 0}
+
+        def step():
+            r = state["i"] % ROTATE
+            state["i"] += 1
+            wq.moe_nvfp4_layer(bank, xs[r], Wr, T, k, None, logits, idx[r], w[r], y, 0, ws)
+
+        ms_total, _ = timed(step, K, Wm)
+        idx_h = idx.cpu().numpy()
+        rs = [(Wm + i) % ROTATE for i in range(K)]
+        nb = np.array([len(np.unique(idx_h[r])) * rec + H * E * 4 + 2 * T * H * 2 for r in rs], dtype=np.float64)
+        gbs = nb.sum() / (ms_total * 1e-3) / 1e9
+        row = {"T": T, "us_per_step": round(ms_total / K * 1e3, 2), "GBps": round(gbs, 1),
+               "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4), "distinct_experts": round(float(nb.mean() - H * E * 4) / rec, 2)}
+        rows.append(row)
+        log(f"verify T={T}: {ms_total / K * 1e3:.1f} us/step, {gbs:.1f} GB/s")
+    return {"workload": "one-call layer on T = 1..4 tokens (router f32, top-8 of 256, H=5120, I=2560), "
+                        "64 rotating activations", "rows": rows}
+
+
 def vq_leg(K, Wm):
     c = W.CONFIGS["decode"]
     H, I, E, k = c["H"], c["I"], c["E"], c["k"]
@@ -407,7 +445,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "cache", "vq"])
+    ap.add_argument("--only", choices=["decode", "prefill", "cache", "vq", "verify"])
     ap.add_argument("--two-call", action="store_true",
                     help="decode step as moe_route_topk + moe_nvfp4_forward instead of moe_nvfp4_layer")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -441,6 +479,9 @@ def main():
         return
     if args.only == "cache":
         print(json.dumps({"expert_cache": cache_leg(bank, base)}), flush=True)
+        return
+    if args.only == "verify":
+        print(json.dumps({"verify": verify_leg(bank, args.steps, args.warmup)}), flush=True)
         return
 
     # ---- decode leg

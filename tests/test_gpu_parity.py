@@ -587,6 +587,26 @@ def test_forward_decode_full_shape(big_bank):
             check_bf16_of(yb, yf, "decode bf16")
 
 
+@pytest.mark.parametrize("T", [2, 4])
+def test_forward_verify_shape_full(big_bank, T):
+    # a draft-verify pass of a few tokens (the multi-token expert-streaming
+    # path, routed inside its blocks), with a residual, against the oracle;
+    # and the one-call layer against route + forward
+    bank, _ = big_bank
+    c = W.CONFIGS["decode"]
+    x = synth.activations(40 + T, T, c["H"])
+    res = synth.activations(50 + T, T, c["H"])
+    _, Wr, _ = W.inputs("decode")
+    _, idx, w = oracle_routing("decode", x, Wr, None, c["k"])
+    say(f"verify T={T}: {len(np.unique(idx))} distinct experts")
+    recs = host_records(c["bank_seed"], np.unique(idx), c["H"], c["I"])
+    ref_f, _ = oracle.moe_forward(recs, c["E"], c["H"], c["I"], x, idx, w, residual=res)
+    yf, yb = gpu_forward(bank, x, idx, w, c["k"], 0, res)
+    check_f32(yf, ref_f, f"verify T={T}")
+    check_bf16_of(yb, yf, f"verify T={T} bf16")
+    check_layer_call(bank, f"verify T={T}", x, Wr, c["k"], residual=res)
+
+
 def gpu_layer(bank, x_bits, Wr, k, flags=0, residual=None, ws=None):
     """moe_nvfp4_layer: router, top-k and layer in one call. Returns logits,
     idx, w, y f32 and y bf16 (two calls, the second with the f32 flag off) and

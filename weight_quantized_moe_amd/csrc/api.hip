@@ -557,9 +557,11 @@ static int layer_checks(const char* who, const BankView& v, const uint16_t* x, i
   return MOE_OK;
 }
 
-// one token and at most kFlatDecodeMaxK pairs whose mids fit in 64 KiB of LDS
+// up to kFlatDecodeMaxT tokens of at most kFlatDecodeMaxK pairs each, whose
+// mids fit in 64 KiB of LDS
 static bool flat_path(const BankView& v, int T, int k, unsigned flags) {
-  return T == 1 && !(flags & MOE_FORCE_PREFILL) && k <= kFlatDecodeMaxK && (size_t)k * v.I * 2 <= 65536;
+  return T >= 1 && T <= kFlatDecodeMaxT && !(flags & MOE_FORCE_PREFILL) && k <= kFlatDecodeMaxK &&
+         (size_t)k * v.I * 2 <= 65536 && v.I % 16 == 0;
 }
 
 static int forward_run(const BankView& v, const uint16_t* x, int T, const int32_t* idx, const float* w, int k,
@@ -582,7 +584,7 @@ static int forward_run(const BankView& v, const uint16_t* x, int T, const int32_
   if (flags & MOE_FORCE_PREFILL) prefill = true;
   const bool f32_out = (flags & MOE_F32_OUT) != 0;
   if (!prefill && flat_path(v, T, k, flags))
-    return hip_check(launch_flat_decode(v, x, idx, w, k, residual, mid, y, f32_out, s), "decode");
+    return hip_check(launch_flat_decode(v, x, T, idx, w, k, residual, mid, y, f32_out, s), "decode");
 
   if (prefill) {
     rc = hip_check(launch_sort(idx, P, v.E, rt, kPrefillMTile, L.max_tiles, s), "sort");
@@ -655,7 +657,7 @@ MOE_API int moe_nvfp4_layer(const moe_nvfp4_bank* b, const uint16_t* x, const fl
     return fail(MOE_EALIGN, "layer: w_router must be 16-byte aligned, logits/idx/w 4-byte");
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  if (flat_path(v, T, k, flags)) {
+  if (T == 1 && flat_path(v, T, k, flags)) {
     uint64_t* tags = reinterpret_cast<uint64_t*>(ws + L.tags);
     uint32_t* status = reinterpret_cast<uint32_t*>(ws + L.counts) + 2;
     uint16_t* mid = reinterpret_cast<uint16_t*>(ws + L.mid);

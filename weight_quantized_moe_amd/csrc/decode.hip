@@ -415,19 +415,36 @@ __device__ __forceinline__ void flat_gateup_items(const FlatArgs& a, const uint3
   }
 }
 
-__global__ __launch_bounds__(kDecThreads) void flat_gateup_kernel(FlatArgs a) {
+// A few tokens: the first bpt workgroups serve token 0, the next bpt token 1,
+// ... (bpt = k * I/16 with one item per wave, so a workgroup's items belong
+// to one token); each stages its token's x.
+__global__ __launch_bounds__(kDecThreads) void flat_gateup_kernel(FlatArgs a, int bpt) {
   extern __shared__ __attribute__((aligned(16))) uint32_t xs[];  // [H/2]
   __shared__ int s_idx[kFlatDecodeMaxK];
+  const int t = blockIdx.x / bpt;
+  FlatArgs b = a;
+  b.x = a.x + (size_t)t * a.H;
+  b.idx = a.idx + (size_t)t * a.k;
+  b.mid = a.mid + (size_t)t * a.k * a.I;
   if (threadIdx.x < a.k) {
-    const int e = a.idx[threadIdx.x];
+    const int e = b.idx[threadIdx.x];
     s_idx[threadIdx.x] = (e >= 0 && e < a.E) ? e : -1;
   }
-  flat_stage_x(a, xs);
+  flat_stage_x(b, xs);
   __syncthreads();
-  flat_gateup_items(a, xs, s_idx, blockIdx.x, gridDim.x);
+  flat_gateup_items(b, xs, s_idx, blockIdx.x - t * bpt, bpt);
 }
 
-__global__ __launch_bounds__(64 * kFlatDecodeMaxK) void flat_down_kernel(FlatArgs a) {
+__global__ __launch_bounds__(64 * kFlatDecodeMaxK) void flat_down_kernel(FlatArgs a0) {
+  // token blockIdx.y of a few: its pairs, mids, residual and output row
+  const int tok = blockIdx.y;
+  FlatArgs a = a0;
+  a.idx = a0.idx + (size_t)tok * a0.k;
+  a.w = a0.w + (size_t)tok * a0.k;
+  a.mid = a0.mid + (size_t)tok * a0.k * a0.I;
+  if (a0.residual) a.residual = a0.residual + (size_t)tok * a0.H;
+  a.y = a0.f32_out ? static_cast<void*>(static_cast<float*>(a0.y) + (size_t)tok * a0.H)
+                   : static_cast<void*>(static_cast<uint16_t*>(a0.y) + (size_t)tok * a0.H);
   constexpr int G = 8, R = 64 / G, QB = 5;
   extern __shared__ __attribute__((aligned(16))) uint32_t ms[];  // [k][I/2]
   __shared__ int s_idx[kFlatDecodeMaxK];
@@ -692,22 +709,24 @@ static FlatArgs flat_args(const BankView& b, const uint16_t* x, const int32_t* i
   return a;
 }
 
-static hipError_t launch_flat_down(const FlatArgs& a, hipStream_t s) {
-  launch_kernel("decode_down", flat_down_kernel, dim3((a.H + 7) / 8), dim3(64 * a.k),
+static hipError_t launch_flat_down(const FlatArgs& a, int T, hipStream_t s) {
+  launch_kernel("decode_down", flat_down_kernel, dim3((a.H + 7) / 8, T), dim3(64 * a.k),
                 (uint32_t)(a.k * a.I * 2), s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_flat_decode(const BankView& b, const uint16_t* x, const int32_t* idx,
+hipError_t launch_flat_decode(const BankView& b, const uint16_t* x, int T, const int32_t* idx,
                               const float* w, int k, const uint16_t* residual, uint16_t* mid,
                               void* y, bool f32_out, hipStream_t s) {
   const FlatArgs a = flat_args(b, x, idx, w, k, residual, mid, y, f32_out);
   const int groups = (b.I + 3) / 4;
-  launch_kernel("decode_gateup", flat_gateup_kernel, dim3(flat_blocks(k * groups)), dim3(kDecThreads),
-                (uint32_t)(b.H * 2), s, a);
+  // one token may take the tuned block count; several take one item per wave
+  const int bpt = T == 1 ? flat_blocks(k * groups) : k * groups / kDecWaves;
+  launch_kernel("decode_gateup", flat_gateup_kernel, dim3(bpt * T), dim3(kDecThreads), (uint32_t)(b.H * 2), s, a,
+                bpt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_flat_down(a, s);
+  return launch_flat_down(a, T, s);
 }
 
 hipError_t launch_flat_layer(const BankView& b, const uint16_t* x, const float* wr, int k,
@@ -730,7 +749,7 @@ hipError_t launch_flat_layer(const BankView& b, const uint16_t* x, const float* 
   launch_kernel("decode_route_gateup", flat_route_gateup_kernel, grid, block, lds, s, a, r);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_flat_down(a, s);
+  return launch_flat_down(a, 1, s);
 }
 
 // ---- S7: weighted combine (the routing weight is already in `part`) -----------

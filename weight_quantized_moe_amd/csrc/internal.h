@@ -90,11 +90,14 @@ hipError_t launch_decode_gateup(const BankView& b, const uint16_t* x, const int3
 hipError_t launch_decode_down(const BankView& b, const uint16_t* mid, const float* w,
                               const int32_t* idx, int P, int k, const RouteTables* rt, int slots,
                               int max_m, float* part, hipStream_t s);
-// one token (T = 1, k <= kFlatDecodeMaxK, k * I * 2 <= 64 KiB of mids in
-// LDS): gate/up then down with the combine folded in; mid [k][I] is scratch,
-// y [H] the layer output
+// up to kFlatDecodeMaxT tokens (k <= kFlatDecodeMaxK, k * I * 2 <= 64 KiB of
+// mids in LDS, I % 16 == 0): gate/up then down with the combine folded in;
+// mid [T*k][I] is scratch, y [T][H] the layer output
 constexpr int kFlatDecodeMaxK = 16;
-hipError_t launch_flat_decode(const BankView& b, const uint16_t* x, const int32_t* idx,
+// tokens the one-item-per-wave decode kernels take (a draft-verify pass);
+// more tokens share experts enough for the routed GEMV to pay
+constexpr int kFlatDecodeMaxT = 4;
+hipError_t launch_flat_decode(const BankView& b, const uint16_t* x, int T, const int32_t* idx,
                               const float* w, int k, const uint16_t* residual, uint16_t* mid,
                               void* y, bool f32_out, hipStream_t s);
 // router + top-k + gate/up in one launch, then down (T = 1, the same limits
