@@ -41,8 +41,12 @@ Verify leg (--only verify, not part of the default run): the one-call layer
 (moe_nvfp4_layer: router, top-k, experts, combine) on T = 1..4 tokens, the
 draft-verify shape; GB/s over the distinct selected records + W_r + x, y.
 
+Residents leg (--only affine8, not part of the default run): the 5120 x 5120
+affine8_g64 resident linear at T = 256, 1,024 and 8,192 tokens (the MFMA GEMM
+path), as TFLOP/s of 2 T K N against 2.5 PFLOP/s.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--prefill-steps P]
-       [--only decode|prefill|cache|vq|verify] [--no-cpu-baseline] [--two-call]
+       [--only decode|prefill|cache|vq|verify|affine8] [--no-cpu-baseline] [--two-call]
 Profiling helpers: --copy-calibration (device copies of 1 GiB, for the
 counter scale factor); --summarize-pmc DIR (per-kernel mean counter values
 per dispatch from a rocprofv3 --pmc output directory; no GPU needed).
@@ -271,6 +275,33 @@ def prefill_leg(bank, P):
             "kernels_us": {n_: round(v[0] * 1e3, 2) for n_, v in pk.items()}}
 
 
+def affine8_leg(K=5120, N=5120, steps=20, warm=3):
+    w = synth.resident_weights(16, N, K)
+    # codes, scales and biases of a 5120 x 5120 resident: the seeded bf16
+    # weights through the library-independent q8 draw below (uniform codes,
+    # scale and bias from the weight rows' range) keep the run free of the oracle
+    wt = torch.from_numpy(w.view(np.int16)).cuda().view(torch.bfloat16).float().view(N, K // 64, 64)
+    lo, hi = wt.amin(dim=2), wt.amax(dim=2)
+    scale = ((hi - lo) / 255.0).to(torch.bfloat16)
+    bias = lo.to(torch.bfloat16)
+    codes = torch.randint(0, 256, (N, K), dtype=torch.uint8, device="cuda", generator=torch.Generator("cuda").manual_seed(3))
+    codes32 = codes.view(torch.int32).contiguous()
+    rows = []
+    for T in (256, 1024, 8192):
+        x = bf16_dev(synth.activations(19, T, K))
+        y = torch.empty((T, N), dtype=torch.int16, device="cuda")
+
+        def step():
+            wq.affine8_g64_linear(x, codes32, scale.view(torch.int16), bias.view(torch.int16), T, K, N, y)
+
+        ms_total, _ = timed(step, steps, warm)
+        tf = 2.0 * T * K * N / (ms_total / steps * 1e-3) / 1e12
+        rows.append({"T": T, "ms": round(ms_total / steps, 4), "TFLOPs": round(tf, 1),
+                     "frac_of_2.5PF": round(tf / BF16_PEAK_TFLOPS, 4)})
+        log(f"affine8 T={T}: {ms_total / steps:.3f} ms, {tf:.1f} TFLOP/s")
+    return {"workload": "affine8_g64 resident linear, K = N = 5120, bf16 activations", "rows": rows}
+
+
 def verify_leg(bank, K, Wm):
     c = W.CONFIGS["decode"]
     H, I, E, k = c["H"], c["I"], c["E"], c["k"]
@@ -445,7 +476,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "cache", "vq", "verify"])
+    ap.add_argument("--only", choices=["decode", "prefill", "cache", "vq", "verify", "affine8"])
     ap.add_argument("--two-call", action="store_true",
                     help="decode step as moe_route_topk + moe_nvfp4_forward instead of moe_nvfp4_layer")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -468,6 +499,9 @@ def main():
         return
     if args.only == "vq":
         print(json.dumps({"vq": vq_leg(args.steps, args.warmup)}), flush=True)
+        return
+    if args.only == "affine8":
+        print(json.dumps({"affine8": affine8_leg()}), flush=True)
         return
     c = W.CONFIGS["decode"]
     log(f"building the bank: {c['E']} records of {wq.moe_nvfp4_record_bytes(c['H'], c['I'])} B")

@@ -748,6 +748,37 @@ def test_affine8_and_rmsnorm():
     check_bf16(to_np_bits(y), oracle.bf16_to_f32(ref), "rmsnorm")
 
 
+@pytest.mark.parametrize("T,K,N", [(300, 256, 200), (64, 128, 64), (129, 512, 130)])
+def test_affine8_gemm_ragged(T, K, N):
+    # from 64 tokens the linear runs as the MFMA GEMM: ragged token and row
+    # tiles, K of 2 to 8 groups
+    v = synth.resident_weights(14, N, K)
+    codes, scales, biases = oracle.q8_quantize(v)
+    x = synth.activations(15, T, K)
+    ref_f, _ = oracle.affine8_linear(x, codes, scales, biases)
+    y = torch.full((T, N), 0x7FC0, dtype=torch.int16, device=DEV)
+    wq.affine8_g64_linear(bf16_tensor(x), torch.from_numpy(codes.view(np.int32)).to(DEV),
+                          bf16_tensor(scales), bf16_tensor(biases), T, K, N, y)
+    torch.cuda.synchronize()
+    check_bf16(to_np_bits(y), ref_f, f"affine8 gemm {T}x{K}x{N}")
+
+
+def test_affine8_gemm_full_shape_sampled():
+    # a 5120 x 5120 resident over 1,024 tokens (8 token tiles x 40 row tiles);
+    # the oracle on 24 sampled tokens, every output row
+    T, K, N = 1024, 5120, 5120
+    v = synth.resident_weights(16, N, K)
+    codes, scales, biases = oracle.q8_quantize(v)
+    x = synth.activations(17, T, K)
+    y = torch.empty((T, N), dtype=torch.int16, device=DEV)
+    wq.affine8_g64_linear(bf16_tensor(x), torch.from_numpy(codes.view(np.int32)).to(DEV),
+                          bf16_tensor(scales), bf16_tensor(biases), T, K, N, y)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 511, 1023], np.random.default_rng(18).integers(0, T, 18)]))
+    ref_f, _ = oracle.affine8_linear(x[rows], codes, scales, biases)
+    check_bf16(to_np_bits(y)[rows], ref_f, "affine8 gemm 1024x5120x5120 sampled")
+
+
 # ---- the stacked decode workload: 12 chained layers ------------------------------------
 def check_state(got_bits, ref_bits, what):
     """A bf16 layer state h_l of the chain. The single-layer bound (relative L2

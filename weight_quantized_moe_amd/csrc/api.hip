@@ -673,6 +673,18 @@ MOE_API int moe_nvfp4_layer(const moe_nvfp4_bank* b, const uint16_t* x, const fl
 }
 
 // ---- S8 affine8_g64 --------------------------------------------------------------
+// tokens from which the linear runs as an MFMA GEMM instead of the
+// weight-streaming kernel
+static int affine8_gemm_min_t() {
+  static int v = -1;
+  if (v < 0) {
+    const char* s = std::getenv("MOE_AFFINE8_GEMM_MIN_T");
+    v = (s && *s) ? std::atoi(s) : 64;
+    if (v < 1) v = 1;
+  }
+  return v;
+}
+
 MOE_API int affine8_g64_linear(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
                                const uint16_t* biases, int T, int K, int N, uint16_t* y,
                                void* stream) {
@@ -681,8 +693,10 @@ MOE_API int affine8_g64_linear(const uint16_t* x, const uint32_t* codes, const u
   if (!x || !codes || !scales || !biases || !y) return fail(MOE_EINVAL, "affine8: null pointer");
   if (!aligned(codes, 16) || !aligned(x, 4) || !aligned(y, 2) || !aligned(scales, 2) || !aligned(biases, 2))
     return fail(MOE_EALIGN, "affine8: codes must be 16-byte aligned, x 4-byte aligned");
-  return hip_check(launch_affine8(x, codes, scales, biases, T, K, N, y, static_cast<hipStream_t>(stream)),
-                   "affine8");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T >= affine8_gemm_min_t() && aligned(x, 16))
+    return hip_check(launch_affine8_gemm(x, codes, scales, biases, T, K, N, y, s), "affine8 gemm");
+  return hip_check(launch_affine8(x, codes, scales, biases, T, K, N, y, s), "affine8");
 }
 
 // ---- S9 rmsnorm --------------------------------------------------------------------

@@ -129,6 +129,9 @@ hipError_t launch_dequant(const BankView& b, int expert, int proj, float* out_f3
 hipError_t launch_rmsnorm(const uint16_t* x, int T, int H, float eps, uint16_t* y, hipStream_t s);
 hipError_t launch_affine8(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
                           const uint16_t* biases, int T, int K, int N, uint16_t* y, hipStream_t s);
+// the same linear on bf16 MFMA for many tokens (x 16-byte aligned)
+hipError_t launch_affine8_gemm(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
+                               const uint16_t* biases, int T, int K, int N, uint16_t* y, hipStream_t s);
 
 // kernel timing (api.hip)
 // Kernel timing (moe_profile_enable). When on, prof_events hands out a pair
