@@ -45,8 +45,15 @@ Residents leg (--only affine8, not part of the default run): the 5120 x 5120
 affine8_g64 resident linear at T = 256, 1,024 and 8,192 tokens (the MFMA GEMM
 path), as TFLOP/s of 2 T K N against 2.5 PFLOP/s.
 
+Batched leg (--only batched): T = 32 tokens on Zipf(1.1)-skewed logits
+(given), moe_route_topk + moe_nvfp4_forward, GB/s over the distinct selected
+records + x, y. Stacked leg (--only stacked): 12 layers of the decode shape,
+each RMSNorm + a 5120 x 5120 affine8_g64 resident + the one-call layer with
+the residual, T = 8; GB/s over the residents, routers and distinct records of
+all 12 layers (about 15.6 GB per step).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--prefill-steps P]
-       [--only decode|prefill|cache|vq|verify|affine8] [--no-cpu-baseline] [--two-call]
+       [--only decode|prefill|cache|vq|verify|affine8|batched|stacked] [--no-cpu-baseline] [--two-call]
 Profiling helpers: --copy-calibration (device copies of 1 GiB, for the
 counter scale factor); --summarize-pmc DIR (per-kernel mean counter values
 per dispatch from a rocprofv3 --pmc output directory; no GPU needed).
@@ -275,6 +282,93 @@ def prefill_leg(bank, P):
             "kernels_us": {n_: round(v[0] * 1e3, 2) for n_, v in pk.items()}}
 
 
+def resident_parts(seed, N, K, layer=0):
+    """codes, scales and biases of an affine8_g64 resident from the seeded bf16
+    weights (scale and bias from each group's range; uniform codes: the values
+    do not change the timing), built with torch alone"""
+    w = synth.resident_weights(seed, N, K, layer=layer)
+    wt = torch.from_numpy(w.view(np.int16)).cuda().view(torch.bfloat16).float().view(N, K // 64, 64)
+    lo, hi = wt.amin(dim=2), wt.amax(dim=2)
+    scale = ((hi - lo) / 255.0).to(torch.bfloat16).view(torch.int16).contiguous()
+    bias = lo.to(torch.bfloat16).view(torch.int16).contiguous()
+    g = torch.Generator("cuda").manual_seed(1000 * seed + layer)
+    codes = torch.randint(0, 256, (N, K), dtype=torch.uint8, device="cuda", generator=g).view(torch.int32)
+    return codes.contiguous(), scale, bias
+
+
+def batched_leg(bank, K, Wm):
+    c = W.CONFIGS["batched"]
+    H, I, E, k, T = c["H"], c["I"], c["E"], c["k"], c["T"]
+    nv = 8
+    xs = bf16_dev(np.stack([W.inputs("batched", v)[0] for v in range(nv)]))
+    lgs = torch.from_numpy(np.stack([W.inputs("batched", v)[2] for v in range(nv)])).cuda()
+    idx = torch.empty((nv, T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((nv, T, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    ws = wq.workspace(wq.moe_nvfp4_workspace_bytes(T, k, H, I, E))
+    state = {"i": 0}
+
+    def step():
+        r = state["i"] % nv
+        state["i"] += 1
+        wq.moe_route_topk(None, None, lgs[r], T, H, E, k, idx[r], w[r])
+        wq.moe_nvfp4_forward(bank, xs[r], T, idx[r], w[r], k, None, y, 0, ws)
+
+    ms_total, _ = timed(step, K, Wm)
+    idx_h = idx.cpu().numpy()
+    rec = wq.moe_nvfp4_record_bytes(H, I)
+    rs = [(Wm + i) % nv for i in range(K)]
+    nb = np.array([len(np.unique(idx_h[r])) * rec + 2 * T * H * 2 for r in rs], dtype=np.float64)
+    gbs = nb.sum() / (ms_total * 1e-3) / 1e9
+    log(f"batched T=32: {ms_total / K:.3f} ms/step, {gbs:.1f} GB/s, {nb.mean() / rec:.1f} distinct records")
+    return {"workload": "T=32, top-8 of 256 on Zipf(1.1)-skewed logits (given), H=5120, I=2560", "steps": K,
+            "ms_per_step": round(ms_total / K, 4), "GBps": round(gbs, 1), "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes_per_step": int(nb.mean()), "distinct_records": round(float(nb.mean()) / rec, 1)}
+
+
+def stacked_leg(K, Wm):
+    c = W.CONFIGS["stacked"]
+    H, I, E, k, T, L = c["H"], c["I"], c["E"], c["k"], c["T"], c["layers"]
+    log(f"building the stacked banks: {L} x {E} records")
+    banks = [W.build_bank(c["bank_seed"], H, I, E, expert0=l * E)[0] for l in range(L)]
+    res = [resident_parts(c["seed"], H, H, layer=l) for l in range(L)]
+    wrs = [torch.from_numpy(synth.router_weights(c["seed"], H, E, layer=l)).cuda() for l in range(L)]
+    nv = 4
+    h0s = bf16_dev(np.stack([synth.activations(c["seed"] + 1000 * v, T, H) for v in range(nv)]))
+    hs = [torch.empty((T, H), dtype=torch.int16, device="cuda") for _ in range(2)]
+    nrm = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    a = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((L, T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((L, T, k), dtype=torch.float32, device="cuda")
+    ws = wq.workspace(wq.moe_nvfp4_workspace_bytes(T, k, H, I, E))
+    uniq = []
+    state = {"i": 0}
+
+    def step():
+        h = h0s[state["i"] % nv]
+        state["i"] += 1
+        for l in range(L):
+            wq.moe_rmsnorm(h, T, H, 1e-6, nrm)
+            codes, scale, bias = res[l]
+            wq.affine8_g64_linear(nrm, codes, scale, bias, T, H, H, a)
+            out = hs[l % 2]
+            wq.moe_nvfp4_layer(banks[l], a, wrs[l], T, k, h, logits, idx[l], w[l], out, 0, ws)
+            h = out
+
+    ms_total, _ = timed(step, K, Wm)
+    idx_h = idx.cpu().numpy()
+    rec = wq.moe_nvfp4_record_bytes(H, I)
+    per_layer_fixed = H * H + 2 * 2 * H * (H // 64) + H * E * 4 + 3 * T * H * 2
+    nb = sum(len(np.unique(idx_h[l])) * rec for l in range(L)) + L * per_layer_fixed
+    gbs = nb / (ms_total / K * 1e-3) / 1e9
+    log(f"stacked 12 x T=8: {ms_total / K:.3f} ms/step, {gbs:.1f} GB/s (last step {nb / 1e9:.2f} GB)")
+    return {"workload": "12 layers x (RMSNorm + 5120x5120 affine8_g64 + one-call NVFP4 layer with residual), T=8, "
+                        "3,072 records (68 GB)", "steps": K, "ms_per_step": round(ms_total / K, 4),
+            "GBps": round(gbs, 1), "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes_per_step_last": int(nb), "note": "bytes counted from the last timed step's routing"}
+
+
 def affine8_leg(K=5120, N=5120, steps=20, warm=3):
     w = synth.resident_weights(16, N, K)
     # codes, scales and biases of a 5120 x 5120 resident: the seeded bf16
@@ -476,7 +570,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "cache", "vq", "verify", "affine8"])
+    ap.add_argument("--only", choices=["decode", "prefill", "cache", "vq", "verify", "affine8", "batched",
+                                       "stacked"])
     ap.add_argument("--two-call", action="store_true",
                     help="decode step as moe_route_topk + moe_nvfp4_forward instead of moe_nvfp4_layer")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -503,6 +598,9 @@ def main():
     if args.only == "affine8":
         print(json.dumps({"affine8": affine8_leg()}), flush=True)
         return
+    if args.only == "stacked":
+        print(json.dumps({"stacked": stacked_leg(min(args.steps, 20), min(args.warmup, 3))}), flush=True)
+        return
     c = W.CONFIGS["decode"]
     log(f"building the bank: {c['E']} records of {wq.moe_nvfp4_record_bytes(c['H'], c['I'])} B")
     t0 = time.time()
@@ -516,6 +614,9 @@ def main():
         return
     if args.only == "verify":
         print(json.dumps({"verify": verify_leg(bank, args.steps, args.warmup)}), flush=True)
+        return
+    if args.only == "batched":
+        print(json.dumps({"batched": batched_leg(bank, min(args.steps, 50), min(args.warmup, 5))}), flush=True)
         return
 
     # ---- decode leg

@@ -693,6 +693,25 @@ def test_forward_batched_full_shape_sampled(big_bank):
     check_bf16_of(yb[sample], yf[sample], "batched bf16")
 
 
+def test_forward_routed_gemv_full_shape(big_bank):
+    # 48 tokens on skewed logits: past the one-item-per-wave path, below the
+    # grouped GEMM, i.e. the routed GEMV (sorted pairs, shared experts read
+    # once); sampled tokens against the oracle
+    bank, _ = big_bank
+    c = W.CONFIGS["batched"]
+    T = 48
+    x = synth.activations(60, T, c["H"])
+    logits = synth.skewed_logits(61, T, c["E"], rank_seed=c["seed"])
+    idx, w = oracle.route_topk(logits, c["k"])
+    res = synth.activations(62, T, c["H"])
+    yf, yb = gpu_forward(bank, x, idx, w, c["k"], 0, res)
+    sample = np.array([0, 1, 17, 30, 47])
+    recs = host_records(c["bank_seed"], np.unique(idx[sample]), c["H"], c["I"])
+    ref_f, _ = oracle.moe_forward(recs, c["E"], c["H"], c["I"], x[sample], idx[sample], w[sample], residual=res[sample])
+    check_f32(yf[sample], ref_f, "routed gemv T=48 sampled")
+    check_bf16_of(yb[sample], yf[sample], "routed gemv bf16")
+
+
 def test_forward_prefill_full_shape_sampled(big_bank):
     bank, _ = big_bank
     c = W.CONFIGS["prefill"]

@@ -22,6 +22,13 @@
 // k-slices so that lane half h = l / 32 takes inputs 32 h .. 32 h + 31 (one
 // 32-byte code piece per lane); the activations use the same assignment,
 // which only permutes the order of the sum.
+//
+// Work order: workgroups are dealt round-robin to the 8 XCDs, each with its
+// own L2. Workgroup b runs on XCD b mod 8; when the number of row tiles is a
+// multiple of 8, XCD x takes the row tiles x, x + 8, ... (a fifth of the
+// codes at K = N = 5120, which stay in its L2) for one token tile after the
+// other, so the activations stream through each XCD once and the codes are
+// read from HBM once per XCD.
 #include "common.h"
 #include "internal.h"
 
@@ -50,14 +57,24 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
                                                                   const uint8_t* __restrict__ codes,
                                                                   const uint16_t* __restrict__ scales,
                                                                   const uint16_t* __restrict__ biases, int T,
-                                                                  int K, int N, uint16_t* __restrict__ y) {
+                                                                  int K, int N, int n_tiles,
+                                                                  uint16_t* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) uint8_t As[2][kA8M * 128];
   __shared__ __attribute__((aligned(16))) uint32_t Xs[2][kA8M][2];  // group sums of x as bf16 (x1, x2 | x3, 0)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int G = K / 64;
-  const int m0 = blockIdx.y * kA8M;
-  const int n = blockIdx.x * kA8N + wave * 32 + l32;  // this lane's output row (MFMA column)
+  int mt, nt;
+  if (n_tiles % 8 == 0) {
+    const int per = n_tiles / 8, i = blockIdx.x / 8;
+    mt = i / per;
+    nt = (int)(blockIdx.x % 8) + 8 * (i % per);
+  } else {
+    mt = blockIdx.x / n_tiles;
+    nt = blockIdx.x % n_tiles;
+  }
+  const int m0 = mt * kA8M;
+  const int n = nt * kA8N + wave * 32 + l32;  // this lane's output row (MFMA column)
   const int nc = n < N ? n : N - 1;
   const uint8_t* crow = codes + (size_t)nc * K + 32 * h;
   // activation pieces of this thread: p = tid + 256 i, row p / 8, piece p % 8
@@ -184,9 +201,9 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
 
 hipError_t launch_affine8_gemm(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
                                const uint16_t* biases, int T, int K, int N, uint16_t* y, hipStream_t s) {
-  const dim3 grid((N + kA8N - 1) / kA8N, (T + kA8M - 1) / kA8M);
-  launch_kernel("affine8_gemm", affine8_gemm_kernel, grid, dim3(kA8Threads), 0, s, x,
-                reinterpret_cast<const uint8_t*>(codes), scales, biases, T, K, N, y);
+  const int n_tiles = (N + kA8N - 1) / kA8N, m_tiles = (T + kA8M - 1) / kA8M;
+  launch_kernel("affine8_gemm", affine8_gemm_kernel, dim3(n_tiles * m_tiles), dim3(kA8Threads), 0, s, x,
+                reinterpret_cast<const uint8_t*>(codes), scales, biases, T, K, N, n_tiles, y);
   return hipGetLastError();
 }
 

@@ -559,8 +559,18 @@ static int layer_checks(const char* who, const BankView& v, const uint16_t* x, i
 
 // up to kFlatDecodeMaxT tokens of at most kFlatDecodeMaxK pairs each, whose
 // mids fit in 64 KiB of LDS
+static int flat_max_t() {
+  static int v = -1;
+  if (v < 0) {
+    const char* s = std::getenv("MOE_FLAT_MAX_T");
+    v = (s && *s) ? std::atoi(s) : kFlatDecodeMaxT;
+    if (v < 1) v = 1;
+  }
+  return v;
+}
+
 static bool flat_path(const BankView& v, int T, int k, unsigned flags) {
-  return T >= 1 && T <= kFlatDecodeMaxT && !(flags & MOE_FORCE_PREFILL) && k <= kFlatDecodeMaxK &&
+  return T >= 1 && T <= flat_max_t() && !(flags & MOE_FORCE_PREFILL) && k <= kFlatDecodeMaxK &&
          (size_t)k * v.I * 2 <= 65536 && v.I % 16 == 0;
 }
 

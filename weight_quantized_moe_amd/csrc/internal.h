@@ -94,9 +94,11 @@ hipError_t launch_decode_down(const BankView& b, const uint16_t* mid, const floa
 // mids in LDS, I % 16 == 0): gate/up then down with the combine folded in;
 // mid [T*k][I] is scratch, y [T][H] the layer output
 constexpr int kFlatDecodeMaxK = 16;
-// tokens the one-item-per-wave decode kernels take (a draft-verify pass);
-// more tokens share experts enough for the routed GEMV to pay
-constexpr int kFlatDecodeMaxT = 4;
+// tokens the one-item-per-wave decode kernels take: they stream every pair's
+// record at about 5 TB/s, the routed GEMV reads each distinct record once at
+// about 3 TB/s, so up to 32 tokens (skewed routing: 164 distinct records for
+// 256 pairs) streaming every pair is faster
+constexpr int kFlatDecodeMaxT = 32;
 hipError_t launch_flat_decode(const BankView& b, const uint16_t* x, int T, const int32_t* idx,
                               const float* w, int k, const uint16_t* residual, uint16_t* mid,
                               void* y, bool f32_out, hipStream_t s);
