@@ -767,6 +767,34 @@ def test_affine8_and_rmsnorm():
     check_bf16(to_np_bits(y), oracle.bf16_to_f32(ref), "rmsnorm")
 
 
+def test_affine8_and_rmsnorm_unaligned_rows():
+    # activations 4-byte but not 16-byte aligned: the linear stages them with
+    # single-word loads, the norm takes its strided loop (also for H not a
+    # multiple of 8); 20 tokens take three passes of 8
+    T, K, N = 20, 640, 72
+    v = synth.resident_weights(21, N, K)
+    codes, scales, biases = oracle.q8_quantize(v)
+    x = synth.activations(22, T, K)
+    ref_f, _ = oracle.affine8_linear(x, codes, scales, biases)
+    flat = torch.zeros(T * K + 8, dtype=torch.int16, device=DEV)
+    flat[2:2 + T * K] = bf16_tensor(x).reshape(-1)
+    xv = flat[2:2 + T * K].view(T, K)
+    assert xv.data_ptr() % 16 == 4
+    y = torch.empty((T, N), dtype=torch.int16, device=DEV)
+    wq.affine8_g64_linear(xv, torch.from_numpy(codes.view(np.int32)).to(DEV), bf16_tensor(scales),
+                          bf16_tensor(biases), T, K, N, y)
+    torch.cuda.synchronize()
+    check_bf16(to_np_bits(y), ref_f, f"affine8 unaligned {T}x{K}x{N}")
+    for H in (640, 300):
+        xr = synth.activations(23, 5, H)
+        flat = torch.zeros(5 * H + 8, dtype=torch.int16, device=DEV)
+        flat[2:2 + 5 * H] = bf16_tensor(xr).reshape(-1)
+        yr = torch.empty((5, H), dtype=torch.int16, device=DEV)
+        wq.moe_rmsnorm(flat[2:2 + 5 * H].view(5, H), 5, H, 1e-6, yr)
+        torch.cuda.synchronize()
+        check_bf16(to_np_bits(yr), oracle.bf16_to_f32(oracle.rmsnorm(xr, 1e-6)), f"rmsnorm unaligned H={H}")
+
+
 @pytest.mark.parametrize("T,K,N", [(300, 256, 200), (64, 128, 64), (129, 512, 130)])
 def test_affine8_gemm_ragged(T, K, N):
     # from 64 tokens the linear runs as the MFMA GEMM: ragged token and row

@@ -83,14 +83,42 @@ hipError_t launch_dequant(const BankView& b, int expert, int proj, float* out_f3
 }
 
 // ---- weightless RMS norm -------------------------------------------------------
+// One workgroup per token. A row of up to 8,192 values (16-byte aligned, H a
+// multiple of 8) is read once into registers, all loads in flight together;
+// other rows take a strided loop over single values.
+constexpr int kRmsU = 4;  // 16-byte pieces per thread held in registers
+
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* x, int H, float eps,
                                                       uint16_t* y) {
   const size_t t = blockIdx.x;
   const uint16_t* xr = x + t * H;
+  uint16_t* yr = y + t * H;
+  const int np = H / 8;
+  const bool vec =
+      (H % 8 == 0) && np <= kRmsU * 256 && ((uintptr_t)xr & 15) == 0 && ((uintptr_t)yr & 15) == 0;
+  u32x4 v[kRmsU];
   float ss = 0.0f;
-  for (int h = threadIdx.x; h < H; h += 256) {
-    float v = bf16_to_f32(xr[h]);
-    ss = fmaf(v, v, ss);
+  if (vec) {
+#pragma unroll
+    for (int u = 0; u < kRmsU; u++) {
+      const int i = threadIdx.x + 256 * u;
+      v[u] = i < np ? reinterpret_cast<const u32x4*>(xr)[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kRmsU; u++) {
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const float a = bf16_to_f32(w[q] & 0xFFFFu), b = bf16_to_f32(w[q] >> 16);
+        ss = fmaf(a, a, ss);
+        ss = fmaf(b, b, ss);
+      }
+    }
+  } else {
+    for (int h = threadIdx.x; h < H; h += 256) {
+      const float a = bf16_to_f32(xr[h]);
+      ss = fmaf(a, a, ss);
+    }
   }
   ss = wave_sum(ss);
   __shared__ float part[4];
@@ -98,7 +126,23 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* x, int H, 
   __syncthreads();
   const float tot = (part[0] + part[1]) + (part[2] + part[3]);
   const float inv = 1.0f / sqrtf(tot / (float)H + eps);
-  for (int h = threadIdx.x; h < H; h += 256) y[t * H + h] = f32_to_bf16(bf16_to_f32(xr[h]) * inv);
+  if (vec) {
+#pragma unroll
+    for (int u = 0; u < kRmsU; u++) {
+      const int i = threadIdx.x + 256 * u;
+      if (i < np) {
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+          o[q] = (uint32_t)f32_to_bf16(bf16_to_f32(w[q] & 0xFFFFu) * inv) |
+                 ((uint32_t)f32_to_bf16(bf16_to_f32(w[q] >> 16) * inv) << 16);
+        reinterpret_cast<u32x4*>(yr)[i] = u32x4{o[0], o[1], o[2], o[3]};
+      }
+    }
+  } else {
+    for (int h = threadIdx.x; h < H; h += 256) yr[h] = f32_to_bf16(bf16_to_f32(xr[h]) * inv);
+  }
 }
 
 hipError_t launch_rmsnorm(const uint16_t* x, int T, int H, float eps, uint16_t* y, hipStream_t s) {
@@ -108,98 +152,165 @@ hipError_t launch_rmsnorm(const uint16_t* x, int T, int H, float eps, uint16_t* 
 
 // ---- affine8_g64 resident linear ("Beam 1.0 501B-A23B, streaming pack, NVFP4
 // experts / MLX 8-bit residents", residents and q8-rule bullets) --------------------
-// y[t][n] = sum_g scale[n][g] * (sum_{k in g} x[t][k] q[n][k]) + bias[n][g] * (sum_{k in g} x[t][k]).
-// Bandwidth-bound for small T: a wave owns one output row, its lanes sweep the
-// row's 8-bit codes 16 bytes at a time (64 lanes x 16 B = 1 KiB per load).
-// A code q <= 255 has at most 8 significant bits, so it is exact in bf16: two
-// codes become one packed bf16 pair (byte -> f32 -> high half), and v_dot2
-// multiplies them with a pair of activations. The activations (bf16 pairs) and
-// their 16-element partial sums (for the bias term) sit in LDS, 4 tokens per
-// pass.
-constexpr int kAffTok = 4;
-constexpr int kAffRows = 16;
+// y[t][n] = sum_g scale[n][g] * (sum_{k in g} x[t][k] q[n][k]) + bias[n][g] * (sum_{k in g} x[t][k])
+// over the 64-input groups g, exactly. Bandwidth-bound for a few tokens (1 B
+// per weight plus 4 B per 64 read once), so the arithmetic must stay off the
+// critical path: both sums run on v_mfma_f32_16x16x32_bf16 with the tokens as
+// M (16 per pass) and weight rows as N. A code q <= 255 is exact in bf16, and
+// the group sum of x comes from an MFMA against a B operand of ones, which
+// leaves it in the output layout next to the others.
+//
+// A workgroup of 16 waves owns 32 rows (two 16-row MFMA blocks that share the
+// activations and the ones-MFMA): at K = N = 5120 its 160 workgroups run as
+// one round on the chip, where 16-row workgroups left a second round a
+// quarter full and took twice as long. The K groups are split over the waves
+// (5 consecutive groups each per block of 5120 inputs), so every wave has all
+// its loads (16 bytes of codes per row block and 32 bytes of activations per
+// group and lane) in flight at once, straight into registers; the scales and
+// biases of the workgroup's rows (adjacent in memory) come in by consecutive
+// lanes and wait in LDS. The waves' partial sums meet in LDS and are added in
+// wave order.
+//
+// MFMA layouts (16x16x32): A lane l holds token l%16, inputs 8(l/16)..+7 of
+// the k-slice; B lane l holds row l%16, the same inputs; D lane l holds row
+// l%16 for tokens 4(l/16)..+3. The 64 inputs of a group go to two k-slices
+// so that lane group j = l/16 takes inputs 16j..16j+15 (one 16-byte piece of
+// codes), the first 8 in slice 0 and the rest in slice 1; A takes the same
+// assignment, which only permutes the order of the sum.
+//
+// Every load is unconditional (indices are clamped instead): a load under a
+// lane-dependent branch makes the compiler wait for it where the branch
+// rejoins, which would serialize the round trips. Padding tokens (lanes with
+// l%16 >= the pass's token count) load the last real token's row, and rows
+// past N load row N-1; neither is stored.
+constexpr int kAffWaves = 16;                       // waves per workgroup
+constexpr int kAffGW = 5;                           // groups per wave in a K block
+constexpr int kAffKB = 64 * kAffGW * kAffWaves;     // inputs per K block (5120)
+constexpr int kAffTok = 16;                         // tokens per pass
+constexpr int kAffRB = 2;                           // 16-row blocks per workgroup
+constexpr int kAffPre = (16 * kAffRB * (kAffKB / 64) + 64 * kAffWaves - 1) / (64 * kAffWaves);
 
-__device__ __forceinline__ uint32_t u8pair_bf16(uint32_t word, int lo_byte) {
-  const float a = (float)((word >> (8 * lo_byte)) & 0xFFu);
-  const float b = (float)((word >> (8 * lo_byte + 8)) & 0xFFu);
-  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+// 8 codes (two words) -> 8 bf16 values (exact: a code has at most 8
+// significant bits, so its f32 value has a zero low half)
+__device__ __forceinline__ bf16x8 u8x8_bf16(uint32_t w0, uint32_t w1) {
+  uint32_t o[4];
+  const uint32_t w[2] = {w0, w1};
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    const float a = (float)(w[h] & 0xFFu), b = (float)((w[h] >> 8) & 0xFFu);
+    const float c = (float)((w[h] >> 16) & 0xFFu), d = (float)(w[h] >> 24);
+    o[2 * h] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+    o[2 * h + 1] = (__float_as_uint(c) >> 16) | (__float_as_uint(d) & 0xFFFF0000u);
+  }
+  return __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
 }
 
-__global__ __launch_bounds__(256) void affine8_kernel(const uint16_t* __restrict__ x,
-                                                      const uint32_t* __restrict__ codes,
-                                                      const uint16_t* __restrict__ scales,
-                                                      const uint16_t* __restrict__ biases, int T,
-                                                      int K, int N, uint16_t* __restrict__ y) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-  uint32_t* xs = lds;                                          // [kAffTok][K/2] bf16 pairs
-  float* xc = reinterpret_cast<float*>(lds + kAffTok * (K / 2));  // [kAffTok][K/16]
+template <bool X16>
+__global__ __launch_bounds__(64 * kAffWaves) void affine8_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint8_t* __restrict__ codes,
+                                                                 const uint16_t* __restrict__ scales,
+                                                                 const uint16_t* __restrict__ biases, int T,
+                                                                 int K, int N, uint16_t* __restrict__ y) {
+  constexpr int R = 16 * kAffRB;                      // rows per workgroup
+  __shared__ float red[kAffWaves][kAffTok][R];        // [wave][token][row]
+  __shared__ uint32_t sbl[R][kAffKB / 64];            // scale | bias << 16 of the block's groups
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int G = K / 64, C16 = K / 16;
-  const int r0 = blockIdx.x * kAffRows, r1 = min(N, r0 + kAffRows);
+  const int n = lane & 15, j = lane >> 4;
+  const int G = K / 64;
+  const int r0 = blockIdx.x * R;
+  int row[kAffRB];
+#pragma unroll
+  for (int b = 0; b < kAffRB; b++) row[b] = min(r0 + 16 * b + n, N - 1);
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   for (int t0 = 0; t0 < T; t0 += kAffTok) {
     const int nt = min(kAffTok, T - t0);
-    __syncthreads();
-    for (int i = threadIdx.x; i < kAffTok * (K / 2); i += 256) {
-      int tt = i / (K / 2), kk = i % (K / 2);
-      xs[i] = (tt < nt) ? reinterpret_cast<const uint32_t*>(x + (size_t)(t0 + tt) * K)[kk] : 0u;
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < kAffTok * C16; i += 256) {
-      int tt = i / C16, c = i % C16;
-      float s = 0.0f;
-      for (int q = 0; q < 8; q++) {
-        uint32_t pr = xs[tt * (K / 2) + 8 * c + q];
-        s += bf16_to_f32(pr & 0xFFFFu) + bf16_to_f32(pr >> 16);
+    f32x4 acc[kAffRB];
+#pragma unroll
+    for (int b = 0; b < kAffRB; b++) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int kb = 0; kb < K; kb += kAffKB) {
+      const int gb = kb / 64, gn = min(kAffKB, K - kb) / 64;  // the block's first group and group count
+      const int g0 = gb + wave * kAffGW;
+      // the rows' scales and biases of the block, by consecutive lanes from
+      // consecutive addresses; loaded first, so storing them to LDS waits
+      // for these loads only
+      uint16_t ps[kAffPre], pb[kAffPre];
+#pragma unroll
+      for (int u = 0; u < kAffPre; u++) {
+        const int i = min((int)threadIdx.x + 64 * kAffWaves * u, R * gn - 1);
+        const size_t o = (size_t)min(r0 + i / gn, N - 1) * G + gb + i % gn;
+        ps[u] = scales[o];
+        pb[u] = biases[o];
       }
-      xc[i] = s;
-    }
-    __syncthreads();
-    for (int r = r0 + wave; r < r1; r += 4) {
-      float acc[kAffTok];
+      u32x4 q[kAffRB][kAffGW], xa[kAffGW], xb[kAffGW];
 #pragma unroll
-      for (int tt = 0; tt < kAffTok; tt++) acc[tt] = 0.0f;
-      const uint8_t* row = reinterpret_cast<const uint8_t*>(codes) + (size_t)r * K;
-      for (int c = lane; c < C16; c += 64) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(row + 16 * (size_t)c);
-        const int g = c / 4;
-        const float sc = bf16_to_f32(scales[(size_t)r * G + g]);
-        const float bi = bf16_to_f32(biases[(size_t)r * G + g]);
-        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-        uint32_t qp[8];
+      for (int i = 0; i < kAffGW; i++) {
+        const int g = min(g0 + i, G - 1);  // groups past G: loaded, weighted by zero
 #pragma unroll
-        for (int b = 0; b < 4; b++) {
-          qp[2 * b] = u8pair_bf16(wv[b], 0);
-          qp[2 * b + 1] = u8pair_bf16(wv[b], 2);
-        }
-#pragma unroll
-        for (int tt = 0; tt < kAffTok; tt++) {
-          if (tt < nt) {
-            const u32x4* xp = reinterpret_cast<const u32x4*>(xs + tt * (K / 2) + 8 * c);
-            const u32x4 xa = xp[0], xb = xp[1];
-            const uint32_t xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-            float s = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; j++) s = dot2(__builtin_bit_cast(bf16x2, qp[j]), xv[j], s);
-            acc[tt] = fmaf(sc, s, fmaf(bi, xc[tt * C16 + c], acc[tt]));
-          }
+        for (int b = 0; b < kAffRB; b++)
+          q[b][i] = *reinterpret_cast<const u32x4*>(codes + (size_t)row[b] * K + 64 * g + 16 * j);
+        const uint16_t* xp = x + (size_t)(t0 + min(n, nt - 1)) * K + 64 * g + 16 * j;
+        if (X16) {
+          xa[i] = reinterpret_cast<const u32x4*>(xp)[0];
+          xb[i] = reinterpret_cast<const u32x4*>(xp)[1];
+        } else {
+          const uint32_t* xw = reinterpret_cast<const uint32_t*>(xp);
+          xa[i] = u32x4{xw[0], xw[1], xw[2], xw[3]};
+          xb[i] = u32x4{xw[4], xw[5], xw[6], xw[7]};
         }
       }
+      // keep every load above the first use (the scheduler would otherwise
+      // spread them over the MFMAs, one round trip per group)
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();  // sbl of the previous block is read
 #pragma unroll
-      for (int tt = 0; tt < kAffTok; tt++) {
-        if (tt < nt) {
-          float v = wave_sum(acc[tt]);
-          if (lane == 0) y[(size_t)(t0 + tt) * N + r] = f32_to_bf16(v);
+      for (int u = 0; u < kAffPre; u++) {
+        // unconditional (a conditional store would pull its load below the
+        // others); threads past the end rewrite the last entry's own value
+        const int i = min((int)threadIdx.x + 64 * kAffWaves * u, R * gn - 1);
+        sbl[i / gn][i % gn] = (uint32_t)ps[u] | ((uint32_t)pb[u] << 16);
+      }
+      __syncthreads();  // sbl is written
+#pragma unroll
+      for (int i = 0; i < kAffGW; i++) {
+        const bf16x8 a0 = __builtin_bit_cast(bf16x8, xa[i]), a1 = __builtin_bit_cast(bf16x8, xb[i]);
+        const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, ones, z, 0, 0, 0);
+        xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, ones, xs, 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < kAffRB; b++) {
+          f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, u8x8_bf16(q[b][i].x, q[b][i].y), z, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, u8x8_bf16(q[b][i].z, q[b][i].w), s, 0, 0, 0);
+          const uint32_t sb = (g0 + i < G) ? sbl[16 * b + n][g0 - gb + i] : 0u;
+          const float sc = bf16_to_f32(sb & 0xFFFFu), bi = bf16_to_f32(sb >> 16);
+#pragma unroll
+          for (int e = 0; e < 4; e++) acc[b][e] = fmaf(sc, s[e], fmaf(bi, xs[e], acc[b][e]));
         }
       }
     }
+#pragma unroll
+    for (int b = 0; b < kAffRB; b++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) red[wave][4 * j + e][16 * b + n] = acc[b][e];
+    __syncthreads();
+    if (threadIdx.x < kAffTok * R) {
+      const int tt = threadIdx.x / R, nn = threadIdx.x % R;
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kAffWaves; w++) v += red[w][tt][nn];
+      if (tt < nt && r0 + nn < N) y[(size_t)(t0 + tt) * N + r0 + nn] = f32_to_bf16(v);
+    }
+    __syncthreads();  // red is rewritten by the next pass
   }
 }
 
 hipError_t launch_affine8(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
                           const uint16_t* biases, int T, int K, int N, uint16_t* y, hipStream_t s) {
-  size_t lds = (size_t)kAffTok * (K / 2) * 4 + (size_t)kAffTok * (K / 16) * 4;
-  launch_kernel("affine8", affine8_kernel, dim3((N + kAffRows - 1) / kAffRows), dim3(256), (uint32_t)lds, s, x,
-                codes, scales, biases, T, K, N, y);
+  const dim3 grid((N + 16 * kAffRB - 1) / (16 * kAffRB)), block(64 * kAffWaves);
+  const uint8_t* c8 = reinterpret_cast<const uint8_t*>(codes);
+  if (((uintptr_t)x & 15) == 0)
+    launch_kernel("affine8", affine8_kernel<true>, grid, block, 0, s, x, c8, scales, biases, T, K, N, y);
+  else
+    launch_kernel("affine8", affine8_kernel<false>, grid, block, 0, s, x, c8, scales, biases, T, K, N, y);
   return hipGetLastError();
 }
 

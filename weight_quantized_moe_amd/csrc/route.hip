@@ -17,11 +17,12 @@ namespace moe {
 // Router weights are f32 [E][H], one contiguous row per expert. Block
 // (expert e, token group) computes the whole dot product of that row with up
 // to 8 token rows: thread j sums 16-byte pieces h = 4j, 4j + 1024, ... of the
-// row (coalesced) against the matching x values (router_thread_sum, the
-// arithmetic the one-token layer kernel uses too); the sum is reduced in the
-// wave, then over the 4 waves in wave order. The row is read once per token
-// (the token's pass hits it in the cache after the first). One block per
-// expert keeps every CU busy at E = 256 without partial sums across blocks.
+// row (coalesced) against the matching x values (router_thread_sum's
+// arithmetic, which the one-token layer kernel uses too); the sum is reduced
+// in the wave, then over the 4 waves in wave order. The row's pieces are
+// loaded once for all the block's tokens, with every token's x pieces in the
+// same round trip. One block per expert keeps every CU busy at E = 256
+// without partial sums across blocks.
 __global__ __launch_bounds__(256) void router_kernel(const uint16_t* x, const float* Wr, float* logits, int T,
                                                      int H, int E) {
   const int e = blockIdx.x, t0 = blockIdx.y * kRouterTok;
@@ -29,9 +30,14 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t* x, const fl
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ float red[4][kRouterTok];
   const float* row = Wr + (size_t)e * H;
-  for (int tt = 0; tt < nt; tt++) {
-    const float s = wave_sum(router_thread_sum<256>(row, x + (size_t)(t0 + tt) * H, H, threadIdx.x));
-    if (lane == 0) red[wave][tt] = s;
+  float acc[kRouterTok];
+  router_thread_sums<256, kRouterTok>(row, x + (size_t)t0 * H, H, nt, threadIdx.x, acc);
+#pragma unroll
+  for (int tt = 0; tt < kRouterTok; tt++) {
+    if (tt < nt) {
+      const float s = wave_sum(acc[tt]);
+      if (lane == 0) red[wave][tt] = s;
+    }
   }
   __syncthreads();
   if (threadIdx.x < nt) {

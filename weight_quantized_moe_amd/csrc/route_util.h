@@ -63,4 +63,42 @@ __device__ __forceinline__ float router_thread_sum(const float* __restrict__ row
   return acc;
 }
 
+// The same chain for the nt <= TT tokens of x (rows H apart) at once: the row
+// piece is loaded once for all of them, and each token's FMAs run in exactly
+// router_thread_sum's order, so acc[tt] equals router_thread_sum for token tt.
+template <int NT, int TT>
+__device__ __forceinline__ void router_thread_sums(const float* __restrict__ row, const uint16_t* __restrict__ x,
+                                                   int H, int nt, int j, float (&acc)[TT]) {
+  constexpr int U = 8;
+#pragma unroll
+  for (int tt = 0; tt < TT; tt++) acc[tt] = 0.0f;
+  for (int h0 = 4 * j; h0 < H; h0 += 4 * NT * U) {
+    f32x4 wv[U];
+    u32x2 xv[TT][U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int h = h0 + 4 * NT * u;
+      if (h < H) {
+        wv[u] = *reinterpret_cast<const f32x4*>(row + h);
+#pragma unroll
+        for (int tt = 0; tt < TT; tt++)
+          if (tt < nt) xv[tt][u] = *reinterpret_cast<const u32x2*>(x + (size_t)tt * H + h);
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < TT; tt++) {
+      if (tt >= nt) continue;
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        if (h0 + 4 * NT * u < H) {
+          acc[tt] = fmaf(bf16_to_f32(xv[tt][u].x & 0xFFFFu), wv[u].x, acc[tt]);
+          acc[tt] = fmaf(bf16_to_f32(xv[tt][u].x >> 16), wv[u].y, acc[tt]);
+          acc[tt] = fmaf(bf16_to_f32(xv[tt][u].y & 0xFFFFu), wv[u].z, acc[tt]);
+          acc[tt] = fmaf(bf16_to_f32(xv[tt][u].y >> 16), wv[u].w, acc[tt]);
+        }
+      }
+    }
+  }
+}
+
 }  // namespace moe
