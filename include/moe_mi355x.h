@@ -218,7 +218,11 @@ int moe_nvfp4_layer(const moe_nvfp4_bank* b, const uint16_t* x, const float* w_r
  * bias[n][k/64]), f32 accumulation, bf16 out.
  * x bf16 [T][K]; codes U32 [N][K/4] (4 codes per word, first in the low
  * byte); scales, biases bf16 [N][K/64]; y bf16 [T][N].
- * Rules: K % 64 == 0, N >= 1, T >= 0; codes 16-byte aligned. */
+ * Rules: K % 64 == 0, N >= 1, T >= 0; codes 16-byte aligned, x 4-byte
+ * aligned (MOE_EALIGN otherwise). From 64 tokens (env
+ * MOE_AFFINE8_GEMM_MIN_T) with x 16-byte aligned the call runs as a tiled
+ * MFMA GEMM, below that as a bandwidth-bound pass that reads the weights
+ * once per 16 tokens; both accumulate in f32. */
 int affine8_g64_linear(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
                        const uint16_t* biases, int T, int K, int N, uint16_t* y, void* stream);
 

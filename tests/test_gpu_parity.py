@@ -749,7 +749,8 @@ def test_forward_deterministic(big_bank):
 
 # ---- S8 / S9 -------------------------------------------------------------------------------
 def test_affine8_and_rmsnorm():
-    for T, K, N in [(8, 5120, 5120), (3, 256, 192), (1, 64, 64), (13, 512, 100)]:
+    # (8, 128, 4100): 17-row workgroups on a 256-CU device, the last with 3 rows
+    for T, K, N in [(8, 5120, 5120), (3, 256, 192), (1, 64, 64), (13, 512, 100), (8, 128, 4100)]:
         v = synth.resident_weights(11, N, K)
         codes, scales, biases = oracle.q8_quantize(v)
         x = synth.activations(12, T, K)

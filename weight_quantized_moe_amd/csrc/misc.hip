@@ -160,10 +160,12 @@ hipError_t launch_rmsnorm(const uint16_t* x, int T, int H, float eps, uint16_t* 
 // the group sum of x comes from an MFMA against a B operand of ones, which
 // leaves it in the output layout next to the others.
 //
-// A workgroup of 16 waves owns 32 rows (two 16-row MFMA blocks that share the
-// activations and the ones-MFMA): at K = N = 5120 its 160 workgroups run as
-// one round on the chip, where 16-row workgroups left a second round a
-// quarter full and took twice as long. The K groups are split over the waves
+// A workgroup of 16 waves owns rw rows, 16 to 32 (two 16-row MFMA blocks that
+// share the activations and the ones-MFMA; lanes of the second block past rw
+// re-read the last row, from the cache): rw = N / (number of CUs), rounded
+// up, so the workgroups run as one round on the chip (20 rows at N = 5120).
+// A round of these workgroups costs about the same whether full or not:
+// 16-row workgroups left a second round a quarter full and took twice as long. The K groups are split over the waves
 // (5 consecutive groups each per block of 5120 inputs), so every wave has all
 // its loads (16 bytes of codes per row block and 32 bytes of activations per
 // group and lane) in flight at once, straight into registers; the scales and
@@ -210,17 +212,17 @@ __global__ __launch_bounds__(64 * kAffWaves) void affine8_kernel(const uint16_t*
                                                                  const uint8_t* __restrict__ codes,
                                                                  const uint16_t* __restrict__ scales,
                                                                  const uint16_t* __restrict__ biases, int T,
-                                                                 int K, int N, uint16_t* __restrict__ y) {
-  constexpr int R = 16 * kAffRB;                      // rows per workgroup
+                                                                 int K, int N, int rw, uint16_t* __restrict__ y) {
+  constexpr int R = 16 * kAffRB;                      // rows per workgroup at most
   __shared__ float red[kAffWaves][kAffTok][R];        // [wave][token][row]
   __shared__ uint32_t sbl[R][kAffKB / 64];            // scale | bias << 16 of the block's groups
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, j = lane >> 4;
   const int G = K / 64;
-  const int r0 = blockIdx.x * R;
+  const int r0 = blockIdx.x * rw, rend = min(r0 + rw, N);  // this workgroup's rows [r0, rend)
   int row[kAffRB];
 #pragma unroll
-  for (int b = 0; b < kAffRB; b++) row[b] = min(r0 + 16 * b + n, N - 1);
+  for (int b = 0; b < kAffRB; b++) row[b] = min(r0 + 16 * b + n, rend - 1);
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   for (int t0 = 0; t0 < T; t0 += kAffTok) {
     const int nt = min(kAffTok, T - t0);
@@ -237,7 +239,7 @@ __global__ __launch_bounds__(64 * kAffWaves) void affine8_kernel(const uint16_t*
 #pragma unroll
       for (int u = 0; u < kAffPre; u++) {
         const int i = min((int)threadIdx.x + 64 * kAffWaves * u, R * gn - 1);
-        const size_t o = (size_t)min(r0 + i / gn, N - 1) * G + gb + i % gn;
+        const size_t o = (size_t)min(r0 + i / gn, rend - 1) * G + gb + i % gn;
         ps[u] = scales[o];
         pb[u] = biases[o];
       }
@@ -297,20 +299,30 @@ __global__ __launch_bounds__(64 * kAffWaves) void affine8_kernel(const uint16_t*
       float v = 0.0f;
 #pragma unroll
       for (int w = 0; w < kAffWaves; w++) v += red[w][tt][nn];
-      if (tt < nt && r0 + nn < N) y[(size_t)(t0 + tt) * N + r0 + nn] = f32_to_bf16(v);
+      if (tt < nt && r0 + nn < rend) y[(size_t)(t0 + tt) * N + r0 + nn] = f32_to_bf16(v);
     }
     __syncthreads();  // red is rewritten by the next pass
   }
 }
 
+// compute units of the current device (0 if the query fails)
+static int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
 hipError_t launch_affine8(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
                           const uint16_t* biases, int T, int K, int N, uint16_t* y, hipStream_t s) {
-  const dim3 grid((N + 16 * kAffRB - 1) / (16 * kAffRB)), block(64 * kAffWaves);
+  const int cus = device_cus();
+  const int rw = std::min(16 * kAffRB, std::max(16, cus > 0 ? (N + cus - 1) / cus : 16 * kAffRB));
+  const dim3 grid((N + rw - 1) / rw), block(64 * kAffWaves);
   const uint8_t* c8 = reinterpret_cast<const uint8_t*>(codes);
   if (((uintptr_t)x & 15) == 0)
-    launch_kernel("affine8", affine8_kernel<true>, grid, block, 0, s, x, c8, scales, biases, T, K, N, y);
+    launch_kernel("affine8", affine8_kernel<true>, grid, block, 0, s, x, c8, scales, biases, T, K, N, rw, y);
   else
-    launch_kernel("affine8", affine8_kernel<false>, grid, block, 0, s, x, c8, scales, biases, T, K, N, y);
+    launch_kernel("affine8", affine8_kernel<false>, grid, block, 0, s, x, c8, scales, biases, T, K, N, rw, y);
   return hipGetLastError();
 }
 
