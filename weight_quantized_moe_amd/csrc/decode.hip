@@ -91,19 +91,6 @@ __device__ int route_in_block(const int32_t* idx, int P, int E, int slot, int* s
   return total;
 }
 
-// Stage the bf16 input rows of pairs[m0..m0+mt) into LDS as packed pairs,
-// xs[m][0..len/2). by_token: row = pair / k (x), else row = pair (mid).
-__device__ __forceinline__ void stage_rows(uint32_t* xs, const uint16_t* src, int len,
-                                           const int* pairs, int m0, int mt, int k, bool by_token) {
-  for (int m = 0; m < mt; m++) {
-    const int p = pairs[m0 + m];
-    const size_t row = by_token ? (size_t)(p / k) : (size_t)p;
-    const u32x4* s = reinterpret_cast<const u32x4*>(src + row * (size_t)len);
-    u32x4* d = reinterpret_cast<u32x4*>(xs + m * (len / 2));
-    for (int i = threadIdx.x; i < len / 8; i += kDecThreads) d[i] = s[i];
-  }
-}
-
 // NPROJ = 2: gate and up rows (input x, SwiGLU into mid); NPROJ = 1: down
 // rows (input mid, routing-weighted f32 into part). MT tokens per pass.
 // A wave walks its rows in steps (pass, quad batch); all loads of a step are
@@ -134,7 +121,7 @@ __global__ __launch_bounds__(kDecThreads) void gemv_kernel(DecodeArgs a) {
   const int p0 = (NPROJ == 2) ? 0 : 2;
   const uint8_t* rec = a.bank + (size_t)e * a.stride;
   extern __shared__ __attribute__((aligned(16))) uint32_t xs[];  // [MT][K/2]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rsub = lane / G, sub = lane % G;
   const int rows_per_block = a.passes * kDecWaves * R;
   const int r0 = blockIdx.x * rows_per_block, r1 = min(N, r0 + rows_per_block);
@@ -164,11 +151,41 @@ __global__ __launch_bounds__(kDecThreads) void gemv_kernel(DecodeArgs a) {
 #pragma unroll
   for (int q = 0; q < NPROJ; q++) t[q] = global_factor(*reinterpret_cast<const float*>(rec + a.g[p0 + q]));
 
+  // The chunk's input rows go HBM -> LDS with no registers (one wave-wide
+  // load per 1 KiB of a row). With one load step per wave (every row's quads
+  // in one batch, the usual case) the weights are loaded once, before the
+  // first chunk's rows, and stay in registers for every chunk: the rows and
+  // the weights are in flight together and one wait covers both. Loads
+  // complete in issue order, so nothing waited for between the weights and
+  // the rows may be a load: the first chunk's row numbers are read before
+  // the weights, and the barriers wait for LDS only (step_barrier).
+  const int per_row = K / 8, ipr = (per_row + 63) / 64;  // 16-byte pieces and wave loads per row
+  int prow[MT];  // input rows of the chunk (wave-uniform)
+  auto chunk_rows = [&](int m0, int mt) {
+#pragma unroll
+    for (int m = 0; m < MT; m++) {
+      const int p = pairs[m0 + min(m, mt - 1)];
+      prow[m] = __builtin_amdgcn_readfirstlane((NPROJ == 2) ? p / a.k : p);
+    }
+  };
+  chunk_rows(0, min(MT, M));
+  if (nsteps == 1) load_step(0);
   for (int m0 = 0; m0 < M; m0 += MT) {
     const int mt = min(MT, M - m0);
-    __syncthreads();
-    stage_rows(xs, a.in, K, pairs, m0, mt, a.k, NPROJ == 2);
-    __syncthreads();
+    step_barrier();  // the previous chunk's rows are read
+    if (m0 > 0) chunk_rows(m0, mt);
+    for (int jj = wave; jj < mt * ipr; jj += kDecWaves) {
+      const int m = jj / ipr, blk = jj - m * ipr, pin = 64 * blk + lane;
+      int row = prow[0];
+#pragma unroll
+      for (int mm = 1; mm < MT; mm++)
+        if (m == mm) row = prow[mm];
+      if (pin < per_row)
+        dma16(uniform_ptr(a.in + (size_t)row * K), 16u * (uint32_t)pin,
+              __builtin_amdgcn_readfirstlane(lds_addr(xs + m * (K / 2)) + 1024u * (uint32_t)blk));
+    }
+    wait_vmcnt<0>();
+    step_barrier();
     float wt[MT];
     int pr[MT];
 #pragma unroll
@@ -182,7 +199,7 @@ __global__ __launch_bounds__(kDecThreads) void gemv_kernel(DecodeArgs a) {
 #pragma unroll
       for (int m = 0; m < MT; m++) acc[q][m] = 0.0f;
     for (int st = 0; st < nsteps; st++) {
-      load_step(st);
+      if (nsteps > 1) load_step(st);
       const int p = st / nqb, qb = (st % nqb) * G * kQB;
       const int r = r0 + (p * kDecWaves + wave) * R + rsub;
       const bool row_ok = r < r1;

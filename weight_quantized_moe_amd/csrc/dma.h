@@ -43,6 +43,17 @@ __device__ __forceinline__ void dma_copy_lds(const void* src, void* dst, uint32_
   }
 }
 
+// Workgroup barrier after this wave's LDS accesses have completed. No memory
+// fence: __syncthreads()'s fence would also wait for every load in flight
+// (weights loaded into registers ahead of their use, HBM -> LDS copies). The
+// asm statement keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void step_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // s_waitcnt vmcnt(n) alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
 // expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
 template <int N>

@@ -58,16 +58,6 @@ struct PrefillArgs {
   float* part;
 };
 
-// Workgroup barrier after this wave's LDS accesses have completed. No memory
-// fence: a fence would also wait for every HBM -> LDS load in flight. The
-// asm statement keeps the compiler from moving memory accesses across it.
-__device__ __forceinline__ void step_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
-  asm volatile("s_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // 16-byte slot of piece j in A row r (8 pieces per row)
 __device__ __forceinline__ int a_slot(int r, int j) { return j ^ ((r & 7) ^ ((r >> 3) & 1)); }
 // 16-byte slot of piece c in B row r (4 pieces per row)
