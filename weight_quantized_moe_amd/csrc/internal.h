@@ -95,10 +95,10 @@ hipError_t launch_decode_down(const BankView& b, const uint16_t* mid, const floa
 // mid [T*k][I] is scratch, y [T][H] the layer output
 constexpr int kFlatDecodeMaxK = 16;
 // tokens the one-item-per-wave decode kernels take: they stream every pair's
-// record at about 5 TB/s, the routed GEMV reads each distinct record once at
-// about 3 TB/s, so up to 32 tokens (skewed routing: 164 distinct records for
-// 256 pairs) streaming every pair is faster
-constexpr int kFlatDecodeMaxT = 32;
+// record at about 6 TB/s, the routed GEMV reads each distinct record once
+// but more slowly; on skewed routing the two cross between 20 and 24 tokens
+// (577 against 588 us at 20, 689 against 683 us at 24)
+constexpr int kFlatDecodeMaxT = 20;
 hipError_t launch_flat_decode(const BankView& b, const uint16_t* x, int T, const int32_t* idx,
                               const float* w, int k, const uint16_t* residual, uint16_t* mid,
                               void* y, bool f32_out, hipStream_t s);
