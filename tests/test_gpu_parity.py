@@ -712,6 +712,25 @@ def test_forward_routed_gemv_full_shape(big_bank):
     check_bf16_of(yb[sample], yf[sample], "routed gemv bf16")
 
 
+def test_routed_gemv_inblock_routing_matches_tables(big_bank, monkeypatch):
+    # 24 tokens take the routed GEMV; its blocks read their expert and pairs
+    # from the sort tables, or (MOE_GEMV_INBLOCK=1, up to 256 pairs) find them
+    # in idx themselves: same pairs in the same order, so bit-identical
+    bank, _ = big_bank
+    c = W.CONFIGS["batched"]
+    T = 24
+    x = synth.activations(91, T, c["H"])
+    lg = synth.skewed_logits(92, T, c["E"], rank_seed=93)
+    idx, w = oracle.route_topk(lg, c["k"])
+    yf_t, yb_t = gpu_forward(bank, x, idx, w, c["k"], 0, None)
+    monkeypatch.setenv("MOE_GEMV_INBLOCK", "1")
+    yf_i, yb_i = gpu_forward(bank, x, idx, w, c["k"], 0, None)
+    monkeypatch.delenv("MOE_GEMV_INBLOCK")
+    assert np.array_equal(yf_t.view(np.uint32), yf_i.view(np.uint32))
+    assert np.array_equal(yb_t, yb_i)
+    say(f"routed GEMV T={T}: in-block routing matches the sort tables bit for bit")
+
+
 def test_forward_prefill_full_shape_sampled(big_bank):
     bank, _ = big_bank
     c = W.CONFIGS["prefill"]

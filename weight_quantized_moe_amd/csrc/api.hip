@@ -557,15 +557,10 @@ static int layer_checks(const char* who, const BankView& v, const uint16_t* x, i
   return MOE_OK;
 }
 
-// up to kFlatDecodeMaxT tokens of at most kFlatDecodeMaxK pairs each, whose
-// mids fit in 64 KiB of LDS
+// read at each call (a test compares both routings in one process)
 static bool gemv_inblock() {
-  static int v = -1;
-  if (v < 0) {
-    const char* s = std::getenv("MOE_GEMV_INBLOCK");
-    v = (s && *s && std::atoi(s) != 0) ? 1 : 0;
-  }
-  return v == 1;
+  const char* s = std::getenv("MOE_GEMV_INBLOCK");
+  return s && *s && std::atoi(s) != 0;
 }
 
 static int flat_max_t() {
@@ -578,6 +573,8 @@ static int flat_max_t() {
   return v;
 }
 
+// up to kFlatDecodeMaxT tokens of at most kFlatDecodeMaxK pairs each, whose
+// mids fit in 64 KiB of LDS
 static bool flat_path(const BankView& v, int T, int k, unsigned flags) {
   return T >= 1 && T <= flat_max_t() && !(flags & MOE_FORCE_PREFILL) && k <= kFlatDecodeMaxK &&
          (size_t)k * v.I * 2 <= 65536 && v.I % 16 == 0;
