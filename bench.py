@@ -183,15 +183,16 @@ def timed(fn, steps, warmup):
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_gateup.txt")
 DECODE_SRC = os.path.join(ROOT, "weight_quantized_moe_amd", "csrc", "decode.hip")
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_T8192_counters.txt")
+PREFILL_SRC = os.path.join(ROOT, "weight_quantized_moe_amd", "csrc", "prefill.hip")
 
 
-def recorded_traffic(name):
-    """Bytes per launch of the decode gate/up launch `name` from the committed
-    counter summary, if it was measured on that launch and the current kernel
-    source; else None."""
+def recorded_traffic(name, path=TRAFFIC_FILE, source=DECODE_SRC):
+    """Bytes per launch of launch `name` from a committed counter summary, if
+    it was measured on that launch and the current kernel source; else None."""
     try:
-        fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line)
-        src = hashlib.sha1(open(DECODE_SRC, "rb").read()).hexdigest()
+        fields = dict(line.split(":", 1) for line in open(path) if ":" in line and not line.startswith("#"))
+        src = hashlib.sha1(open(source, "rb").read()).hexdigest()
         if fields.get("source_sha1", "").strip() != src or fields.get("launch", "").strip() != name:
             return None
         return int(float(fields["traffic_bytes_per_launch"]))
@@ -276,7 +277,8 @@ def prefill_leg(bank, P):
                         "65,536 pairs, 5.154 TFLOP per step",
             "roofline": {"kernel": "prefill_gateup", "bound": "mfma", "achieved": round(gu_tf, 2),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(gu_tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "frac": round(gu_tf / BF16_PEAK_TFLOPS, 4),
+                         "traffic": recorded_traffic("prefill_gateup", PREFILL_TRAFFIC_FILE, PREFILL_SRC),
                          "flop_per_launch": gu_flop,
                          "avg_launch_ms": round(pk["prefill_gateup"][0], 4)},
             "kernels_us": {n_: round(v[0] * 1e3, 2) for n_, v in pk.items()}}
