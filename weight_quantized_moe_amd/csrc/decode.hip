@@ -262,8 +262,9 @@ static void launch_gemv_g(const DecodeArgs& b, dim3 grid, size_t lds, bool one, 
 }
 
 // Tuning knobs (environment, read at each launch): MOE_GEMV_QB_{GATEUP,DOWN}
-// quads per lane per load step (1, 2 or 5); MOE_GEMV_PASSES_{GATEUP,DOWN} wave
-// passes per block.
+// quads per lane per load step (1, 2 or 5; defaults 1 and 5: gate/up with one
+// quad per step measured 5-9 % faster from 24 to 127 tokens, e.g. 1,350
+// against 1,480 us at 64); MOE_GEMV_PASSES_{GATEUP,DOWN} wave passes per block.
 template <int NPROJ>
 static hipError_t launch_gemv(const DecodeArgs& a, int slots, int max_m, hipStream_t s) {
   const int K = (NPROJ == 2) ? a.H : a.I;
@@ -271,7 +272,7 @@ static hipError_t launch_gemv(const DecodeArgs& a, int slots, int max_m, hipStre
   const int nquads = K / 64;
   const int G = (nquads % 16 == 0 || nquads > 40) ? 16 : 8;
   const int R = 64 / G;
-  const int qb = env_int(NPROJ == 2 ? "MOE_GEMV_QB_GATEUP" : "MOE_GEMV_QB_DOWN", 5);
+  const int qb = NPROJ == 2 ? env_int("MOE_GEMV_QB_GATEUP", 1) : env_int("MOE_GEMV_QB_DOWN", 5);
   DecodeArgs b = a;
   b.passes = env_int(NPROJ == 2 ? "MOE_GEMV_PASSES_GATEUP" : "MOE_GEMV_PASSES_DOWN", 1);
   if (b.passes < 1) b.passes = 1;

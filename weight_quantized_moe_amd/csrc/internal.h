@@ -96,9 +96,10 @@ hipError_t launch_decode_down(const BankView& b, const uint16_t* mid, const floa
 constexpr int kFlatDecodeMaxK = 16;
 // tokens the one-item-per-wave decode kernels take: they stream every pair's
 // record at about 6 TB/s, the routed GEMV reads each distinct record once
-// but more slowly; on skewed routing the two cross between 20 and 24 tokens
-// (577 against 588 us at 20, 689 against 683 us at 24)
-constexpr int kFlatDecodeMaxT = 20;
+// but more slowly; on skewed routing the two cross between 12 and 16 tokens
+// (392 against 402 us at 12, 477-490 against 470 us at 16, 574-584 against
+// 557 us at 20)
+constexpr int kFlatDecodeMaxT = 14;
 hipError_t launch_flat_decode(const BankView& b, const uint16_t* x, int T, const int32_t* idx,
                               const float* w, int k, const uint16_t* residual, uint16_t* mid,
                               void* y, bool f32_out, hipStream_t s);
