@@ -712,6 +712,32 @@ def test_forward_routed_gemv_full_shape(big_bank):
     check_bf16_of(yb[sample], yf[sample], "routed gemv bf16")
 
 
+@pytest.mark.parametrize("T", [14, 15])
+def test_flat_and_gemv_paths_at_the_token_limit(T, big_bank, monkeypatch):
+    # up to 14 tokens take the one-item-per-wave kernels, from 15 the routed
+    # GEMV; at the limit both paths (forced with MOE_FLAT_MAX_T) and the
+    # default one must each match the oracle on sampled tokens
+    bank, _ = big_bank
+    c = W.CONFIGS["batched"]
+    x = synth.activations(400 + T, T, c["H"])
+    lg = synth.skewed_logits(410 + T, T, c["E"], rank_seed=c["seed"])
+    idx, w = oracle.route_topk(lg, c["k"])
+    res = synth.activations(420 + T, T, c["H"])
+    sample = np.array([0, T // 2, T - 1])
+    recs = host_records(c["bank_seed"], np.unique(idx[sample]), c["H"], c["I"])
+    ref_f, _ = oracle.moe_forward(recs, c["E"], c["H"], c["I"], x[sample], idx[sample], w[sample],
+                                  residual=res[sample])
+    for lim in [None, "64", "1"]:
+        if lim is None:
+            monkeypatch.delenv("MOE_FLAT_MAX_T", raising=False)
+        else:
+            monkeypatch.setenv("MOE_FLAT_MAX_T", lim)
+        yf, yb = gpu_forward(bank, x, idx, w, c["k"], 0, res)
+        check_f32(yf[sample], ref_f, f"T={T} flat limit {lim or 'default'}")
+        check_bf16_of(yb[sample], yf[sample], f"T={T} flat limit {lim or 'default'} bf16")
+    monkeypatch.delenv("MOE_FLAT_MAX_T", raising=False)
+
+
 def test_routed_gemv_inblock_routing_matches_tables(big_bank, monkeypatch):
     # 24 tokens take the routed GEMV; its blocks read their expert and pairs
     # from the sort tables, or (MOE_GEMV_INBLOCK=1, up to 256 pairs) find them

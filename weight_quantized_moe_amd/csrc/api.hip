@@ -563,14 +563,11 @@ static bool gemv_inblock() {
   return s && *s && std::atoi(s) != 0;
 }
 
+// read at each call (a test runs both sides of the limit in one process)
 static int flat_max_t() {
-  static int v = -1;
-  if (v < 0) {
-    const char* s = std::getenv("MOE_FLAT_MAX_T");
-    v = (s && *s) ? std::atoi(s) : kFlatDecodeMaxT;
-    if (v < 1) v = 1;
-  }
-  return v;
+  const char* s = std::getenv("MOE_FLAT_MAX_T");
+  const int v = (s && *s) ? std::atoi(s) : kFlatDecodeMaxT;
+  return v < 1 ? 1 : v;
 }
 
 // up to kFlatDecodeMaxT tokens of at most kFlatDecodeMaxK pairs each, whose
