@@ -382,7 +382,10 @@ __device__ __forceinline__ void flat_stage_x(const FlatArgs& a, uint32_t* xs) {
 // expert s_idx[j] (-1: none).
 __device__ __forceinline__ void flat_gateup_items(const FlatArgs& a, const uint32_t* xs, const int* s_idx,
                                                   int blk, int nblk) {
-  constexpr int G = 16, R = 64 / G, QB = 5;
+  // two quads per lane per load step (three steps per 5,120-input row): the
+  // one-token launch measured 27.2-27.5 against 28.6-29.4 us with all five
+  // at once
+  constexpr int G = 16, R = 64 / G, QB = 2;
   const int H = a.H, I = a.I, nquads = H / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rsub = lane / G, sub = lane % G;
