@@ -1,7 +1,9 @@
 """Pins of the oracle's record layout against the numbers the pack page prints,
 and of nibble order / orientation by constructed one-hot records."""
 import json
+import math
 import os
+from fractions import Fraction
 
 import numpy as np
 
@@ -104,3 +106,45 @@ def test_pack_bytes_layout():
         assert rec[off[2 * p]:off[2 * p] + codes[p].nbytes].tobytes() == codes[p].astype("<u4").tobytes()
         assert rec[off[2 * p + 1]:off[2 * p + 1] + scales[p].nbytes].tobytes() == scales[p].tobytes()
         assert rec[off[6 + p]:off[6 + p] + 4].view("<f4")[0] == g[p]
+
+
+def _unit_want(codes_row_words, scale_row, in_):
+    """bf16 bits of e2m1(c) * e4m3(s) for one row, from the OCP E2M1 table, a
+    library E4M3 decoder and exact rational rounding (no oracle code)"""
+    e2m1 = exact.e2m1_table()
+    e4m3 = exact.e4m3_table()
+    out = np.empty(in_, np.uint16)
+    for c in range(in_):
+        code = (int(codes_row_words[c // 8]) >> (4 * (c % 8))) & 15
+        a, b = e2m1[code], float(e4m3[int(scale_row[c // 16])])
+        q = Fraction(a) * Fraction(b)
+        # a zero product takes the sign rule of IEEE multiplication
+        neg = (math.copysign(1.0, a) < 0) != (math.copysign(1.0, b) < 0)
+        out[c] = exact.round_bf16_bits(q) if q != 0 else (0x8000 if neg else 0)
+    return out
+
+
+def test_unit_values_follow_codes_and_scales_not_g():
+    # The bf16 unit value of a weight is e2m1(code) * e4m3(block scale), exact
+    # ([PACK] "What this pack holds", global-scales bullet: the global factor
+    # g / 2688 multiplies e4m3(scale) on top of it). Random codes, every finite
+    # E4M3 scale byte of either sign (subnormals 0x01..0x07 included) and
+    # several g far from 2688: every element is compared, and the same codes
+    # and scales under another g give the same unit values.
+    H, I = 64, 48
+    rng = np.random.default_rng(2024)
+    finite = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], np.uint8)
+    codes = [rng.integers(0, 2**32, s, dtype=np.uint64).astype(np.uint32) for s in [(I, H // 8), (I, H // 8), (H, I // 8)]]
+    scales = [rng.choice(finite, s) for s in [(I, H // 16), (I, H // 16), (H, I // 16)]]
+    scales[0].flat[:254] = finite  # every finite byte at least once
+    scales[2].flat[:8] = np.arange(8, dtype=np.uint8)  # zero and the subnormals
+    units = []
+    for g in ([1000.5, 2688.0 * 1.75, 37.0], [5000.0, 0.03125, 2688.0 * 0.6]):
+        rec = oracle.pack_record(H, I, codes, scales, np.array(g, np.float32))
+        units.append([oracle.dequant_projection(rec, H, I, p)[1] for p in range(3)])
+    for p in range(3):
+        out, in_ = oracle.proj_shape(H, I, p)
+        for r in range(out):
+            want = _unit_want(codes[p][r], scales[p][r], in_)
+            assert np.array_equal(units[0][p][r], want), (p, r)
+        assert np.array_equal(units[0][p], units[1][p]), p
