@@ -47,6 +47,14 @@ extern "C" {
 
 enum { MOE_GATE = 0, MOE_UP = 1, MOE_DOWN = 2 };
 
+/* The status word of a forward / layer workspace: the 32-bit word at byte
+ * offset MOE_STATUS_OFFSET. Kernels only ever set its bits; the library never
+ * clears them (moe_status_clear does, when the caller asks), so a caller that
+ * checks the word clears it before the calls it wants to cover. */
+#define MOE_STATUS_OFFSET 8
+#define MOE_STATUS_ROUTE_TIMEOUT 1u /* moe_nvfp4_layer, one token: the wait for the router expired */
+#define MOE_STATUS_BAD_IDX 2u       /* moe_nvfp4_forward: a pair named an expert outside [0, E) */
+
 /* Message for the last error on the calling thread ("" if none). */
 const char* moe_last_error(void);
 
@@ -173,7 +181,10 @@ int moe_sort_pairs_ws(const int32_t* idx, int T, int k, int E, int32_t* offsets,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* S3..S7, the layer (shape rules: H and I multiples of 64, T >= 0,
- * 1 <= k <= min(E, 64)):
+ * 1 <= k <= min(E, 64); a bank accepts multiples of 16, but every layer
+ * kernel walks a weight row in 64-input quads of four E4M3 blocks, 32 bytes
+ * of codes and 4 scale bytes per load, so a row that ends inside a quad is
+ * rejected with MOE_ESHAPE rather than read past its end):
  *   y[t] = residual[t] + sum_j w[t][j] * down_e( bf16( silu(gate_e x[t]) * up_e x[t] ) )
  * with e = idx[t][j], each projection dequantized by the [PACK] global-scales
  * rule (weight = e2m1 * f32(e4m3 * f32(g / 2688))), f32 accumulation, FP32
@@ -184,7 +195,11 @@ int moe_sort_pairs_ws(const int32_t* idx, int T, int k, int E, int32_t* offsets,
  * MFMA) kernels for large T*k; flags can force either.
  * workspace: device, >= moe_nvfp4_workspace_bytes(T, k, H, I, E) bytes,
  * 256-byte aligned, not shared with a concurrent call. idx values outside
- * [0, E) are a caller error (those pairs contribute nothing). */
+ * [0, E) are a caller error: those pairs contribute nothing, and the kernels
+ * set MOE_STATUS_BAD_IDX in the workspace's status word (the call itself
+ * returns MOE_OK: the values are only seen on the device). Prefills of more
+ * than 2 GiB of activations (T * H * 2 bytes) run as several passes over
+ * token chunks, with the same results. */
 size_t moe_nvfp4_workspace_bytes(int T, int k, int H, int I, int E);
 int moe_nvfp4_forward(const moe_nvfp4_bank* b, const uint16_t* x, int T, const int32_t* idx,
                       const float* w, int k, const uint16_t* residual, void* y, unsigned flags,
@@ -203,15 +218,23 @@ int moe_nvfp4_forward(const moe_nvfp4_bank* b, const uint16_t* x, int T, const i
  * 64-bit tags stamped with a per-call number, so the workspace needs no
  * clearing between calls, must not be shared by calls that can overlap, and
  * a region never written by this library matches a call number with
- * probability 2^-32 per tag. The wait for the tags is bounded; if it ever
- * expires (it does not in a correct launch), bit 0 of the 32-bit word at byte
- * offset 8 of the workspace is set (a caller that checks it clears it first;
- * the library never clears it), idx holds -1 and the call's outputs are
- * invalid. Otherwise the call runs the router, top-k and forward launches in
- * order. */
+ * probability 2^-32 per tag. The wait for the tags is bounded (about 0.1 s);
+ * if it ever expires (it does not in a correct launch), MOE_STATUS_ROUTE_TIMEOUT
+ * is set in the workspace's status word, idx holds -1, w holds 0 and y holds
+ * the residual (or 0): the call's routing is lost and it returns MOE_OK,
+ * so a caller that must know checks the status word. (The environment
+ * variable MOE_DEBUG_ROUTE_GIVEUP=1 forces this path, for tests.) Otherwise
+ * the call runs the router, top-k and forward launches in order. */
 int moe_nvfp4_layer(const moe_nvfp4_bank* b, const uint16_t* x, const float* w_router, int T, int k,
                     const uint16_t* residual, float* logits, int32_t* idx, float* w, void* y,
                     unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The status word of `workspace` (256-byte aligned): moe_status_read waits for
+ * `stream` and copies the word into *status (host); moe_status_clear enqueues
+ * a store of 0 on `stream` (a kernel, not a memset, so it may be captured in
+ * a graph). Errors: MOE_EINVAL (null), MOE_EALIGN, MOE_EHIP. */
+int moe_status_read(const void* workspace, uint32_t* status, void* stream);
+int moe_status_clear(void* workspace, void* stream);
 
 /* S8, resident linear in MLX affine 8-bit, group 64 ([PACK] residents and
  * q8-rule bullets): y[t][n] = sum_k x[t][k] * (scale[n][k/64]*q[n][k] +
@@ -280,13 +303,27 @@ int moe_vq_forward(const moe_vq_bank* b, const uint16_t* x, int T, const int32_t
                    const uint16_t* residual, void* y, unsigned flags, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* Achievable-peak probes, the measured denominators beside the data-sheet
+ * peaks of the rooflines (measurement only; no step of the layer uses them).
+ * moe_probe_hbm_read: reads nbytes (a multiple of 16) at buf (device,
+ * 16-byte aligned) once, with `blocks` workgroups of 256 threads in
+ * grid-stride order, 16-byte loads, 4 (variant 0, 2) or 8 (1, 3) in flight per
+ * thread, nontemporal in variants 2 and 3. moe_probe_mfma_bf16: `blocks`
+ * workgroups of 4 waves, each wave 4 independent chains of `iters`
+ * v_mfma_f32_32x32x16_bf16 (32,768 flop each) on register operands. sink:
+ * device, `blocks` words, which the probes do not write for real data (they
+ * only keep the compiler from dropping the work). Errors: MOE_EINVAL,
+ * MOE_EALIGN, MOE_EHIP. */
+int moe_probe_hbm_read(const void* buf, size_t nbytes, int variant, int blocks, uint32_t* sink, void* stream);
+int moe_probe_mfma_bf16(int blocks, int iters, float* sink, void* stream);
+
 /* Kernel timing with HIP events that hipExtLaunchKernel records at each
  * kernel's own start and end on its stream. moe_profile_enable(1) clears and
  * starts collection; moe_profile_read(name, ...) synchronizes the events and
  * returns the summed duration and count of the kernel family `name` since the
  * last enable. Names: "router", "topk", "sort", "decode_gateup", "decode_down",
  * "combine", "prefill_gateup", "prefill_down", "affine8", "rmsnorm", "sha256",
- * "vq_gateup", "vq_down", "vq_dequant". */
+ * "vq_gateup", "vq_down", "vq_dequant", "probe_hbm_read", "probe_mfma". */
 int moe_profile_enable(int on);
 int moe_profile_read(const char* name, double* total_ms, int64_t* launches);
 

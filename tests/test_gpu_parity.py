@@ -615,7 +615,7 @@ def gpu_layer(bank, x_bits, Wr, k, flags=0, residual=None, ws=None):
     E = Wr.shape[0]
     if ws is None:
         ws = wq.workspace(wq.moe_nvfp4_workspace_bytes(T, k, bank.H, bank.I, bank.E))
-    ws.view(torch.int32)[2] = 0  # the status word: set only if a bounded wait expires
+    wq.moe_status_clear(ws)  # the status word: set only if a bounded wait expires
     xd = bf16_tensor(x_bits)
     wrd = torch.from_numpy(np.ascontiguousarray(Wr)).to(DEV)
     rd = None if residual is None else bf16_tensor(residual)
@@ -627,7 +627,7 @@ def gpu_layer(bank, x_bits, Wr, k, flags=0, residual=None, ws=None):
     wq.moe_nvfp4_layer(bank, xd, wrd, T, k, rd, lg, idx, w, yf, flags | wq.MOE_F32_OUT, ws)
     wq.moe_nvfp4_layer(bank, xd, wrd, T, k, rd, lg, idx, w, yb, flags, ws)
     torch.cuda.synchronize()
-    status = int(ws.view(torch.int32)[2].item())
+    status = wq.moe_status_read(ws)
     return lg.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy(), yf.cpu().numpy(), to_np_bits(yb), status
 
 
@@ -680,17 +680,18 @@ def test_layer_call_decode_full_shape(big_bank):
         check_f32(yf, ref_f, f"layer call decode v{variant}")
 
 
-def test_forward_batched_full_shape_sampled(big_bank):
+def test_forward_batched_full_shape(big_bank):
+    # the batched-decode workload, every one of its 32 tokens against the oracle
     bank, _ = big_bank
     c = W.CONFIGS["batched"]
     x, _, logits = W.inputs("batched")
     idx, w = oracle.route_topk(logits, c["k"])
     yf, yb = gpu_forward(bank, x, idx, w, c["k"])
-    sample = [0, 13, 31]
-    recs = host_records(c["bank_seed"], np.unique(idx[sample]), c["H"], c["I"])
-    ref_f, _ = oracle.moe_forward(recs, c["E"], c["H"], c["I"], x[sample], idx[sample], w[sample])
-    check_f32(yf[sample], ref_f, "batched sampled")
-    check_bf16_of(yb[sample], yf[sample], "batched bf16")
+    recs = host_records(c["bank_seed"], np.unique(idx), c["H"], c["I"])
+    say(f"batched: {len(recs)} distinct experts, all {c['T']} tokens")
+    ref_f, _ = oracle.moe_forward(recs, c["E"], c["H"], c["I"], x, idx, w)
+    check_f32(yf, ref_f, "batched T=32")
+    check_bf16_of(yb, yf, "batched bf16")
 
 
 def test_forward_routed_gemv_full_shape(big_bank):
@@ -757,26 +758,140 @@ def test_routed_gemv_inblock_routing_matches_tables(big_bank, monkeypatch):
     say(f"routed GEMV T={T}: in-block routing matches the sort tables bit for bit")
 
 
-def test_forward_prefill_full_shape_sampled(big_bank):
+def prefill_sample_tokens(idx, E, k, n=512, seed=3):
+    """Tokens whose pairs sit at the grouped GEMM's tile edges, then seeded
+    random tokens up to n. Slots are the stable sort of the pairs by expert;
+    an expert's slots form tiles of 128 rows, and a tile holds 1 to 4 blocks
+    of 32 rows. For every block count, among full and partial (last) tiles,
+    the tokens of a tile's first and last rows and of the rows on each side of
+    a 32-row boundary are taken."""
+    P = idx.size
+    offs, srt = oracle.sort_pairs(idx.ravel(), E)
+    picks, by_class = [], {}
+    for e in range(E):
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        for r0 in range(lo, hi, 128):
+            rows = min(128, hi - r0)
+            key = ((rows + 31) // 32, rows == 128)
+            by_class.setdefault(key, []).append((r0, rows))
+    for key in sorted(by_class):
+        tiles = by_class[key]
+        for r0, rows in tiles[:: max(1, len(tiles) // 3)][:3]:
+            for r in sorted(set([0, rows - 1] + [b for b in (31, 32, 63, 64, 95, 96) if b < rows])):
+                picks.append(int(srt[r0 + r]) // k)
+    picks = list(dict.fromkeys(picks))
+    rng = np.random.default_rng(seed)
+    rest = [t for t in rng.permutation(P // k).tolist() if t not in set(picks)]
+    return np.array(sorted(picks + rest[: max(0, n - len(picks))])), sorted(by_class)
+
+
+def test_forward_prefill_full_shape(big_bank):
+    # The prefill workload (8192 tokens, 65,536 pairs on the grouped GEMM):
+    # 512 tokens against the oracle, chosen to cover tile edges of every
+    # 32-row-block count plus seeded random tokens; then all 8192 tokens
+    # against the routed GEMV on the same inputs (that path is itself held to
+    # the oracle), which covers every tile row and k step at full shape.
     bank, _ = big_bank
     c = W.CONFIGS["prefill"]
     x, _, logits = W.inputs("prefill")
     idx, w = oracle.route_topk(logits, c["k"])
-    say("prefill forward on the GPU")
+    say("prefill forward on the GPU (grouped GEMM)")
     yf, yb = gpu_forward(bank, x, idx, w, c["k"])
     assert np.isfinite(yf).all()
-    # sampled tokens: the first, the last, and tokens routed to the largest and
-    # the smallest expert groups (tile tails)
-    counts = np.bincount(idx.ravel(), minlength=c["E"])
-    big_e, small_e = int(np.argmax(counts)), int(np.argmin(counts))
-    t_big = int(np.nonzero((idx == big_e).any(axis=1))[0][-1])
-    t_small = int(np.nonzero((idx == small_e).any(axis=1))[0][-1])
-    sample = sorted(set([0, c["T"] - 1, t_big, t_small]))
-    say(f"prefill sample tokens {sample}")
+    sample, classes = prefill_sample_tokens(idx, c["E"], c["k"])
+    say(f"prefill oracle sample: {len(sample)} tokens, tile classes (32-row blocks, full) {classes}")
     recs = host_records(c["bank_seed"], np.unique(idx[sample]), c["H"], c["I"])
     ref_f, _ = oracle.moe_forward(recs, c["E"], c["H"], c["I"], x[sample], idx[sample], w[sample])
-    check_f32(yf[sample], ref_f, "prefill sampled")
-    check_bf16_of(yb[sample], yf[sample], "prefill bf16")
+    check_f32(yf[sample], ref_f, f"prefill {len(sample)} tokens vs oracle")
+    check_bf16_of(yb, yf, "prefill bf16, all tokens")
+    say("prefill forward on the GPU (routed GEMV, forced)")
+    gf, _ = gpu_forward(bank, x, idx, w, c["k"], wq.MOE_FORCE_DECODE)
+    # Two f32 paths round some bf16 mids differently (their gate/up sums
+    # differ in the last bits), and a mid that rounds the other way moves a
+    # whole output row by one bf16 ulp of that mid times the down weights: the
+    # paths agree to the layer tolerance in L2, element by element within twice
+    # the per-element bound, and the tokens where they differ most are held to
+    # the oracle on both paths.
+    rms = np.sqrt(np.mean(gf.astype(np.float64) ** 2))
+    diff = np.abs(yf.astype(np.float64) - gf)
+    rel = np.linalg.norm(diff) / np.linalg.norm(gf.astype(np.float64))
+    worst = np.argsort(diff.max(axis=1))[-16:]
+    say(f"grouped GEMM vs routed GEMV, all tokens: rel L2 {rel:.3e}, max |diff|/rms {diff.max() / rms:.3e}, "
+        f"worst tokens {sorted(worst.tolist())}")
+    assert rel <= 5e-3 and diff.max() <= 2e-2 * rms
+    recs = host_records(c["bank_seed"], np.unique(idx[worst]), c["H"], c["I"])
+    ref_w, _ = oracle.moe_forward(recs, c["E"], c["H"], c["I"], x[worst], idx[worst], w[worst])
+    check_f32(yf[worst], ref_w, "grouped GEMM, 16 most-disagreeing tokens vs oracle")
+    check_f32(gf[worst], ref_w, "routed GEMV, 16 most-disagreeing tokens vs oracle")
+
+
+def test_status_flags_expert_outside_range(tiny_bank):
+    # The runtime rule for idx: an expert outside [0, E) is a caller error;
+    # the pair contributes nothing and the kernels set MOE_STATUS_BAD_IDX in
+    # the workspace's status word, on each path (one-item-per-wave kernels,
+    # routed GEMV, grouped GEMM). Valid calls leave the word at 0.
+    bank, _ = tiny_bank
+    c = W.CONFIGS["tiny"]
+    H, I, E, k = c["H"], c["I"], c["E"], c["k"]
+    recs = host_records(c["bank_seed"], range(E), H, I)
+    for T, flags in [(3, 0), (20, 2), (40, 4)]:
+        x = synth.activations(500 + T, T, H)
+        lg = np.random.default_rng(T).normal(size=(T, E)).astype(np.float32)
+        idx, w = oracle.route_topk(lg, k)
+        ws = wq.workspace(wq.moe_nvfp4_workspace_bytes(T, k, H, I, E))
+        xd = bf16_tensor(x)
+        yf = torch.empty((T, H), dtype=torch.float32, device=DEV)
+        wd = torch.from_numpy(w).to(DEV)
+        wq.moe_nvfp4_forward(bank, xd, T, torch.from_numpy(idx).to(DEV), wd, k, None, yf, flags | wq.MOE_F32_OUT, ws)
+        assert wq.moe_status_read(ws) == 0, (T, flags)
+        bad = idx.copy()
+        bad[0, 1], bad[T - 1, 0] = E, -7  # one past the end, and negative
+        wq.moe_nvfp4_forward(bank, xd, T, torch.from_numpy(bad).to(DEV), wd, k, None, yf, flags | wq.MOE_F32_OUT, ws)
+        st = wq.moe_status_read(ws)
+        assert st == wq.MOE_STATUS_BAD_IDX, (T, flags, st)
+        # the oracle without those pairs: same experts, routing weight 0
+        w0 = w.copy()
+        w0[0, 1] = w0[T - 1, 0] = 0.0
+        ref_f, _ = oracle.moe_forward(recs, E, H, I, x, idx, w0)
+        check_f32(yf.cpu().numpy(), ref_f, f"bad idx T={T} flags={flags}")
+        wq.moe_status_clear(ws)
+        assert wq.moe_status_read(ws) == 0
+
+
+def test_layer_route_giveup_contract(tiny_bank, monkeypatch):
+    # The one-token layer's bounded wait, forced to give up from the host
+    # (MOE_DEBUG_ROUTE_GIVEUP: the router workgroups withhold their logits and
+    # the waits stop after a few polls; every kernel ends normally): the
+    # status word has MOE_STATUS_ROUTE_TIMEOUT, idx is -1, w is 0 and y is the
+    # residual. The same workspace then serves a normal call.
+    bank, _ = tiny_bank
+    c = W.CONFIGS["tiny"]
+    H, E = c["H"], c["E"]
+    x, Wr, _ = W.inputs("tiny")
+    x1 = x[:1]
+    res = synth.activations(606, 1, H)
+    ws = wq.workspace(wq.moe_nvfp4_workspace_bytes(1, 2, bank.H, bank.I, bank.E))
+    xd, rd = bf16_tensor(x1), bf16_tensor(res)
+    wrd = torch.from_numpy(np.ascontiguousarray(Wr)).to(DEV)
+    lg = torch.empty((1, E), dtype=torch.float32, device=DEV)
+    idx = torch.zeros((1, 2), dtype=torch.int32, device=DEV)
+    w = torch.ones((1, 2), dtype=torch.float32, device=DEV)
+    yf = torch.empty((1, H), dtype=torch.float32, device=DEV)
+    yb = torch.empty((1, H), dtype=torch.int16, device=DEV)
+    monkeypatch.setenv("MOE_DEBUG_ROUTE_GIVEUP", "1")
+    wq.moe_nvfp4_layer(bank, xd, wrd, 1, 2, rd, lg, idx, w, yf, wq.MOE_F32_OUT, ws)
+    wq.moe_nvfp4_layer(bank, xd, wrd, 1, 2, rd, lg, idx, w, yb, 0, ws)
+    st = wq.moe_status_read(ws)
+    monkeypatch.delenv("MOE_DEBUG_ROUTE_GIVEUP")
+    assert st == wq.MOE_STATUS_ROUTE_TIMEOUT, st
+    assert idx.cpu().numpy().tolist() == [[-1, -1]]
+    assert w.cpu().numpy().tolist() == [[0.0, 0.0]]
+    rv = oracle.bf16_to_f32(res).astype(np.float32)
+    assert np.array_equal(yf.cpu().numpy(), rv)
+    assert np.array_equal(oracle.bf16_to_f32(to_np_bits(yb)), rv)
+    say("layer give-up: status, idx, w and y as documented")
+    wq.moe_status_clear(ws)
+    check_layer_call(bank, "tiny after a give-up", x1, Wr, 2, residual=res, ws=ws)
 
 
 def test_forward_deterministic(big_bank):

@@ -221,3 +221,29 @@ def test_vq_sizes_and_validation():
     assert f(T=0) == wq.MOE_OK
     assert L.moe_vq_dequant(C.byref(b), 256, 0, fake, None) == wq.MOE_EINVAL
     assert L.moe_vq_dequant(C.byref(b), 0, 3, fake, None) == wq.MOE_EINVAL
+
+
+def test_layer_shapes_off_the_quad_grid_rejected():
+    # A bank takes rows of any multiple of 16 inputs, the layer kernels walk
+    # rows in 64-input quads: H or I of 16 * odd are refused before a launch.
+    L = wq.lib()
+    fake = C.c_void_p(1 << 26)
+    for H, I in [(208, 112), (16 * 13, 128), (256, 16 * 9), (48, 64)]:
+        b = wq.moe_nvfp4_bank()
+        assert L.moe_nvfp4_bank_init(C.byref(b), C.c_void_p(1 << 24), H, I, 16) == wq.MOE_OK
+        need = L.moe_nvfp4_workspace_bytes(4, 2, H, I, 16)
+        rc = L.moe_nvfp4_forward(C.byref(b), fake, 4, fake, fake, 2, None, fake, 0, fake, need, None)
+        assert rc == wq.MOE_ESHAPE and b"multiples of 64" in L.moe_last_error()
+        rc = L.moe_nvfp4_layer(C.byref(b), fake, fake, 1, 2, None, fake, fake, fake, fake, 0, fake, need, None)
+        assert rc == wq.MOE_ESHAPE
+
+
+def test_status_word_calls_validate():
+    L = wq.lib()
+    v = C.c_uint32()
+    assert L.moe_status_read(None, C.byref(v), None) == wq.MOE_EINVAL
+    assert L.moe_status_read(C.c_void_p(1 << 26), None, None) == wq.MOE_EINVAL
+    assert L.moe_status_read(C.c_void_p((1 << 26) + 64), C.byref(v), None) == wq.MOE_EALIGN
+    assert L.moe_status_clear(None, None) == wq.MOE_EINVAL
+    assert L.moe_status_clear(C.c_void_p((1 << 26) + 8), None) == wq.MOE_EALIGN
+    assert wq.MOE_STATUS_OFFSET == 8 and (wq.MOE_STATUS_ROUTE_TIMEOUT, wq.MOE_STATUS_BAD_IDX) == (1, 2)

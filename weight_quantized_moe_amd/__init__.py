@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4, -5
 MOE_F32_OUT, MOE_FORCE_DECODE, MOE_FORCE_PREFILL = 1, 2, 4
 GATE, UP, DOWN = 0, 1, 2
+MOE_STATUS_OFFSET, MOE_STATUS_ROUTE_TIMEOUT, MOE_STATUS_BAD_IDX = 8, 1, 2
 
 EXPORTS = [
     "moe_last_error", "moe_nvfp4_record_bytes", "moe_nvfp4_record_stride", "moe_nvfp4_bank_init",
@@ -26,7 +27,8 @@ EXPORTS = [
     "moe_nvfp4_dequant", "moe_profile_enable", "moe_profile_read", "moe_nvfp4_global_from_ws2",
     "moe_nvfp4_record_sha256", "moe_cache_create", "moe_cache_destroy", "moe_cache_prepare", "moe_cache_bank",
     "moe_cache_stats", "moe_vq_record_bytes", "moe_vq_record_stride", "moe_vq_bank_init", "moe_vq_pack_bank",
-    "moe_vq_dequant", "moe_vq_workspace_bytes", "moe_vq_forward",
+    "moe_vq_dequant", "moe_vq_workspace_bytes", "moe_vq_forward", "moe_status_read", "moe_status_clear",
+    "moe_probe_hbm_read", "moe_probe_mfma_bf16",
 ]
 
 
@@ -119,6 +121,14 @@ def lib():
         L.moe_vq_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.moe_vq_forward.restype = i32
         L.moe_vq_forward.argtypes = [vqp, vp, i32, vp, vp, i32, vp, vp, C.c_uint, vp, sz, vp]
+        L.moe_status_read.restype = i32
+        L.moe_status_read.argtypes = [vp, C.POINTER(C.c_uint32), vp]
+        L.moe_status_clear.restype = i32
+        L.moe_status_clear.argtypes = [vp, vp]
+        L.moe_probe_hbm_read.restype = i32
+        L.moe_probe_hbm_read.argtypes = [vp, sz, i32, i32, vp, vp]
+        L.moe_probe_mfma_bf16.restype = i32
+        L.moe_probe_mfma_bf16.argtypes = [i32, i32, vp, vp]
         L.moe_profile_enable.restype = i32
         L.moe_profile_enable.argtypes = [i32]
         L.moe_profile_read.restype = i32
@@ -327,6 +337,14 @@ def moe_vq_forward(bank, x, T, idx, w, k, residual, y, flags, ws, stream=None):
                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def moe_probe_hbm_read(buf, nbytes, variant, blocks, sink, stream=None):
+    _check(lib().moe_probe_hbm_read(_ptr(buf), nbytes, variant, blocks, _ptr(sink), _stream(stream)))
+
+
+def moe_probe_mfma_bf16(blocks, iters, sink, stream=None):
+    _check(lib().moe_probe_mfma_bf16(blocks, iters, _ptr(sink), _stream(stream)))
+
+
 def moe_profile_enable(on):
     _check(lib().moe_profile_enable(1 if on else 0))
 
@@ -337,8 +355,21 @@ def moe_profile_read(name):
     return ms.value, n.value
 
 
+def moe_status_read(workspace, stream=None):
+    """The workspace's status word (waits for the stream)."""
+    v = C.c_uint32()
+    _check(lib().moe_status_read(_ptr(workspace), C.byref(v), _stream(stream)))
+    return v.value
+
+
+def moe_status_clear(workspace, stream=None):
+    _check(lib().moe_status_clear(_ptr(workspace), _stream(stream)))
+
+
 def workspace(nbytes, device="cuda"):
-    """A 256-byte aligned device workspace of at least nbytes (torch allocations are)."""
+    """A 256-byte aligned device workspace of at least nbytes (torch allocations
+    are), its status word cleared."""
     t = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
     assert t.data_ptr() % 256 == 0
+    moe_status_clear(t)
     return t

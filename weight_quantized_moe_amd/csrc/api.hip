@@ -5,6 +5,7 @@
 
 #include <unistd.h>
 
+#include <algorithm>
 #include <atomic>
 #include <chrono>
 #include <cstdarg>
@@ -449,7 +450,8 @@ struct FwdLayout {
   int max_tiles;
 };
 // counts area (256 bytes): [0] active experts, [1] tiles (pair sort),
-// [2] status word of the layer entry point
+// [2] the status word (byte offset MOE_STATUS_OFFSET)
+static_assert(MOE_STATUS_OFFSET == 8, "status word is counts[2]");
 
 static FwdLayout fwd_layout(int T, int k, int H, int I, int E) {
   FwdLayout L{};
@@ -577,6 +579,12 @@ static bool flat_path(const BankView& v, int T, int k, unsigned flags) {
          (size_t)k * v.I * 2 <= 65536 && v.I % 16 == 0;
 }
 
+// The grouped-GEMM kernels address activation rows with 32-bit byte offsets
+// from one base, so a prefill runs over token chunks whose activations span
+// at most 2 GiB (209,715 tokens at H = 5120); each chunk is a forward of its
+// own (rows of y depend only on their own tokens).
+static long long prefill_chunk_tokens(int H) { return (1LL << 31) / (2LL * H); }
+
 static int forward_run(const BankView& v, const uint16_t* x, int T, const int32_t* idx, const float* w, int k,
                        const uint16_t* residual, void* y, unsigned flags, uint8_t* ws, const FwdLayout& L,
                        hipStream_t s) {
@@ -589,6 +597,7 @@ static int forward_run(const BankView& v, const uint16_t* x, int T, const int32_
   rt.tile_expert = reinterpret_cast<int32_t*>(ws + L.tile_e);
   rt.tile_row0 = reinterpret_cast<int32_t*>(ws + L.tile_r);
   rt.hist = reinterpret_cast<int32_t*>(ws + L.hist);
+  rt.status = reinterpret_cast<uint32_t*>(ws + L.counts) + 2;
   uint16_t* mid = reinterpret_cast<uint16_t*>(ws + L.mid);
   float* part = reinterpret_cast<float*>(ws + L.part);
   const int P = T * k;
@@ -597,35 +606,46 @@ static int forward_run(const BankView& v, const uint16_t* x, int T, const int32_
   if (flags & MOE_FORCE_PREFILL) prefill = true;
   const bool f32_out = (flags & MOE_F32_OUT) != 0;
   if (!prefill && flat_path(v, T, k, flags))
-    return hip_check(launch_flat_decode(v, x, T, idx, w, k, residual, mid, y, f32_out, s), "decode");
+    return hip_check(launch_flat_decode(v, x, T, idx, w, k, residual, mid, y, f32_out, rt.status, s), "decode");
 
   if (prefill) {
-    rc = hip_check(launch_sort(idx, P, v.E, rt, kPrefillMTile, L.max_tiles, s), "sort");
-    if (rc) return rc;
-    rc = hip_check(launch_prefill_gateup(v, x, k, rt, L.max_tiles, mid, s), "prefill gate/up");
-    if (rc) return rc;
-    rc = hip_check(launch_prefill_down(v, mid, w, k, rt, L.max_tiles, part, s), "prefill down");
-    if (rc) return rc;
-  } else {
-    // few pairs: the GEMV blocks take their expert and its pairs from the
-    // sorted tables (one small sort launch). Routing inside every block
-    // (env MOE_GEMV_INBLOCK=1, up to kDecInblockMaxP pairs) saves the launch
-    // but measured slower: 1.01 against 0.88 ms at T = 32, k = 8.
-    const bool inblock = gemv_inblock() && P <= kDecInblockMaxP;
-    if (!inblock) {
-      rc = hip_check(launch_sort(idx, P, v.E, rt, 0, L.max_tiles, s), "sort");
+    const size_t ysize = f32_out ? 4 : 2;
+    const int tc_max = (int)std::min<long long>(T, prefill_chunk_tokens(v.H));
+    for (int t0 = 0; t0 < T; t0 += tc_max) {
+      const int tc = std::min(tc_max, T - t0), pc = tc * k;
+      const uint16_t* xc = x + (size_t)t0 * v.H;
+      const int32_t* ic = idx + (size_t)t0 * k;
+      const float* wc = w + (size_t)t0 * k;
+      const uint16_t* rc_res = residual ? residual + (size_t)t0 * v.H : nullptr;
+      void* yc = static_cast<uint8_t*>(y) + (size_t)t0 * v.H * ysize;
+      rc = hip_check(launch_sort(ic, pc, v.E, rt, kPrefillMTile, L.max_tiles, s), "sort");
+      if (rc) return rc;
+      rc = hip_check(launch_prefill_gateup(v, xc, k, rt, L.max_tiles, mid, s), "prefill gate/up");
+      if (rc) return rc;
+      rc = hip_check(launch_prefill_down(v, mid, wc, k, rt, L.max_tiles, part, s), "prefill down");
+      if (rc) return rc;
+      rc = hip_check(launch_combine(part, ic, v.E, tc, v.H, k, rc_res, yc, f32_out, s), "combine");
       if (rc) return rc;
     }
-    const RouteTables* rtp = inblock ? nullptr : &rt;
-    const int slots = P < v.E ? P : v.E;
-    const int max_m = T;  // top-k selects an expert at most once per token
-    rc = hip_check(launch_decode_gateup(v, x, idx, P, k, rtp, slots, max_m, mid, s), "decode gate/up");
-    if (rc) return rc;
-    rc = hip_check(launch_decode_down(v, mid, w, idx, P, k, rtp, slots, max_m, part, s), "decode down");
+    return MOE_OK;
+  }
+  // few pairs: the GEMV blocks take their expert and its pairs from the
+  // sorted tables (one small sort launch). Routing inside every block
+  // (env MOE_GEMV_INBLOCK=1, up to kDecInblockMaxP pairs) saves the launch
+  // but measured slower: 1.01 against 0.88 ms at T = 32, k = 8.
+  const bool inblock = gemv_inblock() && P <= kDecInblockMaxP;
+  if (!inblock) {
+    rc = hip_check(launch_sort(idx, P, v.E, rt, 0, L.max_tiles, s), "sort");
     if (rc) return rc;
   }
-  return hip_check(launch_combine(part, idx, v.E, T, v.H, k, residual, y, f32_out, s),
-                   "combine");
+  const RouteTables* rtp = inblock ? nullptr : &rt;
+  const int slots = P < v.E ? P : v.E;
+  const int max_m = T;  // top-k selects an expert at most once per token
+  rc = hip_check(launch_decode_gateup(v, x, idx, P, k, rtp, slots, max_m, mid, rt.status, s), "decode gate/up");
+  if (rc) return rc;
+  rc = hip_check(launch_decode_down(v, mid, w, idx, P, k, rtp, slots, max_m, part, s), "decode down");
+  if (rc) return rc;
+  return hip_check(launch_combine(part, idx, v.E, T, v.H, k, residual, y, f32_out, s), "combine");
 }
 
 MOE_API int moe_nvfp4_forward(const moe_nvfp4_bank* b, const uint16_t* x, int T, const int32_t* idx,
@@ -658,6 +678,15 @@ static uint32_t next_call_number() {
   return c;
 }
 
+// Read at each call: MOE_DEBUG_ROUTE_GIVEUP=1 makes the one-token layer's
+// router workgroups withhold their logits and the waits give up after a few
+// polls, so that a test can check the give-up contract (every kernel still
+// ends normally).
+static bool debug_route_giveup() {
+  const char* s = std::getenv("MOE_DEBUG_ROUTE_GIVEUP");
+  return s && *s && std::atoi(s) != 0;
+}
+
 MOE_API int moe_nvfp4_layer(const moe_nvfp4_bank* b, const uint16_t* x, const float* w_router, int T, int k,
                             const uint16_t* residual, float* logits, int32_t* idx, float* w, void* y,
                             unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
@@ -678,7 +707,7 @@ MOE_API int moe_nvfp4_layer(const moe_nvfp4_bank* b, const uint16_t* x, const fl
     uint32_t* status = reinterpret_cast<uint32_t*>(ws + L.counts) + 2;
     uint16_t* mid = reinterpret_cast<uint16_t*>(ws + L.mid);
     return hip_check(launch_flat_layer(v, x, w_router, k, residual, logits, idx, w, mid, tags, status,
-                                       next_call_number(), y, (flags & MOE_F32_OUT) != 0, s),
+                                       next_call_number(), y, (flags & MOE_F32_OUT) != 0, s, debug_route_giveup()),
                      "layer");
   }
   rc = hip_check(launch_router(x, w_router, logits, T, v.H, v.E, s), "router");
@@ -686,6 +715,31 @@ MOE_API int moe_nvfp4_layer(const moe_nvfp4_bank* b, const uint16_t* x, const fl
   rc = hip_check(launch_topk(logits, T, v.E, k, idx, w, s), "topk");
   if (rc) return rc;
   return forward_run(v, x, T, idx, w, k, residual, y, flags, ws, L, s);
+}
+
+// ---- the workspace status word --------------------------------------------------
+static_assert(MOE_STATUS_ROUTE_TIMEOUT == kStatusRouteTimeout && MOE_STATUS_BAD_IDX == kStatusBadIdx,
+              "status bits");
+
+MOE_API int moe_status_read(const void* workspace, uint32_t* status, void* stream) {
+  if (!workspace || !status) return fail(MOE_EINVAL, "status_read: null pointer");
+  if (!aligned(workspace, 256)) return fail(MOE_EALIGN, "status_read: workspace not 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  int rc = hip_check(hipMemcpyAsync(&v, static_cast<const uint8_t*>(workspace) + MOE_STATUS_OFFSET, 4,
+                                    hipMemcpyDeviceToHost, s), "status_read");
+  if (rc) return rc;
+  rc = hip_check(hipStreamSynchronize(s), "status_read");
+  if (rc) return rc;
+  *status = v;
+  return MOE_OK;
+}
+
+MOE_API int moe_status_clear(void* workspace, void* stream) {
+  if (!workspace) return fail(MOE_EINVAL, "status_clear: null workspace");
+  if (!aligned(workspace, 256)) return fail(MOE_EALIGN, "status_clear: workspace not 256-byte aligned");
+  uint32_t* p = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + MOE_STATUS_OFFSET);
+  return hip_check(launch_store_u32(p, 0u, static_cast<hipStream_t>(stream)), "status_clear");
 }
 
 // ---- S8 affine8_g64 --------------------------------------------------------------
@@ -737,6 +791,24 @@ MOE_API int moe_nvfp4_dequant(const moe_nvfp4_bank* b, int expert, int proj, flo
     return fail(MOE_EALIGN, "dequant: output alignment");
   return hip_check(launch_dequant(v, expert, proj, out_f32, out_unit, static_cast<hipStream_t>(stream)),
                    "dequant");
+}
+
+// ---- achievable-peak probes -----------------------------------------------------------
+MOE_API int moe_probe_hbm_read(const void* buf, size_t nbytes, int variant, int blocks, uint32_t* sink,
+                               void* stream) {
+  if (!buf || !sink) return fail(MOE_EINVAL, "probe_hbm_read: null pointer");
+  if (!aligned(buf, 16) || nbytes % 16) return fail(MOE_EALIGN, "probe_hbm_read: buf and nbytes must be 16-byte multiples");
+  if (variant < 0 || variant > 3 || blocks < 1 || blocks > (1 << 20))
+    return fail(MOE_EINVAL, "probe_hbm_read: variant %d outside [0, 3] or blocks %d outside [1, 2^20]", variant, blocks);
+  if (nbytes == 0) return MOE_OK;
+  return hip_check(launch_probe_hbm_read(buf, nbytes, variant, blocks, sink, static_cast<hipStream_t>(stream)),
+                   "probe_hbm_read");
+}
+
+MOE_API int moe_probe_mfma_bf16(int blocks, int iters, float* sink, void* stream) {
+  if (!sink) return fail(MOE_EINVAL, "probe_mfma_bf16: null sink");
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1) return fail(MOE_EINVAL, "probe_mfma_bf16: blocks %d, iters %d", blocks, iters);
+  return hip_check(launch_probe_mfma(blocks, iters, sink, static_cast<hipStream_t>(stream)), "probe_mfma_bf16");
 }
 
 // ---- timing --------------------------------------------------------------------------

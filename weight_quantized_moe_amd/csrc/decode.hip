@@ -44,13 +44,15 @@ struct DecodeArgs {
   RouteTables rt;       // sorted tables, or rt.active == nullptr: in-block routing
   uint16_t* mid;        // gate/up output [P][I] by pair id
   float* part;          // down output [P][H] by pair id
+  uint32_t* status;     // status word, or null
 };
 
 // In-block routing for P <= 256 pairs: finds the slot-th smallest expert id
 // present in idx and its pairs in ascending pair order (s_pairs). Returns
 // the pair count (0 if there are fewer than slot+1 distinct experts).
 // Block-uniform result; all threads call it.
-__device__ int route_in_block(const int32_t* idx, int P, int E, int slot, int* s_pairs, int* s_e) {
+__device__ int route_in_block(const int32_t* idx, int P, int E, int slot, int* s_pairs, int* s_e,
+                              uint32_t* status) {
   __shared__ uint32_t bits[32];  // E <= 1024
   __shared__ int wcount[kDecWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -60,6 +62,7 @@ __device__ int route_in_block(const int32_t* idx, int P, int E, int slot, int* s
   const int my = (tid < P) ? idx[tid] : -1;
   const bool valid = my >= 0 && my < E;
   if (valid) atomicOr(&bits[my >> 5], 1u << (my & 31));
+  if (tid < P && !valid && status && blockIdx.x == 0 && blockIdx.y == 0) atomicOr(status, kStatusBadIdx);
   __syncthreads();
   if (tid == 0) {
     int e = -1, seen = 0;
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(kDecThreads) void gemv_kernel(DecodeArgs a) {
   int e, M;
   const int* pairs;
   if (a.rt.active == nullptr) {
-    M = route_in_block(a.idx, a.P, a.E, blockIdx.y, s_pairs, &s_e);
+    M = route_in_block(a.idx, a.P, a.E, blockIdx.y, s_pairs, &s_e, a.status);
     e = s_e;
     pairs = s_pairs;
   } else {
@@ -153,8 +156,10 @@ __global__ __launch_bounds__(kDecThreads) void gemv_kernel(DecodeArgs a) {
 
   // The chunk's input rows go HBM -> LDS with no registers (one wave-wide
   // load per 1 KiB of a row). With one load step per wave (every row's quads
-  // in one batch, the usual case) the weights are loaded once, before the
-  // first chunk's rows, and stay in registers for every chunk: the rows and
+  // in one batch: down by default; gate/up loads one quad per step and so
+  // re-reads its rows, from the L2, for every chunk) the weights are loaded
+  // once, before the first chunk's rows, and stay in registers for every
+  // chunk: the rows and
   // the weights are in flight together and one wait covers both. Loads
   // complete in issue order, so nothing waited for between the weights and
   // the rows may be a load: the first chunk's row numbers are read before
@@ -313,10 +318,11 @@ static DecodeArgs make_args(const BankView& b, const int32_t* idx, int P, int k,
 
 hipError_t launch_decode_gateup(const BankView& b, const uint16_t* x, const int32_t* idx, int P, int k,
                                 const RouteTables* rt, int slots, int max_m, uint16_t* mid,
-                                hipStream_t s) {
+                                uint32_t* status, hipStream_t s) {
   DecodeArgs a = make_args(b, idx, P, k, rt);
   a.in = x;
   a.mid = mid;
+  a.status = status;
   return launch_gemv<2>(a, slots, max_m, s);
 }
 
@@ -352,6 +358,7 @@ struct FlatArgs {
   uint16_t* mid;            // [k][I]
   void* y;                  // [H] bf16 or f32
   int f32_out;
+  uint32_t* status;         // status word (kStatusBadIdx), or null
 };
 
 // n 16-byte pieces global -> LDS by the workgroup: the first U rounds of
@@ -449,7 +456,10 @@ __global__ __launch_bounds__(kDecThreads) void flat_gateup_kernel(FlatArgs a, in
   b.mid = a.mid + (size_t)t * a.k * a.I;
   if (threadIdx.x < a.k) {
     const int e = b.idx[threadIdx.x];
-    s_idx[threadIdx.x] = (e >= 0 && e < a.E) ? e : -1;
+    const bool ok = e >= 0 && e < a.E;
+    s_idx[threadIdx.x] = ok ? e : -1;
+    // the token's first workgroup reports an expert outside [0, E)
+    if (!ok && a.status && blockIdx.x == (unsigned)(t * bpt)) atomicOr(a.status, kStatusBadIdx);
   }
   flat_stage_x(b, xs);
   __syncthreads();
@@ -573,6 +583,8 @@ struct RouteFuse {
   uint64_t* route;    // [kFlatDecodeMaxK] workspace: the routing record
   uint32_t* status;   // workspace status word
   uint32_t call;      // this call's number
+  uint32_t spins;     // polls of one tag before the wait gives up
+  int publish;        // router workgroups store their tags (0 only to exercise the give-up path)
 };
 
 constexpr uint32_t kTagSpins = 1u << 20;
@@ -602,7 +614,7 @@ __global__ __launch_bounds__(kDecThreads) void flat_route_gateup_kernel(FlatArgs
     const float sw = wave_sum(router_thread_sum<kDecThreads>(r.wr + (size_t)e * H, a.x, H, tid));
     if (lane == 0) red[wave] = sw;
     __syncthreads();
-    if (tid == 0) st_tag(r.tags + e, r.call, __float_as_uint(((red[0] + red[1]) + red[2]) + red[3]));
+    if (tid == 0 && r.publish) st_tag(r.tags + e, r.call, __float_as_uint(((red[0] + red[1]) + red[2]) + red[3]));
     return;
   }
   const int blk = blockIdx.x - E, nblk = gridDim.x - E;
@@ -629,7 +641,7 @@ __global__ __launch_bounds__(kDecThreads) void flat_route_gateup_kernel(FlatArgs
       uint64_t v = ld_tag(r.tags + e);
       uint32_t n = 0;
       while ((uint32_t)(v >> 32) != r.call) {
-        if (++n > kTagSpins) {
+        if (++n > r.spins) {
           failed = 1;
           break;
         }
@@ -645,7 +657,7 @@ __global__ __launch_bounds__(kDecThreads) void flat_route_gateup_kernel(FlatArgs
         r.w[tid] = 0.0f;
         r.idx[tid] = -1;
       }
-      if (tid == 0) atomicOr(r.status, 1u);
+      if (tid == 0) atomicOr(r.status, kStatusRouteTimeout);
       return;
     }
     if (wave == 0) {
@@ -707,7 +719,7 @@ static int flat_blocks(int n_items) {
 }
 
 static FlatArgs flat_args(const BankView& b, const uint16_t* x, const int32_t* idx, const float* w, int k,
-                          const uint16_t* residual, uint16_t* mid, void* y, bool f32_out) {
+                          const uint16_t* residual, uint16_t* mid, void* y, bool f32_out, uint32_t* status) {
   FlatArgs a{};
   a.bank = b.base;
   a.stride = b.stride;
@@ -727,6 +739,7 @@ static FlatArgs flat_args(const BankView& b, const uint16_t* x, const int32_t* i
   a.mid = mid;
   a.y = y;
   a.f32_out = f32_out ? 1 : 0;
+  a.status = status;
   return a;
 }
 
@@ -738,8 +751,8 @@ static hipError_t launch_flat_down(const FlatArgs& a, int T, hipStream_t s) {
 
 hipError_t launch_flat_decode(const BankView& b, const uint16_t* x, int T, const int32_t* idx,
                               const float* w, int k, const uint16_t* residual, uint16_t* mid,
-                              void* y, bool f32_out, hipStream_t s) {
-  const FlatArgs a = flat_args(b, x, idx, w, k, residual, mid, y, f32_out);
+                              void* y, bool f32_out, uint32_t* status, hipStream_t s) {
+  const FlatArgs a = flat_args(b, x, idx, w, k, residual, mid, y, f32_out, status);
   const int groups = (b.I + 3) / 4;
   // one token may take the tuned block count; several take one item per wave
   const int bpt = T == 1 ? flat_blocks(k * groups) : k * groups / kDecWaves;
@@ -753,8 +766,9 @@ hipError_t launch_flat_decode(const BankView& b, const uint16_t* x, int T, const
 hipError_t launch_flat_layer(const BankView& b, const uint16_t* x, const float* wr, int k,
                              const uint16_t* residual, float* logits, int32_t* idx, float* w,
                              uint16_t* mid, uint64_t* tags, uint32_t* status, uint32_t call, void* y,
-                             bool f32_out, hipStream_t s) {
-  const FlatArgs a = flat_args(b, x, idx, w, k, residual, mid, y, f32_out);
+                             bool f32_out, hipStream_t s, bool debug_giveup) {
+  // (the one-token layer computes idx itself, so only its wait can set a bit)
+  const FlatArgs a = flat_args(b, x, idx, w, k, residual, mid, y, f32_out, nullptr);
   RouteFuse r{};
   r.wr = wr;
   r.logits = logits;
@@ -764,6 +778,11 @@ hipError_t launch_flat_layer(const BankView& b, const uint16_t* x, const float* 
   r.route = tags + 1024;
   r.status = status;
   r.call = call;
+  // debug_giveup: the router workgroups keep their logits to themselves and
+  // the waits give up after a few polls, so every gate/up workgroup takes
+  // the give-up path and every kernel still ends normally
+  r.spins = debug_giveup ? 64u : kTagSpins;
+  r.publish = debug_giveup ? 0 : 1;
   const int groups = (b.I + 3) / 4;
   const dim3 grid(b.E + flat_blocks(k * groups)), block(kDecThreads);
   const uint32_t lds = b.H * 2;

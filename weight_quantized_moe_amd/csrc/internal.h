@@ -17,6 +17,12 @@ struct BankView {
   int H, I, E;
 };
 
+// Bits of the forward's status word (a 32-bit word in the workspace): the
+// one-token layer's bounded wait for the router expired; a pair named an
+// expert outside [0, E). Kernels only set bits; the library never clears them.
+constexpr uint32_t kStatusRouteTimeout = 1u;
+constexpr uint32_t kStatusBadIdx = 2u;
+
 // Routing tables written by the pair sort into the forward's workspace.
 struct RouteTables {
   int32_t* offsets;     // [E+1] first sorted slot of each expert
@@ -26,6 +32,7 @@ struct RouteTables {
   int32_t* tile_expert; // [max_tiles] grouped-GEMM tiles: expert
   int32_t* tile_row0;   // [max_tiles] first sorted slot of the tile
   int32_t* hist;        // [sort_hist_ints(P, E)] scratch of the multi-workgroup sort, or null
+  uint32_t* status;     // status word (kStatusBadIdx set for a pair outside [0, E)), or null
 };
 
 // router: logits = x . Wr^T with Wr f32 [E][H]; one block per (expert, 8 tokens)
@@ -86,7 +93,7 @@ hipError_t launch_record_sha256(const uint8_t* base, uint64_t stride, uint64_t n
 constexpr int kDecInblockMaxP = 256;
 hipError_t launch_decode_gateup(const BankView& b, const uint16_t* x, const int32_t* idx, int P, int k,
                                 const RouteTables* rt, int slots, int max_m, uint16_t* mid,
-                                hipStream_t s);
+                                uint32_t* status, hipStream_t s);
 hipError_t launch_decode_down(const BankView& b, const uint16_t* mid, const float* w,
                               const int32_t* idx, int P, int k, const RouteTables* rt, int slots,
                               int max_m, float* part, hipStream_t s);
@@ -102,7 +109,7 @@ constexpr int kFlatDecodeMaxK = 16;
 constexpr int kFlatDecodeMaxT = 14;
 hipError_t launch_flat_decode(const BankView& b, const uint16_t* x, int T, const int32_t* idx,
                               const float* w, int k, const uint16_t* residual, uint16_t* mid,
-                              void* y, bool f32_out, hipStream_t s);
+                              void* y, bool f32_out, uint32_t* status, hipStream_t s);
 // router + top-k + gate/up in one launch, then down (T = 1, the same limits
 // as launch_flat_decode, E <= 1024): logits [E], idx [k] and w [k] are
 // written; tags [E] and status live in the workspace; call is this call's
@@ -111,7 +118,7 @@ hipError_t launch_flat_decode(const BankView& b, const uint16_t* x, int T, const
 hipError_t launch_flat_layer(const BankView& b, const uint16_t* x, const float* wr, int k,
                              const uint16_t* residual, float* logits, int32_t* idx, float* w,
                              uint16_t* mid, uint64_t* tags, uint32_t* status, uint32_t call, void* y,
-                             bool f32_out, hipStream_t s);
+                             bool f32_out, hipStream_t s, bool debug_giveup = false);
 // y[t] = residual[t] + sum_j part[t*k+j] (j ascending); pairs with idx
 // outside [0, E) contribute nothing
 hipError_t launch_combine(const float* part, const int32_t* idx, int E, int T, int H, int k,
@@ -125,6 +132,7 @@ hipError_t launch_prefill_down(const BankView& b, const uint16_t* mid, const flo
                                const RouteTables& rt, int max_tiles, float* part, hipStream_t s);
 
 // misc
+hipError_t launch_store_u32(uint32_t* p, uint32_t v, hipStream_t s);
 hipError_t launch_zero_tails(uint8_t* base, uint64_t stride, uint64_t record_bytes, int E,
                              hipStream_t s);
 hipError_t launch_dequant(const BankView& b, int expert, int proj, float* out_f32,
@@ -135,6 +143,14 @@ hipError_t launch_affine8(const uint16_t* x, const uint32_t* codes, const uint16
 // the same linear on bf16 MFMA for many tokens (x 16-byte aligned)
 hipError_t launch_affine8_gemm(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
                                const uint16_t* biases, int T, int K, int N, uint16_t* y, hipStream_t s);
+
+// achievable-peak probes (peak.hip): a streaming read of nbytes (a multiple of
+// 16, 16-byte aligned) in one of 4 load variants, and a bf16 MFMA loop of
+// blocks x 4 waves x iters x 4 instructions; sink: device scratch of `blocks`
+// words that a real run never writes
+hipError_t launch_probe_hbm_read(const void* buf, uint64_t nbytes, int variant, int blocks, uint32_t* sink,
+                                 hipStream_t s);
+hipError_t launch_probe_mfma(int blocks, int iters, float* sink, hipStream_t s);
 
 // kernel timing (api.hip)
 // Kernel timing (moe_profile_enable). When on, prof_events hands out a pair

@@ -27,6 +27,15 @@ hipError_t launch_zero_tails(uint8_t* base, uint64_t stride, uint64_t record_byt
   return hipGetLastError();
 }
 
+// ---- status word: cleared by a one-lane store (no memset node, so a caller
+// may capture it in a graph)
+__global__ void store_u32_kernel(uint32_t* p, uint32_t v) { *p = v; }
+
+hipError_t launch_store_u32(uint32_t* p, uint32_t v, hipStream_t s) {
+  hipLaunchKernelGGL(store_u32_kernel, dim3(1), dim3(1), 0, s, p, v);
+  return hipGetLastError();
+}
+
 // ---- dequant test export ("Beam 1.0 501B-A23B, streaming pack, NVFP4 experts /
 // MLX 8-bit residents", "What this pack holds", global-scales bullet):
 // w = e2m1 * f32(e4m3 * f32(g / 2688)), u = e2m1 * e4m3 (exact in bf16). The

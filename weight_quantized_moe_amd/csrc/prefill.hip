@@ -275,14 +275,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a)
     if (NPROJ == 2) {
       src_row[tid] = a.rt.sorted[row0 + r] / a.k;
     } else {
-      src_row[tid] = row0 + r;
+      src_row[tid] = r;  // mid rows counted from the tile's first slot (c.in)
       const int pair = a.rt.sorted[row0 + r];
       out_pair[tid] = pair;
       out_w[tid] = a.w[pair];
     }
   }
   TileCtx<NW> c;
-  c.in = uniform_ptr(a.in);
+  // A's base: gate/up the activations x (a token's row at its token id; the
+  // host keeps T * H * 2 below 2^31 bytes per launch), down the tile's first
+  // mid row, so the 32-bit per-lane offsets stay below 128 rows
+  c.in = uniform_ptr(NPROJ == 2 ? a.in : a.in + (size_t)row0 * K);
   c.rec = uniform_ptr(a.bank + (size_t)e * a.stride);
   float t_p[NPROJ];
 #pragma unroll

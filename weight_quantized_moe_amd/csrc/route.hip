@@ -154,7 +154,7 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, f
 // chunk's start + the same-expert pairs of the earlier waves of the chunk +
 // its rank among the earlier lanes of its wave. Counts use integer LDS
 // atomics (order-independent). Pairs with an expert outside [0, E) are
-// dropped.
+// dropped, and reported in the status word when the caller gives one.
 //
 // Few pairs: one workgroup counts, scans and places every chunk in order.
 // Many pairs (with a histogram buffer): three launches. sort_count_kernel
@@ -278,29 +278,41 @@ __global__ __launch_bounds__(kSortThreads) void sort_kernel(const int32_t* __res
     cnt[e] = 0;
     for (int wv = 0; wv < kSortWaves; wv++) wcnt[wv][e] = 0;
   }
+  __shared__ int bad;
+  if (tid == 0) bad = 0;
   __syncthreads();
   for (int p = tid; p < P; p += kSortThreads) {
     int e = idx[p];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    if (e >= 0 && e < E)
+      atomicAdd(&cnt[e], 1);
+    else
+      bad = 1;
   }
   __syncthreads();
+  if (tid == 0 && bad && rt.status) atomicOr(rt.status, kStatusBadIdx);
   sort_tables(cnt, cursor, E, rt, mtile, max_tiles);
   for (int p0 = 0; p0 < P; p0 += kSortThreads) sort_place_chunk(idx, p0, P, E, cursor, wcnt, rt.sorted);
 }
 
 // chunk b's count per expert -> hist[b][e]
 __global__ __launch_bounds__(kSortThreads) void sort_count_kernel(const int32_t* __restrict__ idx, int P, int E,
-                                                                  int32_t* __restrict__ hist) {
+                                                                  int32_t* __restrict__ hist, uint32_t* status) {
   __shared__ int cnt[kMaxE];
+  __shared__ int bad;
   const int tid = threadIdx.x, b = blockIdx.x;
   for (int e = tid; e < E; e += kSortThreads) cnt[e] = 0;
+  if (tid == 0) bad = 0;
   __syncthreads();
   const int p = b * kSortThreads + tid;
   if (p < P) {
     const int e = idx[p];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    if (e >= 0 && e < E)
+      atomicAdd(&cnt[e], 1);
+    else
+      bad = 1;
   }
   __syncthreads();
+  if (tid == 0 && bad && status) atomicOr(status, kStatusBadIdx);
   for (int e = tid; e < E; e += kSortThreads) hist[(size_t)b * E + e] = cnt[e];
 }
 
@@ -358,7 +370,7 @@ hipError_t launch_sort(const int32_t* idx, int P, int E, RouteTables rt, int mti
     launch_kernel("sort", sort_kernel, dim3(1), dim3(kSortThreads), 0, s, idx, P, E, rt, mtile, max_tiles);
     return hipGetLastError();
   }
-  launch_kernel("sort_count", sort_count_kernel, dim3(nb), dim3(kSortThreads), 0, s, idx, P, E, rt.hist);
+  launch_kernel("sort_count", sort_count_kernel, dim3(nb), dim3(kSortThreads), 0, s, idx, P, E, rt.hist, rt.status);
   launch_kernel("sort_scan", sort_scan_kernel, dim3(1), dim3(kSortThreads), 0, s, nb, E, rt.hist, rt, mtile,
                 max_tiles);
   launch_kernel("sort_place", sort_place_kernel, dim3(nb), dim3(kSortThreads), 0, s, idx, P, E,
