@@ -16,8 +16,18 @@ Second leg (prefill): T=8192 with Zipf(1.1)-skewed logits given, as TFLOP/s of
 roofline: the dominant kernel of each leg, its algorithmic bytes (flop) per
 launch over its mean launch time from HIP events recorded around each launch
 on the stream it runs on.
+step_us: median, p10 and p90 of per-step times (a separate pass with an event
+after every step). status: the workspace's status word after the timed
+passes (0, or the run stops: a routing wait that gave up or an expert id
+outside the bank would make the outputs invalid).
+peak_probes / roofline.peak_measured: what this GPU reaches in practice, a
+streaming read of HBM (1 GiB, and pieces of the decode step's 182 MB read in
+turn from a 4 GiB buffer) and a bf16 MFMA loop (moe_probe_*), reported beside
+the data-sheet peaks.
 cpu_baseline: the CPU oracle (as is) on a bounded sample of the decode
-workload, on this host's cores.
+workload, on this host's cores; `extra` times the tiny and decode workloads
+on one thread, the batched T=32 workload in full and the prefill workload on
+a 64-token sample (extrapolated to 8192 tokens).
 
 roofline.traffic: HBM bytes per launch of the dominant decode kernel, from
 rocprofv3 FETCH_SIZE + WRITE_SIZE counter runs scaled by what the same
@@ -53,7 +63,8 @@ the residual, T = 8; GB/s over the residents, routers and distinct records of
 all 12 layers (about 15.6 GB per step).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--prefill-steps P]
-       [--only decode|prefill|cache|vq|verify|affine8|batched|stacked] [--no-cpu-baseline] [--two-call]
+       [--only decode|prefill|cache|vq|verify|affine8|batched|stacked|peak] [--no-cpu-baseline]
+       [--no-probes] [--two-call]
 Profiling helpers: --copy-calibration (device copies of 1 GiB, for the
 counter scale factor); --summarize-pmc DIR (per-kernel mean counter values
 per dispatch from a rocprofv3 --pmc output directory; no GPU needed).
@@ -181,6 +192,79 @@ def timed(fn, steps, warmup):
     return e0.elapsed_time(e1), (time.perf_counter() - t0) * 1e3
 
 
+def step_stats(fn, steps):
+    """Per-step times (us) from an event recorded after every step on the
+    stream (a pass of its own: the events cost a little): median, p10, p90."""
+    s = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(s)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(s)
+    torch.cuda.synchronize()
+    d = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)])
+    return {"median": round(float(np.median(d)), 2), "p10": round(float(np.percentile(d, 10)), 2),
+            "p90": round(float(np.percentile(d, 90)), 2), "steps": steps}
+
+
+def check_status(ws, what):
+    """The layer's workspace status word after the timed passes: 0, or the run
+    is invalid (a routing wait that gave up, an expert outside the bank)."""
+    st = wq.moe_status_read(ws)
+    if st != 0:
+        raise SystemExit(f"{what}: workspace status word {st:#x} after the timed passes: outputs invalid")
+    return st
+
+
+def probe_peaks(fast=False):
+    """What this GPU reaches in practice: a streaming read of HBM (1 GiB, and
+    pieces of the decode step's size read in turn from a 4 GiB buffer, so the
+    256 MB Infinity Cache cannot serve them) and a bf16 MFMA loop in
+    back-to-back bursts of a few ms (the clock settles as under the prefill)."""
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s = torch.cuda.current_stream()
+
+    def time_ms(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        ev0.record(s)
+        for r in range(reps):
+            fn(r)
+        ev1.record(s)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / reps
+
+    buf = torch.ones(4 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1 << 20, dtype=torch.int32, device="cuda")
+    GiB = 1 << 30
+    rows = []
+    configs = [(v, b) for v in range(4) for b in ((2048, 8192) if fast else (1024, 2048, 4096, 8192))]
+    for v, b in configs:
+        ms = time_ms(lambda r=0: wq.moe_probe_hbm_read(buf[(r % 3) * GiB:], GiB, v, b, sink), 6)
+        rows.append({"variant": v, "blocks": b, "GBps": round(GiB / (ms * 1e-3) / 1e9, 1)})
+    best = max(rows, key=lambda r: r["GBps"])
+    piece = 182210656 // 16 * 16
+    n_pieces = (4 * GiB) // piece
+    ms = time_ms(lambda r=0: wq.moe_probe_hbm_read(buf[(r % n_pieces) * piece:], piece, best["variant"],
+                                                   best["blocks"], sink), 64)
+    piece_gbs = piece / (ms * 1e-3) / 1e9
+    del buf
+    fsink = torch.zeros(1 << 20, dtype=torch.float32, device="cuda")
+    blocks, iters = 2048, 4000
+    flop = blocks * 4 * 4 * iters * 32768
+    ms = time_ms(lambda r=0: wq.moe_probe_mfma_bf16(blocks, iters, fsink), 10)
+    mfma_tf = flop / (ms * 1e-3) / 1e12
+    log(f"probes: HBM read 1 GiB {best['GBps']:.0f} GB/s (variant {best['variant']}, {best['blocks']} blocks), "
+        f"{piece / 1e6:.0f} MB pieces {piece_gbs:.0f} GB/s; bf16 MFMA loop {mfma_tf:.0f} TFLOP/s ({ms:.2f} ms bursts)")
+    return {"hbm_read_1GiB_GBps": best["GBps"], "hbm_read_step_size_GBps": round(piece_gbs, 1),
+            "hbm_read_best": {"variant": best["variant"], "blocks": best["blocks"]},
+            "hbm_read_sweep": rows, "mfma_bf16_TFLOPs": round(mfma_tf, 1),
+            "mfma_burst_ms": round(ms, 3),
+            "note": "streaming read: 16-byte loads, grid-stride; MFMA: v_mfma_f32_32x32x16_bf16, register "
+                    "operands, 2048 workgroups of 4 waves, back-to-back bursts"}
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_gateup.txt")
 DECODE_SRC = os.path.join(ROOT, "weight_quantized_moe_amd", "csrc", "decode.hip")
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_T8192_counters.txt")
@@ -224,42 +308,131 @@ def summarize_pmc(d):
         print(f"{k[:70]:70s} {cname:12s} dispatches={len(disp[k]):4d} mean_per_dispatch={v / len(disp[k]):.6g}")
 
 
+def _omp_threads(n):
+    """Sets the OpenMP thread count of the oracle's parallel loops (libgomp's
+    own setter, on this thread); returns the previous count."""
+    import ctypes
+    gomp = ctypes.CDLL("libgomp.so.1")
+    prev = gomp.omp_get_max_threads()
+    gomp.omp_set_num_threads(int(n))
+    return prev
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(c, budget_s=20.0):
-    """The oracle, as it stands, on decode steps (router + top-k + layer), on
-    this host; as many steps as fit the time budget (at least one, at most 8)."""
+    """The oracle, as it stands, timed on this host: the headline is the decode
+    workload (router + top-k + layer, T=1) on all OpenMP threads, as many
+    steps as fit the budget (1 to 8). `extra` times the other layer workloads:
+    tiny and decode on one thread, batched T=32 in full, and prefill on a
+    seeded sample of 64 tokens (512 pairs) with the full layer extrapolated
+    linearly in tokens. Records are generated once (not timed)."""
     import oracle
 
     H, I, E, k = c["H"], c["I"], c["E"], c["k"]
-    _, Wr, _ = W.inputs("decode")
-    t_total, n, nbytes = 0.0, 0, 0
+    threads = _omp_threads(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    _omp_threads(threads)
+    rec_bytes = wq.moe_nvfp4_record_bytes(H, I)
+    t_gen = time.perf_counter()
     cache = {}
-    while n == 0 or t_total < budget_s:
-        x, _, _ = W.inputs("decode", n % ROTATE)
-        idx_probe, _ = oracle.route_topk(oracle.router_logits(x, Wr), k)
-        recs = {}
-        for e in np.unique(idx_probe):
+
+    def records(experts):
+        for e in experts:
             if int(e) not in cache:
                 cc, ss, gg = W.host_parts(c["bank_seed"], int(e), H, I)
                 cache[int(e)] = oracle.pack_record(H, I, cc, ss, gg)
-            recs[int(e)] = cache[int(e)]
+        return {int(e): cache[int(e)] for e in experts}
+
+    def decode_step(x, Wr):
+        idx_probe, _ = oracle.route_topk(oracle.router_logits(x, Wr), k)
+        recs = records(np.unique(idx_probe))
         t0 = time.perf_counter()
         lg = oracle.router_logits(x, Wr)
         idx, w = oracle.route_topk(lg, k)
         oracle.moe_forward(recs, E, H, I, x, idx, w)
-        t_total += time.perf_counter() - t0
-        nbytes += len(np.unique(idx)) * wq.moe_nvfp4_record_bytes(H, I) + H * E * 4 + 2 * H * 2
+        dt = time.perf_counter() - t0
+        return dt, len(np.unique(idx)) * rec_bytes + H * E * 4 + 2 * H * 2
+
+    _, Wr, _ = W.inputs("decode")
+    t_total, n, nbytes = 0.0, 0, 0
+    while n == 0 or t_total < budget_s:
+        dt, nb = decode_step(W.inputs("decode", n % ROTATE)[0], Wr)
+        t_total += dt
+        nbytes += nb
         n += 1
         if n >= 8:
             break
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} decode steps (T=1, router + top-8 + layer), {t_total:.1f} s, f64-accumulating C oracle"}
+    out = {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "cpu_model": _cpu_model(),
+           "sample": f"{n} decode steps (T=1, router + top-8 + layer), {t_total:.1f} s, f64-accumulating C oracle"}
+    extra = {}
+    # decode and tiny on one thread
+    _omp_threads(1)
+    dt, nb = decode_step(W.inputs("decode", 0)[0], Wr)
+    extra["decode_1thread"] = {"GBps": round(nb / dt / 1e9, 4), "s": round(dt, 2), "steps": 1}
+    ct = W.CONFIGS["tiny"]
+    xt, Wrt, _ = W.inputs("tiny")
+    rt = {}
+    for e in range(ct["E"]):
+        cc, ss, gg = W.host_parts(ct["bank_seed"], e, ct["H"], ct["I"])
+        rt[e] = oracle.pack_record(ct["H"], ct["I"], cc, ss, gg)
+    for thr in (1, threads):
+        _omp_threads(thr)
+        t0 = time.perf_counter()
+        reps = 20
+        for _ in range(reps):
+            lgt = oracle.router_logits(xt, Wrt)
+            it, wt = oracle.route_topk(lgt, ct["k"])
+            oracle.moe_forward(rt, ct["E"], ct["H"], ct["I"], xt, it, wt)
+        dt = (time.perf_counter() - t0) / reps
+        extra[f"tiny_{thr}thread"] = {"ms_per_step": round(dt * 1e3, 3), "steps": reps}
+    _omp_threads(threads)
+    # batched T=32 in full (logits given)
+    cb = W.CONFIGS["batched"]
+    xb, _, lgb = W.inputs("batched")
+    ib, wb = oracle.route_topk(lgb, k)
+    recs = records(np.unique(ib))
+    t0 = time.perf_counter()
+    ib, wb = oracle.route_topk(lgb, k)
+    oracle.moe_forward(recs, E, H, I, xb, ib, wb)
+    dt = time.perf_counter() - t0
+    nb = len(np.unique(ib)) * rec_bytes + 2 * cb["T"] * H * 2
+    extra["batched_T32"] = {"GBps": round(nb / dt / 1e9, 4), "s": round(dt, 2), "distinct_records": len(np.unique(ib))}
+    # prefill: top-k of all 8192 tokens, the layer on a seeded sample of 64
+    cp = W.CONFIGS["prefill"]
+    xp, _, lgp = W.inputs("prefill")
+    sample = np.sort(np.random.default_rng(cp["seed"]).choice(cp["T"], 64, replace=False))
+    ip_all, wp_all = oracle.route_topk(lgp, k)
+    recs = records(np.unique(ip_all[sample]))
+    t0 = time.perf_counter()
+    ip_all, wp_all = oracle.route_topk(lgp, k)
+    oracle.moe_forward(recs, E, H, I, xp[sample], ip_all[sample], wp_all[sample])
+    dt = time.perf_counter() - t0
+    flop = 2 * len(sample) * k * 3 * H * I
+    full_s = dt * cp["T"] / len(sample)
+    extra["prefill_sample"] = {"tokens": len(sample), "pairs": len(sample) * k, "s": round(dt, 2),
+                               "TFLOPs": round(flop / dt / 1e12, 6), "full_layer_s_extrapolated": round(full_s, 1),
+                               "basis": "sample time x 8192 / 64 (tokens); the sample's expert dequant is "
+                                        "counted once, so this overstates the full layer slightly"}
+    extra["wall_s_with_record_generation"] = round(time.perf_counter() - t_gen, 1)
+    out["extra"] = extra
+    return out
 
 
-def prefill_leg(bank, P):
+def prefill_leg(bank, P, peaks=None):
     pre = PrefillLeg(bank)
     pms, _ = timed(pre.step, P, 2)
     tflops = pre.flop / (pms / P * 1e-3) / 1e12
+    status = check_status(pre.ws, "prefill")
+    dist = step_stats(pre.step, P)
     wq.moe_profile_enable(True)
     for _ in range(P):
         pre.step()
@@ -272,7 +445,13 @@ def prefill_leg(bank, P):
     gu_flop = 2 * pre.c["T"] * pre.c["k"] * 2 * pre.c["H"] * pre.c["I"]
     gu_tf = gu_flop / (pk["prefill_gateup"][0] * 1e-3) / 1e12
     log(f"prefill: {pms / P:.3f} ms/step, {tflops:.1f} TFLOP/s")
+    roof_extra = {}
+    if peaks:
+        pm = peaks["mfma_bf16_TFLOPs"]
+        roof_extra = {"peak_measured": pm, "frac_measured": round(gu_tf / pm, 4),
+                      "peak_measured_by": "bf16 MFMA loop (moe_probe_mfma_bf16)"}
     return {"value": round(tflops, 2), "unit": "TFLOP/s", "steps": P, "ms_per_step": round(pms / P, 4),
+            "step_us": dist, "status": status,
             "workload": "prefill: T=8192, top-8 of 256 on Zipf(1.1)-skewed logits (given), "
                         "65,536 pairs, 5.154 TFLOP per step",
             "roofline": {"kernel": "prefill_gateup", "bound": "mfma", "achieved": round(gu_tf, 2),
@@ -280,7 +459,7 @@ def prefill_leg(bank, P):
                          "frac": round(gu_tf / BF16_PEAK_TFLOPS, 4),
                          "traffic": recorded_traffic("prefill_gateup", PREFILL_TRAFFIC_FILE, PREFILL_SRC),
                          "flop_per_launch": gu_flop,
-                         "avg_launch_ms": round(pk["prefill_gateup"][0], 4)},
+                         "avg_launch_ms": round(pk["prefill_gateup"][0], 4), **roof_extra},
             "kernels_us": {n_: round(v[0] * 1e3, 2) for n_, v in pk.items()}}
 
 
@@ -573,7 +752,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill", "cache", "vq", "verify", "affine8", "batched",
-                                       "stacked"])
+                                       "stacked", "peak"])
+    ap.add_argument("--no-probes", action="store_true", help="skip the achievable-peak probes")
     ap.add_argument("--two-call", action="store_true",
                     help="decode step as moe_route_topk + moe_nvfp4_forward instead of moe_nvfp4_layer")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -594,6 +774,9 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.only == "peak":
+        print(json.dumps({"peak": probe_peaks()}), flush=True)
+        return
     if args.only == "vq":
         print(json.dumps({"vq": vq_leg(args.steps, args.warmup)}), flush=True)
         return
@@ -608,8 +791,9 @@ def main():
     t0 = time.time()
     bank, base = W.build_bank(c["bank_seed"], c["H"], c["I"], c["E"])
     log(f"bank ready in {time.time() - t0:.1f} s")
+    peaks = None if args.no_probes or args.only in ("cache", "verify", "batched") else probe_peaks(fast=True)
     if args.only == "prefill":
-        print(json.dumps({"prefill": prefill_leg(bank, args.prefill_steps)}), flush=True)
+        print(json.dumps({"prefill": prefill_leg(bank, args.prefill_steps, peaks)}), flush=True)
         return
     if args.only == "cache":
         print(json.dumps({"expert_cache": cache_leg(bank, base)}), flush=True)
@@ -626,6 +810,7 @@ def main():
     dec.two_call = args.two_call
     K, Wm = args.steps, args.warmup
     ms_total, wall_ms = timed(dec.step, K, Wm)
+    status = check_status(dec.ws, "decode")
     dec.idx_host = dec.idx.cpu().numpy()
     first = (Wm) % ROTATE
     rs = [(first + i) % ROTATE for i in range(K)]
@@ -634,6 +819,8 @@ def main():
     value = step_bytes.sum() / (ms_total * 1e-3) / 1e9
     log(f"decode: {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s (wall {wall_ms / K * 1e3:.1f} us/step)")
 
+    dec.i = Wm
+    dist = step_stats(dec.step, K)
     # per-kernel times from events around each launch (a separate pass: the
     # events add a little launch overhead)
     wq.moe_profile_enable(True)
@@ -657,6 +844,10 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": recorded_traffic(gu_name),
                 "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(gu_ms * 1e3, 2)}
+    if peaks:
+        pm = peaks["hbm_read_step_size_GBps"]
+        roofline.update({"peak_measured": pm, "frac_measured": round(achieved / pm, 4),
+                         "peak_measured_by": "streaming read of 182 MB pieces (moe_probe_hbm_read)"})
 
     out = {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": Wm,
            "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
@@ -665,14 +856,16 @@ def main():
                                   "router f32 5120x256; 64 rotating activations",
                       "global_batch": 1, "H": 5120, "I": 2560, "E": 256, "top_k": 8,
                       "bytes_per_step": int(step_bytes.mean())},
-           "roofline": roofline,
+           "roofline": roofline, "step_us": dist, "status": status,
            "kernels_us": {n_: round(v[0] * 1e3, 2) for n_, v in kern.items()}}
+    if peaks:
+        out["peak_probes"] = peaks
 
     # ---- prefill leg
     if not args.no_prefill:
         del dec
         torch.cuda.empty_cache()
-        out["prefill"] = prefill_leg(bank, args.prefill_steps)
+        out["prefill"] = prefill_leg(bank, args.prefill_steps, peaks)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(c)
