@@ -205,6 +205,24 @@ int moe_nvfp4_forward(const moe_nvfp4_bank* b, const uint16_t* x, int T, const i
                       const float* w, int k, const uint16_t* residual, void* y, unsigned flags,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_nvfp4_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, rules and results as moe_nvfp4_forward, without
+ * the workspace: the scratch is a library-owned static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, held from the library's first
+ * use on that GPU until the process ends. A call whose
+ * moe_nvfp4_workspace_bytes(T, k, H, I, E) exceeds it returns MOE_EWORKSPACE
+ * before anything is enqueued (at H = 5120, I = 2560, k = 8: up to 163
+ * tokens). The call allocates nothing. All calls on one GPU share its array
+ * and each leaves its contents behind: calls that can overlap on one GPU (on
+ * different streams, or from several threads) race and must not be made.
+ * status (nullable): device u32 word into which the kernels OR the
+ * MOE_STATUS_* bits (4-byte aligned; the caller clears it). */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moe_nvfp4_forward_noalloc(const moe_nvfp4_bank* b, const uint16_t* x, int T, const int32_t* idx,
+                              const float* w, int k, const uint16_t* residual, void* y, unsigned flags,
+                              uint32_t* status, void* stream);
+
 /* S1..S7 in one call: the router, the top-k with its softmax and the layer,
  * i.e. moe_route_topk(x, w_router, logits, ...) followed by
  * moe_nvfp4_forward(..., idx, w, ...), with the same results: logits f32

@@ -19,6 +19,7 @@ MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2
 MOE_F32_OUT, MOE_FORCE_DECODE, MOE_FORCE_PREFILL = 1, 2, 4
 GATE, UP, DOWN = 0, 1, 2
 MOE_STATUS_OFFSET, MOE_STATUS_ROUTE_TIMEOUT, MOE_STATUS_BAD_IDX = 8, 1, 2
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 EXPORTS = [
     "moe_last_error", "moe_nvfp4_record_bytes", "moe_nvfp4_record_stride", "moe_nvfp4_bank_init",
@@ -28,7 +29,7 @@ EXPORTS = [
     "moe_nvfp4_record_sha256", "moe_cache_create", "moe_cache_destroy", "moe_cache_prepare", "moe_cache_bank",
     "moe_cache_stats", "moe_vq_record_bytes", "moe_vq_record_stride", "moe_vq_bank_init", "moe_vq_pack_bank",
     "moe_vq_dequant", "moe_vq_workspace_bytes", "moe_vq_forward", "moe_status_read", "moe_status_clear",
-    "moe_probe_hbm_read", "moe_probe_mfma_bf16",
+    "moe_probe_hbm_read", "moe_probe_mfma_bf16", "moe_nvfp4_forward_noalloc",
 ]
 
 
@@ -84,6 +85,8 @@ def lib():
         L.moe_nvfp4_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.moe_nvfp4_forward.restype = i32
         L.moe_nvfp4_forward.argtypes = [bankp, vp, i32, vp, vp, i32, vp, vp, C.c_uint, vp, sz, vp]
+        L.moe_nvfp4_forward_noalloc.restype = i32
+        L.moe_nvfp4_forward_noalloc.argtypes = [bankp, vp, i32, vp, vp, i32, vp, vp, C.c_uint, vp, vp]
         L.moe_nvfp4_layer.restype = i32
         L.moe_nvfp4_layer.argtypes = [bankp, vp, vp, i32, i32, vp, vp, vp, vp, vp, C.c_uint, vp, sz, vp]
         L.affine8_g64_linear.restype = i32
@@ -219,6 +222,11 @@ def moe_nvfp4_forward(bank, x, T, idx, w, k, residual, y, flags, workspace, stre
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().moe_nvfp4_forward(C.byref(bank), _ptr(x), T, _ptr(idx), _ptr(w), k, _ptr(residual), _ptr(y),
                                    flags, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def moe_nvfp4_forward_noalloc(bank, x, T, idx, w, k, residual, y, flags, status=None, stream=None):
+    _check(lib().moe_nvfp4_forward_noalloc(C.byref(bank), _ptr(x), T, _ptr(idx), _ptr(w), k, _ptr(residual), _ptr(y),
+                                           flags, _ptr(status), _stream(stream)))
 
 
 def moe_nvfp4_layer(bank, x, w_router, T, k, residual, logits, idx, w, y, flags, workspace, stream=None):

@@ -587,7 +587,7 @@ static long long prefill_chunk_tokens(int H) { return (1LL << 31) / (2LL * H); }
 
 static int forward_run(const BankView& v, const uint16_t* x, int T, const int32_t* idx, const float* w, int k,
                        const uint16_t* residual, void* y, unsigned flags, uint8_t* ws, const FwdLayout& L,
-                       hipStream_t s) {
+                       hipStream_t s, uint32_t* status) {
   int rc;
   RouteTables rt{};
   rt.counts = reinterpret_cast<int32_t*>(ws + L.counts);
@@ -597,7 +597,7 @@ static int forward_run(const BankView& v, const uint16_t* x, int T, const int32_
   rt.tile_expert = reinterpret_cast<int32_t*>(ws + L.tile_e);
   rt.tile_row0 = reinterpret_cast<int32_t*>(ws + L.tile_r);
   rt.hist = reinterpret_cast<int32_t*>(ws + L.hist);
-  rt.status = reinterpret_cast<uint32_t*>(ws + L.counts) + 2;
+  rt.status = status;
   uint16_t* mid = reinterpret_cast<uint16_t*>(ws + L.mid);
   float* part = reinterpret_cast<float*>(ws + L.part);
   const int P = T * k;
@@ -660,8 +660,70 @@ MOE_API int moe_nvfp4_forward(const moe_nvfp4_bank* b, const uint16_t* x, int T,
   if (rc || T == 0) return rc;
   if (!idx || !w) return fail(MOE_EINVAL, "forward: null idx/w");
   if (!aligned(idx, 4) || !aligned(w, 4)) return fail(MOE_EALIGN, "forward: idx/w must be 4-byte aligned");
-  return forward_run(v, x, T, idx, w, k, residual, y, flags, static_cast<uint8_t*>(workspace), L,
-                     static_cast<hipStream_t>(stream));
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  return forward_run(v, x, T, idx, w, k, residual, y, flags, ws, L, static_cast<hipStream_t>(stream),
+                     reinterpret_cast<uint32_t*>(ws + L.counts) + 2);
+}
+
+// ---- the forward with no allocation ------------------------------------------------
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops): the workspace of moe_nvfp4_forward taken from a file-scope device
+// array. Each GPU the library runs on holds its own copy until the process
+// ends. In host code `scratch` is only a stand-in for the device symbol: the
+// address kernels must use comes from hipGetSymbolAddress, once per device.
+static_assert(MOE_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+// The current device's copy of `scratch` (its address on that device).
+static int scratch_ptr(uint8_t** out) {
+  int dev = -1;
+  int rc = hip_check(hipGetDevice(&dev), "forward_noalloc: hipGetDevice");
+  if (rc) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_EINVAL, "forward_noalloc: device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    rc = hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "forward_noalloc: hipGetSymbolAddress");
+    if (rc) return rc;
+    if (!p || !aligned(p, 256)) return fail(MOE_EHIP, "forward_noalloc: scratch address not 256-byte aligned");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<uint8_t*>(g_scratch_ptr[dev]);
+  return MOE_OK;
+}
+
+MOE_API int moe_nvfp4_forward_noalloc(const moe_nvfp4_bank* b, const uint16_t* x, int T, const int32_t* idx,
+                                      const float* w, int k, const uint16_t* residual, void* y, unsigned flags,
+                                      uint32_t* status, void* stream) {
+  BankView v;
+  int rc = bank_view(b, &v, "forward_noalloc");
+  if (rc) return rc;
+  if (status && !aligned(status, 4)) return fail(MOE_EALIGN, "forward_noalloc: status not 4-byte aligned");
+  const size_t need = moe_nvfp4_workspace_bytes(T, k, v.H, v.I, v.E);
+  if (need > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_EWORKSPACE, "forward_noalloc: the call needs %zu bytes of scratch, the library holds %zu per GPU",
+                need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  uint8_t* ws = nullptr;
+  if (T > 0) {
+    rc = scratch_ptr(&ws);
+    if (rc) return rc;
+  }
+  FwdLayout L;
+  // the scratch stands in for the workspace: the same checks, the same layout
+  rc = layer_checks("forward_noalloc", v, x, T, k, residual, y, flags, ws, MOE_NOALLOC_SCRATCH_BYTES, &L);
+  if (rc || T == 0) return rc;
+  if (!idx || !w) return fail(MOE_EINVAL, "forward_noalloc: null idx/w");
+  if (!aligned(idx, 4) || !aligned(w, 4)) return fail(MOE_EALIGN, "forward_noalloc: idx/w must be 4-byte aligned");
+  // without a status word of the caller's, bad expert ids go to the scratch's
+  // own word, which nobody reads
+  uint32_t* st = status ? status : reinterpret_cast<uint32_t*>(ws + L.counts) + 2;
+  return forward_run(v, x, T, idx, w, k, residual, y, flags, ws, L, static_cast<hipStream_t>(stream), st);
 }
 
 // ---- S1..S7 in one call ------------------------------------------------------------
@@ -714,7 +776,7 @@ MOE_API int moe_nvfp4_layer(const moe_nvfp4_bank* b, const uint16_t* x, const fl
   if (rc) return rc;
   rc = hip_check(launch_topk(logits, T, v.E, k, idx, w, s), "topk");
   if (rc) return rc;
-  return forward_run(v, x, T, idx, w, k, residual, y, flags, ws, L, s);
+  return forward_run(v, x, T, idx, w, k, residual, y, flags, ws, L, s, reinterpret_cast<uint32_t*>(ws + L.counts) + 2);
 }
 
 // ---- the workspace status word --------------------------------------------------
