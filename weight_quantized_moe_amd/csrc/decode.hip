@@ -794,7 +794,11 @@ hipError_t launch_flat_layer(const BankView& b, const uint16_t* x, const float* 
 
 // ---- S7: weighted combine (the routing weight is already in `part`) -----------
 // y[t] = residual[t] + sum_j part[t*k + j] in slot order j (f32), four
-// consecutive outputs per thread (16-byte loads of part).
+// consecutive outputs per thread (16-byte loads of part). With k <= KMAX the
+// k rows' loads are all issued before the first add (the rows of pairs with
+// an expert outside [0, E) are read but not added), so a thread waits for one
+// round trip instead of k; KMAX = 0 takes any k one row at a time.
+template <int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part,
                                                      const int32_t* __restrict__ idx, int E, int T,
                                                      int H, int k, const uint16_t* __restrict__ res,
@@ -809,10 +813,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       acc = f32x4{bf16_to_f32(r.x & 0xFFFFu), bf16_to_f32(r.x >> 16), bf16_to_f32(r.y & 0xFFFFu),
                   bf16_to_f32(r.y >> 16)};
     }
-    for (int j = 0; j < k; j++) {
-      const size_t p = t * k + j;
-      const int e = idx[p];
-      if (e >= 0 && e < E) acc += *reinterpret_cast<const f32x4*>(part + p * H + hh);
+    if (KMAX > 0) {
+      f32x4 v[KMAX > 0 ? KMAX : 1];
+      bool ok[KMAX > 0 ? KMAX : 1];
+#pragma unroll
+      for (int j = 0; j < KMAX; j++) {
+        const size_t p = t * k + (j < k ? j : 0);
+        const int e = idx[p];
+        ok[j] = j < k && e >= 0 && e < E;
+        v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(part + p * H + hh));
+      }
+#pragma unroll
+      for (int j = 0; j < KMAX; j++)
+        if (ok[j]) acc += v[j];
+    } else {
+      for (int j = 0; j < k; j++) {
+        const size_t p = t * k + j;
+        const int e = idx[p];
+        if (e >= 0 && e < E) acc += *reinterpret_cast<const f32x4*>(part + p * H + hh);
+      }
     }
     if (f32_out) {
       *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(y) + t * H + hh) = acc;
@@ -827,10 +846,16 @@ hipError_t launch_combine(const float* part, const int32_t* idx, int E, int T, i
                           const uint16_t* residual, void* y, bool f32_out, hipStream_t s) {
   const size_t n4 = (size_t)T * H / 4;
   size_t blocks = (n4 + 255) / 256;
-  if (blocks > 16384) blocks = 16384;
+  if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
-  launch_kernel("combine", combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, part, idx, E, T, H, k,
-                residual, y, f32_out ? 1 : 0);
+  const dim3 grid((unsigned)blocks), block(256);
+  const int fo = f32_out ? 1 : 0;
+  if (k <= 8)
+    launch_kernel("combine", combine_kernel<8>, grid, block, 0, s, part, idx, E, T, H, k, residual, y, fo);
+  else if (k <= 16)
+    launch_kernel("combine", combine_kernel<16>, grid, block, 0, s, part, idx, E, T, H, k, residual, y, fo);
+  else
+    launch_kernel("combine", combine_kernel<0>, grid, block, 0, s, part, idx, E, T, H, k, residual, y, fo);
   return hipGetLastError();
 }
 

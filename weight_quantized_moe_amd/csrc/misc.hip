@@ -2,6 +2,7 @@
 // the dequant test export, the weightless RMS norm between stacked layers, and
 // the affine8_g64 resident linear.
 #include "common.h"
+#include "dma.h"
 #include "internal.h"
 
 namespace moe {
@@ -252,6 +253,9 @@ __global__ __launch_bounds__(64 * kAffWaves) void affine8_kernel(const uint16_t*
         ps[u] = scales[o];
         pb[u] = biases[o];
       }
+      // the scale and bias loads go out first: waiting for them (to stage
+      // them in LDS) then leaves the codes and activations in flight
+      __builtin_amdgcn_sched_barrier(0);
       u32x4 q[kAffRB][kAffGW], xa[kAffGW], xb[kAffGW];
 #pragma unroll
       for (int i = 0; i < kAffGW; i++) {
@@ -272,7 +276,9 @@ __global__ __launch_bounds__(64 * kAffWaves) void affine8_kernel(const uint16_t*
       // keep every load above the first use (the scheduler would otherwise
       // spread them over the MFMAs, one round trip per group)
       __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();  // sbl of the previous block is read
+      // barriers without a memory fence (a fence would wait for every load in
+      // flight): the group MFMAs below start as their own loads land
+      step_barrier();  // sbl of the previous block is read
 #pragma unroll
       for (int u = 0; u < kAffPre; u++) {
         // unconditional (a conditional store would pull its load below the
@@ -280,7 +286,7 @@ __global__ __launch_bounds__(64 * kAffWaves) void affine8_kernel(const uint16_t*
         const int i = min((int)threadIdx.x + 64 * kAffWaves * u, R * gn - 1);
         sbl[i / gn][i % gn] = (uint32_t)ps[u] | ((uint32_t)pb[u] << 16);
       }
-      __syncthreads();  // sbl is written
+      step_barrier();  // sbl is written
 #pragma unroll
       for (int i = 0; i < kAffGW; i++) {
         const bf16x8 a0 = __builtin_bit_cast(bf16x8, xa[i]), a1 = __builtin_bit_cast(bf16x8, xb[i]);
