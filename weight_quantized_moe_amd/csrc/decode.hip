@@ -185,8 +185,9 @@ __global__ __launch_bounds__(kDecThreads) void gemv_kernel(DecodeArgs a) {
 #pragma unroll
       for (int mm = 1; mm < MT; mm++)
         if (m == mm) row = prow[mm];
+      // swizzled layout (gemv_util.h): position pin holds chunk pin ^ (quad & 7)
       if (pin < per_row)
-        dma16(uniform_ptr(a.in + (size_t)row * K), 16u * (uint32_t)pin,
+        dma16(uniform_ptr(a.in + (size_t)row * K), 16u * (uint32_t)xchunk(pin >> 3, pin & 7),
               __builtin_amdgcn_readfirstlane(lds_addr(xs + m * (K / 2)) + 1024u * (uint32_t)blk));
     }
     wait_vmcnt<0>();
@@ -361,10 +362,13 @@ struct FlatArgs {
   uint32_t* status;         // status word (kStatusBadIdx), or null
 };
 
-// n 16-byte pieces global -> LDS by the workgroup: the first U rounds of
-// loads are all issued before any store, so they cost one round trip
-template <int U>
-__device__ __forceinline__ void stage_lds(const u32x4* src, u32x4* dst, int n) {
+// x [H] (bf16) -> LDS, as packed pairs in the swizzled chunk layout
+// (gemv_util.h); the first 3 rounds of loads are issued before any store
+__device__ __forceinline__ void flat_stage_x(const FlatArgs& a, uint32_t* xs) {
+  constexpr int U = 3;
+  const u32x4* src = reinterpret_cast<const u32x4*>(a.x);
+  u32x4* dst = reinterpret_cast<u32x4*>(xs);
+  const int n = a.H / 8;
   u32x4 v[U];
 #pragma unroll
   for (int u = 0; u < U; u++) {
@@ -374,14 +378,9 @@ __device__ __forceinline__ void stage_lds(const u32x4* src, u32x4* dst, int n) {
 #pragma unroll
   for (int u = 0; u < U; u++) {
     const int i = threadIdx.x + u * blockDim.x;
-    if (i < n) dst[i] = v[u];
+    if (i < n) dst[xchunk(i >> 3, i & 7)] = v[u];
   }
-  for (int i = threadIdx.x + U * blockDim.x; i < n; i += blockDim.x) dst[i] = src[i];
-}
-
-// x [H] (bf16) -> LDS, as packed pairs
-__device__ __forceinline__ void flat_stage_x(const FlatArgs& a, uint32_t* xs) {
-  stage_lds<3>(reinterpret_cast<const u32x4*>(a.x), reinterpret_cast<u32x4*>(xs), a.H / 8);
+  for (int i = threadIdx.x + U * blockDim.x; i < n; i += blockDim.x) dst[xchunk(i >> 3, i & 7)] = src[i];
 }
 
 // The gate/up items of workgroup `blk` of `nblk`: wave w takes items
@@ -491,7 +490,8 @@ __global__ __launch_bounds__(64 * kFlatDecodeMaxK) void flat_down_kernel(FlatArg
     s_idx[threadIdx.x] = (e >= 0 && e < a.E) ? e : -1;
     s_w[threadIdx.x] = a.w[threadIdx.x];
   }
-  dma_copy_lds(a.mid, ms, (uint32_t)(k * I * 2), k);  // the k waves copy the mids, all chunks at once
+  // the k waves copy the mids, all chunks at once, into the swizzled layout
+  dma_copy_lds_swz(a.mid, ms, (uint32_t)(k * I * 2), k);
   wait_vmcnt<0>();
   __syncthreads();
   {
@@ -503,7 +503,7 @@ __global__ __launch_bounds__(64 * kFlatDecodeMaxK) void flat_down_kernel(FlatArg
       const float td = global_factor(*reinterpret_cast<const float*>(rec + a.g[2]));
       const uint8_t* cd = rec + a.codes[2] + (size_t)(row_ok ? r : 0) * (I / 2);
       const uint8_t* sd = rec + a.scales[2] + (size_t)(row_ok ? r : 0) * (I / 16);
-      const uint32_t* mrow = ms + (size_t)j * (I / 2);
+      const int q0 = j * nquads;  // pair j's mids start at this quad of the buffer
       for (int qb = 0; qb < nquads; qb += G * QB) {
         Quad vd[QB];
 #pragma unroll
@@ -518,7 +518,7 @@ __global__ __launch_bounds__(64 * kFlatDecodeMaxK) void flat_down_kernel(FlatArg
 #pragma unroll
             for (int b = 0; b < 4; b++) {
               uint32_t xw[8];
-              load_x8(mrow, qd, b, xw);
+              load_x8(ms, q0 + qd, b, xw);
               ad = fmaf(quad_scale(vd[i], b) * td,
                         block_dot16(quad_word(vd[i], 2 * b), quad_word(vd[i], 2 * b + 1), xw), ad);
             }

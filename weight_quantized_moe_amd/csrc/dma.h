@@ -43,6 +43,24 @@ __device__ __forceinline__ void dma_copy_lds(const void* src, void* dst, uint32_
   }
 }
 
+// The same copy into the swizzled input layout of the expert-streaming
+// kernels (16-byte chunk c of 64-input quad q at chunk position 8 q + (c ^
+// (q & 7)), quads counted from src): lane l of a load fills position l of its
+// 64 chunks, so it reads the chunk that belongs there (the XOR is its own
+// inverse, and a KiB holds 8 whole quads). nbytes: whole quads (128 bytes).
+__device__ __forceinline__ void dma_copy_lds_swz(const void* src, void* dst, uint32_t nbytes, int nwaves) {
+  const uint8_t* base = uniform_ptr(src);
+  const uint32_t l0 = lds_addr(dst);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (uint32_t c = wave; c * 1024 < nbytes; c += nwaves) {
+    const uint32_t pos = c * 64 + lane;  // chunk position this lane fills
+    const uint32_t q = pos >> 3;
+    const uint32_t off = 16u * (8u * q + ((pos & 7u) ^ (q & 7u)));
+    if (16u * pos < nbytes) dma16(base, off, __builtin_amdgcn_readfirstlane(l0 + c * 1024));
+  }
+}
+
 // Workgroup barrier after this wave's LDS accesses have completed. No memory
 // fence: __syncthreads()'s fence would also wait for every load in flight
 // (weights loaded into registers ahead of their use, HBM -> LDS copies). The

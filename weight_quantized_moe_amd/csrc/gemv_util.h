@@ -25,10 +25,19 @@ __device__ __forceinline__ Quad load_quad(const uint8_t* row_codes, const uint8_
   return v;
 }
 
-// the 8 packed input pairs of block b (0..3) of quad q, from LDS
-__device__ __forceinline__ void load_x8(const uint32_t* xrow, int q, int b, uint32_t* xw) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(xrow + 32 * q + 8 * b);
-  const u32x4 v0 = p[0], v1 = p[1];
+// Inputs staged in LDS sit in 16-byte chunks (8 bf16 values), 8 chunks per
+// 64-input quad, chunk c of quad q at chunk position 8 q + (c ^ (q & 7)). The
+// lanes of a row read different quads at once, 128 bytes apart, i.e. half the
+// LDS's 64 four-byte banks apart: stored in order, the 16-byte reads of 8 or
+// 16 consecutive quads would fall on two sets of four banks (a 4- or 8-way
+// conflict); swizzled, 8 consecutive quads cover every bank once.
+__device__ __forceinline__ int xchunk(int q, int c) { return 8 * q + (c ^ (q & 7)); }
+
+// the 8 packed input pairs of block b (0..3) of quad q of an LDS input buffer
+// (q counted from the buffer's start)
+__device__ __forceinline__ void load_x8(const uint32_t* xbuf, int q, int b, uint32_t* xw) {
+  const u32x4 v0 = *reinterpret_cast<const u32x4*>(xbuf + 4 * xchunk(q, 2 * b));
+  const u32x4 v1 = *reinterpret_cast<const u32x4*>(xbuf + 4 * xchunk(q, 2 * b + 1));
   xw[0] = v0.x;
   xw[1] = v0.y;
   xw[2] = v0.z;
