@@ -928,6 +928,34 @@ def test_affine8_and_rmsnorm():
     check_bf16(to_np_bits(y), oracle.bf16_to_f32(ref), "rmsnorm")
 
 
+@pytest.mark.parametrize("T,K,N", [(8, 5120, 5120), (1, 1024, 100), (5, 2048, 4100), (2, 3072, 33),
+                                   (7, 4096, 5120), (8, 6144, 300), (3, 5120, 17)])
+def test_affine8_stream_shapes(T, K, N):
+    # up to 8 tokens and K a multiple of 1,024 (at most 6,144): the streaming
+    # form, activations and scale and bias rows staged in LDS; 4100 rows give
+    # 17-row workgroups (the last with 3 rows), 33 and 17 rows a second row
+    # block with 1 row or none. Against the oracle, and against the general
+    # kernel on the same data (x copied to an offset of 4 bytes, off the
+    # streaming form's conditions): at K = 5120 both give wave w the groups
+    # 5 w .. 5 w + 4 and add the same terms in the same order, so bit for bit
+    v = synth.resident_weights(31, N, K)
+    codes, scales, biases = oracle.q8_quantize(v)
+    x = synth.activations(32, T, K)
+    ref_f, _ = oracle.affine8_linear(x, codes, scales, biases)
+    cd, sd, bd = torch.from_numpy(codes.view(np.int32)).to(DEV), bf16_tensor(scales), bf16_tensor(biases)
+    y = torch.full((T, N), 0x7FC0, dtype=torch.int16, device=DEV)
+    wq.affine8_g64_linear(bf16_tensor(x), cd, sd, bd, T, K, N, y)
+    flat = torch.zeros(T * K + 8, dtype=torch.int16, device=DEV)
+    flat[2:2 + T * K] = bf16_tensor(x).reshape(-1)
+    y2 = torch.full((T, N), 0x7FC0, dtype=torch.int16, device=DEV)
+    wq.affine8_g64_linear(flat[2:2 + T * K].view(T, K), cd, sd, bd, T, K, N, y2)
+    torch.cuda.synchronize()
+    check_bf16(to_np_bits(y), ref_f, f"affine8 stream {T}x{K}x{N}")
+    check_bf16(to_np_bits(y2), ref_f, f"affine8 general {T}x{K}x{N}")
+    if K == 5120:
+        assert np.array_equal(to_np_bits(y), to_np_bits(y2)), "streaming and general kernels differ"
+
+
 def test_affine8_and_rmsnorm_unaligned_rows():
     # activations 4-byte but not 16-byte aligned: the linear stages them with
     # single-word loads, the norm takes its strided loop (also for H not a

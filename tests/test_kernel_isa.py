@@ -1,0 +1,54 @@
+"""Properties of the compiled gfx950 code that the kernels' correctness rests
+on and that no source-level test can see (CPU only: hipcc compiles the
+device code to assembly, nothing runs).
+
+The streaming affine8 kernel issues its HBM -> LDS loads from inline asm, then
+every code load as a buffer load, and then waits with vmcnt(number of code
+loads): the wait covers the LDS loads only if the compiler keeps every code
+load above it. If a later compiler moved one below, the count would let an
+LDS load still be in flight when the barrier releases the waves."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from weight_quantized_moe_amd import build as B
+
+SRC = os.path.join(B.SRC, "misc.hip")
+
+
+def _device_asm(src):
+    if not os.path.exists(B.HIPCC) and not shutil.which("hipcc"):
+        pytest.skip("hipcc not available")
+    flags = [f for f in B.FLAGS if not f.startswith("-W")]
+    r = subprocess.run([B.HIPCC, *flags, "--cuda-device-only", "-S", src, "-o", "-"], capture_output=True,
+                       text=True, timeout=600)
+    assert r.returncode == 0, r.stderr
+    return r.stdout
+
+
+def _function(asm, mangled):
+    m = re.search(rf"^{re.escape(mangled)}:[^\n]*\n(.*?)\ts_endpgm", asm, re.S | re.M)
+    assert m, f"{mangled} not found"
+    return m.group(1)
+
+
+def test_affine8_stream_code_loads_precede_the_lds_wait():
+    asm = _device_asm(SRC)
+    for gw in range(1, 7):
+        body = _function(asm, f"_ZN3moe21affine8_stream_kernelILi{gw}EEEvPKtPKhS2_S2_iiiPt")
+        lines = body.splitlines()
+        first_wait = next(i for i, l in enumerate(lines) if re.search(r"s_waitcnt\s+vmcnt", l))
+        before = lines[:first_wait]
+        n_buf = sum("buffer_load_dwordx4" in l for l in before)
+        n_buf_all = sum("buffer_load" in l for l in lines)
+        assert n_buf == n_buf_all == 2 * gw, (gw, n_buf, n_buf_all)
+        assert re.search(rf"vmcnt\({2 * gw}\)", lines[first_wait]), lines[first_wait]
+        # every HBM -> LDS load comes before the first code load
+        first_buf = next(i for i, l in enumerate(lines) if "buffer_load" in l)
+        assert not any("global_load_lds" in l for l in lines[first_buf:first_wait])
+        assert any("global_load_lds" in l for l in lines[:first_buf])
+        # no other vector-memory load between them
+        assert not any(re.search(r"global_load_(?!lds)|scratch_", l) for l in before)

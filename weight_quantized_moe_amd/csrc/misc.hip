@@ -320,6 +320,122 @@ __global__ __launch_bounds__(64 * kAffWaves) void affine8_kernel(const uint16_t*
   }
 }
 
+// The same linear for up to 8 tokens where K is a multiple of 1,024 (G = 16
+// GW groups, GW <= 6), as a stream over the codes with the activations in
+// LDS. The kernel above reads every group's activations into registers, a
+// piece per lane and MFMA, twice over for 8 tokens (the 16-token MFMA is half
+// padding), in each of the 256 workgroups; with the codes of the padding rows
+// of its second row block that is three times the code bytes through each
+// CU's vector memory path, and with the codes removed that kernel still took
+// 7.5 of its 13.2 us at 8 x 5120 x 5120. Here:
+//   - the activations and the workgroup's scale and bias rows go HBM -> LDS
+//     with global_load_lds_dwordx4, once per workgroup, behind one barrier;
+//     lanes of padding tokens read a real token's row (their outputs are
+//     never stored);
+//   - the codes are raw buffer loads straight into registers, all issued at
+//     the start (marked volatile, so the compiler keeps them above the wait
+//     for the LDS loads); the lanes of rows past the workgroup's last row get
+//     an offset past the buffer's range, which the hardware answers with
+//     zeros without a memory access;
+//   - the arithmetic is the kernel above's: both sums on
+//     v_mfma_f32_16x16x32_bf16 (tokens as M, 16 weight rows as N), the group
+//     sum of x against a B operand of ones, scale and bias folded per group,
+//     the 16 waves' partial sums added in LDS in wave order.
+constexpr int kAfsTok = 8;  // tokens at most
+
+template <int GW>
+__global__ __launch_bounds__(64 * kAffWaves) void affine8_stream_kernel(const uint16_t* __restrict__ x,
+                                                                        const uint8_t* codes,
+                                                                        const uint16_t* __restrict__ scales,
+                                                                        const uint16_t* __restrict__ biases, int T,
+                                                                        int N, int rw, uint16_t* __restrict__ y) {
+  constexpr int K = 1024 * GW, G = 16 * GW, R = 16 * kAffRB;
+  constexpr uint32_t kXRow = 2 * K + 16;  // bytes per staged token row (16 more: rows start 4 banks apart)
+  constexpr int kChunks = 2 * K / 1024;   // 1 KiB loads per token row
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kAfsTok * kXRow];
+  __shared__ __attribute__((aligned(16))) uint16_t ss[R * G], bs[R * G];  // [row][group]
+  __shared__ float red[kAffWaves][kAfsTok][R];                              // [wave][token][row]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, j = lane >> 4;
+  const int r0 = blockIdx.x * rw, nr = min(rw, N - r0);  // this workgroup's rows [r0, r0 + nr)
+  const int g0 = wave * GW;                              // this wave's groups [g0, g0 + GW)
+
+  // HBM -> LDS: the rows' scales and biases (nr * G * 2 contiguous bytes each,
+  // a multiple of 32), and the activations (1 KiB chunk c: token c / kChunks,
+  // part c % kChunks)
+  dma_copy_lds(scales + (size_t)r0 * G, ss, (uint32_t)(nr * G * 2), kAffWaves);
+  dma_copy_lds(biases + (size_t)r0 * G, bs, (uint32_t)(nr * G * 2), kAffWaves);
+  {
+    const uint8_t* xb = uniform_ptr(x);
+    const uint32_t l0 = lds_addr(xs);
+    for (int c = wave; c < T * kChunks; c += kAffWaves) {
+      const int t = c / kChunks, part = c % kChunks;
+      dma16(xb, (uint32_t)(t * 2 * K + 1024 * part + 16 * lane),
+            __builtin_amdgcn_readfirstlane(l0 + t * kXRow + 1024 * part));
+    }
+  }
+  // the codes: lane (n, j) of row block b holds 16 bytes of row r0 + 16 b + n
+  // for each of the wave's groups
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(codes), (short)0, N * K, 0x00020000);
+  u32x4 q[kAffRB][GW];
+#pragma unroll
+  for (int i = 0; i < GW; i++)
+#pragma unroll
+    for (int b = 0; b < kAffRB; b++) {
+      const int rr = 16 * b + n;
+      const uint32_t off = rr < nr ? (uint32_t)((r0 + rr) * K + 64 * (g0 + i) + 16 * j) : 0x80000000u;
+      q[b][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+    }
+  // the wait covers the HBM -> LDS loads (issued first) and leaves the codes
+  // in flight
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<kAffRB * GW>();
+  step_barrier();
+
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  // A operand: lane (n, j) holds token n (padding rows n >= T read token
+  // T - 1), inputs 16 j .. 16 j + 15 of a group (8 per k-slice)
+  const uint8_t* xa = xs + min(n, T - 1) * kXRow + 32 * j;
+  f32x4 acc[kAffRB];
+#pragma unroll
+  for (int b = 0; b < kAffRB; b++) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < GW; i++) {
+    const int g = g0 + i;
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(xa + 128 * g);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(xa + 128 * g + 16);
+    const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 xsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, ones, z, 0, 0, 0);
+    xsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, ones, xsum, 0, 0, 0);
+#pragma unroll
+    for (int b = 0; b < kAffRB; b++) {
+      f32x4 sq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, u8x8_bf16(q[b][i].x, q[b][i].y), z, 0, 0, 0);
+      sq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, u8x8_bf16(q[b][i].z, q[b][i].w), sq, 0, 0, 0);
+      // rows past nr read another row's entries (their outputs are not stored)
+      const float sc = bf16_to_f32(ss[(16 * b + n) * G + g]), bi = bf16_to_f32(bs[(16 * b + n) * G + g]);
+#pragma unroll
+      for (int e = 0; e < 4; e++) acc[b][e] = fmaf(sc, sq[e], fmaf(bi, xsum[e], acc[b][e]));
+    }
+  }
+  // D layout: lane (n, j) holds row 16 b + n for tokens 4 j .. 4 j + 3
+  if (j < kAfsTok / 4) {
+#pragma unroll
+    for (int b = 0; b < kAffRB; b++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) red[wave][4 * j + e][16 * b + n] = acc[b][e];
+  }
+  __syncthreads();
+  if (threadIdx.x < kAfsTok * R) {
+    const int tt = threadIdx.x / R, rr = threadIdx.x % R;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kAffWaves; w++) v += red[w][tt][rr];
+    if (tt < T && rr < nr) y[(size_t)tt * N + r0 + rr] = f32_to_bf16(v);
+  }
+}
+
 // compute units of the current device (0 if the query fails)
 static int device_cus() {
   int dev = 0, n = 0;
@@ -328,16 +444,39 @@ static int device_cus() {
   return n;
 }
 
+template <int GW>
+static void launch_affine8_stream(dim3 grid, hipStream_t s, const uint16_t* x, const uint8_t* c8,
+                                  const uint16_t* scales, const uint16_t* biases, int T, int N, int rw, uint16_t* y) {
+  launch_kernel("affine8", affine8_stream_kernel<GW>, grid, dim3(64 * kAffWaves), 0, s, x, c8, scales, biases, T, N,
+                rw, y);
+}
+
 hipError_t launch_affine8(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
                           const uint16_t* biases, int T, int K, int N, uint16_t* y, hipStream_t s) {
   const int cus = device_cus();
   const int rw = std::min(16 * kAffRB, std::max(16, cus > 0 ? (N + cus - 1) / cus : 16 * kAffRB));
   const dim3 grid((N + rw - 1) / rw), block(64 * kAffWaves);
   const uint8_t* c8 = reinterpret_cast<const uint8_t*>(codes);
-  if (((uintptr_t)x & 15) == 0)
+  // the streaming form: up to 8 tokens, K = 1,024 GW with GW <= 6, 16-byte
+  // aligned activations and scale and bias rows, and byte offsets of the
+  // codes within 31 bits
+  const bool stream = T <= kAfsTok && K % 1024 == 0 && K <= 6144 && ((uintptr_t)x & 15) == 0 &&
+                      ((uintptr_t)scales & 15) == 0 &&
+                      ((uintptr_t)biases & 15) == 0 && (uint64_t)N * K < (1ull << 31);
+  if (stream) {
+    switch (K / 1024) {
+      case 1: launch_affine8_stream<1>(grid, s, x, c8, scales, biases, T, N, rw, y); break;
+      case 2: launch_affine8_stream<2>(grid, s, x, c8, scales, biases, T, N, rw, y); break;
+      case 3: launch_affine8_stream<3>(grid, s, x, c8, scales, biases, T, N, rw, y); break;
+      case 4: launch_affine8_stream<4>(grid, s, x, c8, scales, biases, T, N, rw, y); break;
+      case 5: launch_affine8_stream<5>(grid, s, x, c8, scales, biases, T, N, rw, y); break;
+      default: launch_affine8_stream<6>(grid, s, x, c8, scales, biases, T, N, rw, y); break;
+    }
+  } else if (((uintptr_t)x & 15) == 0) {
     launch_kernel("affine8", affine8_kernel<true>, grid, block, 0, s, x, c8, scales, biases, T, K, N, rw, y);
-  else
+  } else {
     launch_kernel("affine8", affine8_kernel<false>, grid, block, 0, s, x, c8, scales, biases, T, K, N, rw, y);
+  }
   return hipGetLastError();
 }
 
