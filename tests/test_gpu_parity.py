@@ -999,6 +999,34 @@ def test_affine8_gemm_ragged(T, K, N):
     check_bf16(to_np_bits(y), ref_f, f"affine8 gemm {T}x{K}x{N}")
 
 
+@pytest.mark.parametrize("T,K,N", [(300, 1024, 200), (129, 512, 130), (64, 5120, 384)])
+def test_affine8_gemm_dma_form_matches_register_form(T, K, N):
+    # K a multiple of 512 with 16-byte aligned scale and bias rows takes the
+    # HBM -> LDS form; the same scales and biases copied to an offset of 2
+    # bytes take the register form. Both run the same operations in the same
+    # order: bit for bit, and within the oracle's bound
+    v = synth.resident_weights(24, N, K)
+    codes, scales, biases = oracle.q8_quantize(v)
+    x = synth.activations(25, T, K)
+    ref_f, _ = oracle.affine8_linear(x, codes, scales, biases)
+    cd, xd = torch.from_numpy(codes.view(np.int32)).to(DEV), bf16_tensor(x)
+    sd, bd = bf16_tensor(scales), bf16_tensor(biases)
+    G = K // 64
+    sflat = torch.zeros(N * G + 8, dtype=torch.int16, device=DEV)
+    bflat = torch.zeros(N * G + 8, dtype=torch.int16, device=DEV)
+    sflat[1:1 + N * G] = sd.reshape(-1)
+    bflat[1:1 + N * G] = bd.reshape(-1)
+    s2, b2 = sflat[1:1 + N * G].view(N, G), bflat[1:1 + N * G].view(N, G)
+    assert s2.data_ptr() % 16 == 2 and sd.data_ptr() % 16 == 0
+    y = torch.full((T, N), 0x7FC0, dtype=torch.int16, device=DEV)
+    y2 = torch.full((T, N), 0x7FC0, dtype=torch.int16, device=DEV)
+    wq.affine8_g64_linear(xd, cd, sd, bd, T, K, N, y)
+    wq.affine8_g64_linear(xd, cd, s2, b2, T, K, N, y2)
+    torch.cuda.synchronize()
+    check_bf16(to_np_bits(y), ref_f, f"affine8 gemm dma form {T}x{K}x{N}")
+    assert np.array_equal(to_np_bits(y), to_np_bits(y2)), "HBM -> LDS and register forms differ"
+
+
 def test_affine8_gemm_full_shape_sampled():
     # a 5120 x 5120 resident over 1,024 tokens (8 token tiles x 40 row tiles);
     # the oracle on 24 sampled tokens, every output row

@@ -52,3 +52,37 @@ def test_affine8_stream_code_loads_precede_the_lds_wait():
         assert any("global_load_lds" in l for l in lines[:first_buf])
         # no other vector-memory load between them
         assert not any(re.search(r"global_load_(?!lds)|scratch_", l) for l in before)
+
+
+def test_affine8_gemm_dma_kernel_waits_are_its_own():
+    """The HBM -> LDS GEMM's loop waits for its loads by count (vmcnt(4): the
+    next group's activations may stay in flight). That count holds only if
+    no compiled vector-memory load shares the counter: every load of the
+    kernel must be one of its own HBM -> LDS loads, and every vmcnt wait one
+    of its own."""
+    asm = _device_asm(os.path.join(B.SRC, "affine8_gemm.hip"))
+    body = _function(asm, "_ZN3moe23affine8_gemm_dma_kernelEPKtPKhS1_S1_iiiiPt")
+    lines = body.splitlines()
+    assert sum("global_load_lds_dwordx4" in l for l in lines) >= 7
+    assert not any(re.search(r"global_load_(?!lds)|buffer_load|scratch_|flat_load", l) for l in lines)
+    waits = [int(m.group(1)) for l in lines for m in [re.search(r"s_waitcnt\s+vmcnt\((\d+)\)", l)] if m]
+    assert waits and set(waits) <= {0, 4}, waits
+
+
+def test_affine8_gemm_group_sums_read_all_four_words():
+    """Each 16-byte piece's sum is four v_dot2 against (1, 1), one per word.
+    Written with a bit cast of the vector's element accesses, this compiler
+    read element 0 four times; the helper takes the words through an array.
+    Every run of four accumulating v_dot2 into one register must read four
+    different source registers."""
+    asm = _device_asm(os.path.join(B.SRC, "affine8_gemm.hip"))
+    for name in ("_ZN3moe19affine8_gemm_kernelEPKtPKhS1_S1_iiiiPt", "_ZN3moe23affine8_gemm_dma_kernelEPKtPKhS1_S1_iiiiPt"):
+        dots = [m.groups() for l in _function(asm, name).splitlines()
+                for m in [re.search(r"v_dot2c_f32_bf16_e32 (v\d+), 0x3f803f80, (v\d+)", l)] if m]
+        assert len(dots) >= 8 and len(dots) % 4 == 0, (name, len(dots))
+        by_dst = {}
+        for dst, src in dots:
+            by_dst.setdefault(dst, []).append(src)
+        for dst, srcs in by_dst.items():
+            for i in range(0, len(srcs) - 3, 4):
+                assert len(set(srcs[i:i + 4])) == 4, (name, dst, srcs)

@@ -30,6 +30,7 @@
 // other, so the activations stream through each XCD once and the codes are
 // read from HBM once per XCD.
 #include "common.h"
+#include "dma.h"
 #include "internal.h"
 
 namespace moe {
@@ -40,12 +41,36 @@ constexpr int kA8M = 128, kA8N = 128, kA8Threads = 256;
 __device__ __forceinline__ int a8_slot(int r, int j) { return j ^ ((r & 7) ^ ((r >> 3) & 1)); }
 
 // 4 bytes of codes -> two packed bf16 pairs (exact: a code has at most 8
-// significant bits, so its f32 value has a zero low half)
+// significant bits, so its f32 value has a zero low half): v_cvt_f32_ubyte0..3,
+// then one byte permute per pair takes the two high halves
 __device__ __forceinline__ void u8x4_bf16(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  const float a = (float)(w & 0xFFu), b = (float)((w >> 8) & 0xFFu);  // v_cvt_f32_ubyte0..3
+  const float a = (float)(w & 0xFFu), b = (float)((w >> 8) & 0xFFu);
   const float c = (float)((w >> 16) & 0xFFu), d = (float)(w >> 24);
-  lo = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
-  hi = (__float_as_uint(c) >> 16) | (__float_as_uint(d) & 0xFFFF0000u);
+  lo = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+  hi = __builtin_amdgcn_perm(__float_as_uint(d), __float_as_uint(c), 0x07060302u);
+}
+
+// sum of the 8 bf16 values of a 16-byte piece, by four v_dot2 against (1, 1)
+// from 0 (the products are exact). The words go through a plain array: this
+// compiler turned a bit cast of a vector element access (v.y) into a read of
+// element 0.
+__device__ __forceinline__ float piece_sum(const u32x4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const bf16x2 one2 = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+  float s = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; q++) s = __builtin_amdgcn_fdot2_f32_bf16(one2, __builtin_bit_cast(bf16x2, w[q]), s, false);
+  return s;
+}
+
+// total of s over each group of 8 consecutive lanes, in the group's first
+// lane (DPP: swap within pairs, then within quads, then the other quad of the
+// 8 through the half-row mirror; the other lanes hold partial totals)
+__device__ __forceinline__ float row8_sum(float s) {
+  s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, false));
+  s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x4E, 0xF, 0xF, false));
+  s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x141, 0xF, 0xF, false));
+  return s;
 }
 
 // f32 -> bf16 by truncation (used only where the value is exact in bf16)
@@ -94,13 +119,7 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
     for (int i = 0; i < 4; i++) {
       const int p = tid + kA8Threads * i, r = p >> 3, j = p & 7;
       *reinterpret_cast<u32x4*>(&As[buf][r * 128 + 16 * a8_slot(r, j)]) = av[i];
-      const uint32_t w[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
-      float s = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 4; q++) s += bf16_to_f32(w[q] & 0xFFFFu) + bf16_to_f32(w[q] >> 16);
-      s += __shfl_xor(s, 1, 64);
-      s += __shfl_xor(s, 2, 64);
-      s += __shfl_xor(s, 4, 64);
+      const float s = row8_sum(piece_sum(av[i]));
       if (j == 0) {
         const float x1 = bf16_to_f32(f32_to_bf16(s));
         const float r1 = s - x1;  // exact
@@ -199,11 +218,205 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
   }
 }
 
+// The same GEMM with every operand going HBM -> LDS by global_load_lds_dwordx4
+// (K a multiple of 512, scale and bias rows 16-byte aligned). The kernel above
+// loads the next group's activations into registers during a group and
+// stores them to LDS at its end, so each group waits out the round trip of
+// loads issued one group earlier. Here the loads write no registers and the
+// loop waits for them itself, by count:
+//   - activations: three LDS stages, loaded two groups ahead (4 loads per
+//     wave: rows 32 w + 8 i + l / 8, the 16-byte piece that belongs in slot
+//     l % 8 of the swizzled row);
+//   - codes: two stages, one group ahead, each wave its own 32 rows (2 loads:
+//     rows 16 i + l / 4, piece (l % 4) ^ ((row / 4) % 4) in slot l % 4, so
+//     that 16 lanes' reads of 16 consecutive rows fall in distinct banks);
+//   - scales and biases: 16 bytes (8 groups) of each row, a block ahead
+//     (wave w loads 64 rows of one of the two arrays), double-buffered.
+// Per group g: wait for group g's loads (the only loads issued later are the
+// activations of group g + 1: vmcnt(4)), barrier, issue the next loads, then
+// the group sums from LDS, the group's MFMAs into tmp, a second barrier (the
+// group sums are complete), the bias MFMA and the scale fold: the same
+// operations in the same order as the kernel above, so the output is the
+// same bit for bit.
+constexpr int kA8DStages = 3;  // activation stages
+
+__device__ __forceinline__ int a8_cslot(int r, int p) { return p ^ ((r >> 2) & 3); }
+
+__global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2))) void affine8_gemm_dma_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* codes, const uint16_t* scales, const uint16_t* biases, int T,
+    int K, int N, int n_tiles, uint16_t* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint8_t As[kA8DStages][kA8M * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t Cs[2][kA8N * 64];            // [row][64 codes], swizzled
+  __shared__ __attribute__((aligned(16))) uint16_t Ss[2][2][kA8N][8];          // [block][scale|bias][row][group]
+  __shared__ __attribute__((aligned(16))) uint32_t Xs[kA8M][2];               // group sums of x as bf16
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int G = K / 64;
+  int mt, nt;
+  if (n_tiles % 8 == 0) {
+    const int per = n_tiles / 8, i = blockIdx.x / 8;
+    mt = i / per;
+    nt = (int)(blockIdx.x % 8) + 8 * (i % per);
+  } else {
+    mt = blockIdx.x / n_tiles;
+    nt = blockIdx.x % n_tiles;
+  }
+  const int m0 = mt * kA8M, n0 = nt * kA8N;
+  const int n = n0 + wave * 32 + l32;  // this lane's output row (MFMA column)
+
+  // load sources: uniform bases and per-lane 32-bit offsets
+  const uint8_t* xb = uniform_ptr(x + (size_t)m0 * K);
+  const uint8_t* cb = uniform_ptr(codes + (size_t)n0 * K);
+  const uint8_t* sb = uniform_ptr((wave < 2 ? scales : biases) + (size_t)n0 * G);
+  uint32_t a_off[4], c_off[2];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int r = 32 * wave + 8 * i + (lane >> 3);
+    a_off[i] = (uint32_t)((min(m0 + r, T - 1) - m0) * K * 2 + 16 * a8_slot(r, lane & 7));
+  }
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int r = 32 * wave + 16 * i + (lane >> 2);
+    c_off[i] = (uint32_t)((min(n0 + r, N - 1) - n0) * K + 16 * a8_cslot(r, lane & 3));
+  }
+  const int s_row = 64 * (wave & 1) + lane;
+  const uint32_t s_off = (uint32_t)((min(n0 + s_row, N - 1) - n0) * G * 2);
+  // LDS destinations: wave-uniform bases, the stage or buffer added per load
+  const uint32_t a_lds = __builtin_amdgcn_readfirstlane(lds_addr(&As[0][0]) + 32 * wave * 128);
+  const uint32_t c_lds = __builtin_amdgcn_readfirstlane(lds_addr(&Cs[0][0]) + 32 * wave * 64);
+  const uint32_t s_lds = __builtin_amdgcn_readfirstlane(lds_addr(&Ss[0][wave >> 1][64 * (wave & 1)][0]));
+  // group g's activations into stage g % 3 (4 loads)
+  auto issue_a = [&](int g) {
+    const uint32_t l = __builtin_amdgcn_readfirstlane(a_lds + (uint32_t)(g % kA8DStages) * (kA8M * 128));
+#pragma unroll
+    for (int i = 0; i < 4; i++) dma16(xb + 128 * g, a_off[i], l + 1024 * i);
+  };
+  // group g's codes into buffer g % 2 (2 loads), and at the start of a block
+  // of 8 groups the block's scales or biases (1 load)
+  auto issue_c = [&](int g) {
+    const uint32_t l = __builtin_amdgcn_readfirstlane(c_lds + (uint32_t)(g & 1) * (kA8N * 64));
+#pragma unroll
+    for (int i = 0; i < 2; i++) dma16(cb + 64 * g, c_off[i], l + 1024 * i);
+    if ((g & 7) == 0)
+      dma16(sb + 2 * g, s_off,
+            __builtin_amdgcn_readfirstlane(s_lds + (uint32_t)((g >> 3) & 1) * (uint32_t)sizeof(Ss[0])));
+  };
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; mb++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[mb][r] = 0.0f;
+
+  issue_c(0);
+  issue_a(0);
+  if (G > 1) issue_a(1);
+  for (int g = 0; g < G; g++) {
+    // group g's codes, scales and activations have landed for this wave: the
+    // loads issued after them are group g + 1's activations
+    if (g + 1 < G)
+      wait_vmcnt<4>();
+    else
+      wait_vmcnt<0>();
+    // every wave's loads of group g have landed, and every wave is done with
+    // group g - 1 (codes buffer (g + 1) % 2, activation stage (g + 2) % 3)
+    step_barrier();
+    if (g + 1 < G) issue_c(g + 1);
+    if (g + 2 < G) issue_a(g + 2);
+    const uint8_t* A = As[g % kA8DStages];
+    // group sums of group g: thread t sums pieces (row p / 8, piece p % 8) for
+    // p = t + 256 i (piece_sum), the 8 pieces of a row added in the row's
+    // first lane (row8_sum); split exactly into three bf16 values
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int p = tid + kA8Threads * i, r = p >> 3, j = p & 7;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(A + r * 128 + 16 * a8_slot(r, j));
+      const float s = row8_sum(piece_sum(v));
+      if (j == 0) {
+        const float x1 = bf16_to_f32(f32_to_bf16(s));
+        const float r1 = s - x1;  // exact
+        const float x2 = bf16_to_f32(f32_to_bf16(r1));
+        const float x3 = r1 - x2;  // exact, and exact in bf16 (at most 8 significant bits left)
+        Xs[r][0] = bf16_trunc(x1) | (bf16_trunc(x2) << 16);
+        Xs[r][1] = bf16_trunc(x3);
+      }
+    }
+    // B: this lane's 32 codes (row 32 w + l32, bytes 32 h .. 32 h + 31)
+    const int cr = 32 * wave + l32;
+    const uint8_t* crow = Cs[g & 1] + cr * 64;
+    const u32x4 bc0 = *reinterpret_cast<const u32x4*>(crow + 16 * a8_cslot(cr, 2 * h));
+    const u32x4 bc1 = *reinterpret_cast<const u32x4*>(crow + 16 * a8_cslot(cr, 2 * h + 1));
+    f32x16 tmp[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) {
+      // slice kk: bytes 8 kk .. 8 kk + 7 of the lane's 32
+      const uint32_t w0 = kk < 2 ? (kk == 0 ? bc0.x : bc0.z) : (kk == 2 ? bc1.x : bc1.z);
+      const uint32_t w1 = kk < 2 ? (kk == 0 ? bc0.y : bc0.w) : (kk == 2 ? bc1.y : bc1.w);
+      uint32_t q0, q1, q2, q3;
+      u8x4_bf16(w0, q0, q1);
+      u8x4_bf16(w1, q2, q3);
+      const bf16x8 bfr = __builtin_bit_cast(bf16x8, u32x4{q0, q1, q2, q3});
+#pragma unroll
+      for (int mb = 0; mb < 4; mb++) {
+        const int r = 32 * mb + l32;
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(A + r * 128 + 16 * a8_slot(r, 4 * h + kk));
+        if (kk == 0) {
+          f32x16 z;
+#pragma unroll
+          for (int e = 0; e < 16; e++) z[e] = 0.0f;
+          tmp[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, z, 0, 0, 0);
+        } else {
+          tmp[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, tmp[mb], 0, 0, 0);
+        }
+      }
+    }
+    step_barrier();  // the group sums are complete
+    const uint16_t sc = Ss[(g >> 3) & 1][0][cr][g & 7], bi = Ss[(g >> 3) & 1][1][cr][g & 7];
+    // bias: inputs 0..2 of a k-slice carry (x1, x2, x3) against (b, b, b)
+    {
+      const uint32_t bb = bi;
+      const bf16x8 bbf = __builtin_bit_cast(
+          bf16x8, h == 0 ? u32x4{bb | (bb << 16), bb, 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+      for (int mb = 0; mb < 4; mb++) {
+        const int r = 32 * mb + l32;
+        const bf16x8 xf =
+            __builtin_bit_cast(bf16x8, h == 0 ? u32x4{Xs[r][0], Xs[r][1], 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, bbf, acc[mb], 0, 0, 0);
+      }
+    }
+    const float scf = bf16_to_f32(sc);
+#pragma unroll
+    for (int mb = 0; mb < 4; mb++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) acc[mb][e] = fmaf(scf, tmp[mb][e], acc[mb][e]);
+  }
+  // element e of lane l: token 8 (e / 4) + 4 h + e % 4 of block mb, row n
+  if (n < N) {
+#pragma unroll
+    for (int mb = 0; mb < 4; mb++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) {
+        const int t = m0 + 32 * mb + 8 * (e / 4) + 4 * h + (e % 4);
+        if (t < T) y[(size_t)t * N + n] = f32_to_bf16(acc[mb][e]);
+      }
+  }
+}
+
 hipError_t launch_affine8_gemm(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
                                const uint16_t* biases, int T, int K, int N, uint16_t* y, hipStream_t s) {
   const int n_tiles = (N + kA8N - 1) / kA8N, m_tiles = (T + kA8M - 1) / kA8M;
-  launch_kernel("affine8_gemm", affine8_gemm_kernel, dim3(n_tiles * m_tiles), dim3(kA8Threads), 0, s, x,
-                reinterpret_cast<const uint8_t*>(codes), scales, biases, T, K, N, n_tiles, y);
+  // the HBM -> LDS form: K a multiple of 512 (blocks of 8 groups), 16-byte
+  // aligned scale and bias rows, and 32-bit load offsets within a tile
+  const bool dma = K % 512 == 0 && ((uintptr_t)scales & 15) == 0 && ((uintptr_t)biases & 15) == 0 &&
+                   (uint64_t)kA8M * K * 2 < (1ull << 31);
+  if (dma)
+    launch_kernel("affine8_gemm", affine8_gemm_dma_kernel, dim3(n_tiles * m_tiles), dim3(kA8Threads), 0, s, x,
+                  reinterpret_cast<const uint8_t*>(codes), scales, biases, T, K, N, n_tiles, y);
+  else
+    launch_kernel("affine8_gemm", affine8_gemm_kernel, dim3(n_tiles * m_tiles), dim3(kA8Threads), 0, s, x,
+                  reinterpret_cast<const uint8_t*>(codes), scales, biases, T, K, N, n_tiles, y);
   return hipGetLastError();
 }
 
