@@ -568,12 +568,9 @@ __global__ __launch_bounds__(64 * kFlatDecodeMaxK) void flat_down_kernel(FlatArg
 //
 // Selection, with 256 threads: thread t waits for the tags t, t + 256, ...
 // and turns each logit into a key (topk_key: unique, ordered as the
-// selection rule); wave 0 takes the largest key of each lane's stripe (keys
-// l, l + 64, ...); tau, the k-th largest of these 64 maxima, is at most the
-// k-th largest key, since k stripes reach it. So the top-k keys are all
-// >= tau, and the keys >= tau (at most k stripes' worth) are ranked among
-// themselves by counting: a key's rank among them is its rank among all keys.
-// A workgroup that starts once the record is out reads k words instead.
+// selection rule); one wave then takes the k largest keys in k rounds of a
+// wave-wide maximum (wave_topk: DPP, no barrier). A workgroup that starts once
+// the record is out reads k words instead.
 struct RouteFuse {
   const float* wr;    // [E][H] router weights, f32
   float* logits;      // [E] out
@@ -596,14 +593,54 @@ __device__ __forceinline__ void st_tag(uint64_t* p, uint32_t call, uint32_t v) {
   __hip_atomic_store(p, ((uint64_t)call << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Maximum of v over the wave, uniform: DPP row shifts leave each 16-lane
+// row's maximum in its lane 15, two row broadcasts carry them to lane 63
+// (lanes without a source read 0, the identity here)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true));  // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true));  // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true));  // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true));  // row_shr:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xF, 0xF, true));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xF, 0xF, true));  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// The k largest of the E keys (E <= 64 PER), by one wave: lane l holds keys
+// l, l + 64, ... in registers; each round takes the largest remaining key of
+// the wave (its high word, then among the lanes holding that the low word:
+// keys are unique) and removes it from its lane. Writes s_idx[round] and
+// sel_v[round] in the order of the selection rule, as ranking all keys does.
+template <int PER>
+__device__ __forceinline__ void wave_topk(const uint64_t* keys, const float* lv, int E, int k, int* s_idx,
+                                          float* sel_v) {
+  const int lane = threadIdx.x & 63;
+  uint64_t kk[PER];
+#pragma unroll
+  for (int i = 0; i < PER; i++) kk[i] = lane + 64 * i < E ? keys[lane + 64 * i] : 0;  // 0: below every key
+  for (int round = 0; round < k; round++) {
+    uint64_t h = kk[0];
+#pragma unroll
+    for (int i = 1; i < PER; i++) h = kk[i] > h ? kk[i] : h;
+    const uint32_t hi = wave_max_u32((uint32_t)(h >> 32));
+    const uint32_t lo = wave_max_u32((uint32_t)(h >> 32) == hi ? (uint32_t)h : 0u);
+    const uint64_t win = ((uint64_t)hi << 32) | lo;
+#pragma unroll
+    for (int i = 0; i < PER; i++)
+      if (kk[i] == win) kk[i] = 0;
+    if (lane == 0) {
+      const int e = topk_key_expert(win);
+      s_idx[round] = e;
+      sel_v[round] = lv[e];
+    }
+  }
+}
+
 __global__ __launch_bounds__(kDecThreads) void flat_route_gateup_kernel(FlatArgs a, RouteFuse r) {
   extern __shared__ __attribute__((aligned(16))) uint32_t xs[];  // [H/2]
   __shared__ uint64_t keys[1024];
   __shared__ float lv[1024];
-  __shared__ uint64_t lmax[64];
-  __shared__ uint64_t cand[kFlatDecodeMaxK * 16];  // k stripes of at most 1024 / 64 keys
-  __shared__ uint64_t tau;
-  __shared__ int ncand, failed, have_route;
+  __shared__ int failed, have_route;
   __shared__ float red[kDecWaves];
   __shared__ float sel_v[kFlatDecodeMaxK];
   __shared__ int s_idx[kFlatDecodeMaxK];
@@ -619,10 +656,8 @@ __global__ __launch_bounds__(kDecThreads) void flat_route_gateup_kernel(FlatArgs
   }
   const int blk = blockIdx.x - E, nblk = gridDim.x - E;
   if (tid == 0) {
-    ncand = 0;
     failed = 0;
     have_route = 1;
-    tau = ~0ull;
   }
   if (tid < kFlatDecodeMaxK) s_idx[tid] = -1;
   __syncthreads();
@@ -660,36 +695,19 @@ __global__ __launch_bounds__(kDecThreads) void flat_route_gateup_kernel(FlatArgs
       if (tid == 0) atomicOr(r.status, kStatusRouteTimeout);
       return;
     }
-    if (wave == 0) {
-      uint64_t m = 0;
-      for (int e = lane; e < E; e += 64) m = max(m, keys[e]);
-      lmax[lane] = m;
-    }
-    __syncthreads();
-    if (wave == 0) {
-      const uint64_t m = lmax[lane];
-      int ahead = 0;
-      for (int j = 0; j < 64; j++) ahead += lmax[j] > m ? 1 : 0;
-      if (ahead == k - 1 && m != 0) tau = m;  // exactly one lane
-    }
-    __syncthreads();
-    constexpr int kCand = kFlatDecodeMaxK * 16;
-    for (int e = tid; e < E; e += kDecThreads)
-      if (keys[e] >= tau) {
-        const int pos = atomicAdd(&ncand, 1);
-        if (pos < kCand) cand[pos] = keys[e];
-      }
-    __syncthreads();
-    const int nc = min(ncand, kCand);
-    for (int i = tid; i < nc; i += kDecThreads) {
-      const uint64_t c = cand[i];
-      int rank = 0;
-      for (int j = 0; j < nc; j++) rank += cand[j] > c ? 1 : 0;
-      if (rank < k) {
-        const int e = topk_key_expert(c);
-        s_idx[rank] = e;
-        sel_v[rank] = lv[e];
-      }
+    // the selecting wave differs between neighbouring workgroups, so that the
+    // several workgroups on a CU select on different SIMDs
+    if (wave == (blk & (kDecWaves - 1))) {
+      if (E <= 64)
+        wave_topk<1>(keys, lv, E, k, s_idx, sel_v);
+      else if (E <= 128)
+        wave_topk<2>(keys, lv, E, k, s_idx, sel_v);
+      else if (E <= 256)
+        wave_topk<4>(keys, lv, E, k, s_idx, sel_v);
+      else if (E <= 512)
+        wave_topk<8>(keys, lv, E, k, s_idx, sel_v);
+      else
+        wave_topk<16>(keys, lv, E, k, s_idx, sel_v);
     }
     __syncthreads();
     // one workgroup writes the outputs and the record (the first gate/up
