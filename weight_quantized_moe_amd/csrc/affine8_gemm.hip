@@ -54,27 +54,34 @@ __device__ __forceinline__ void u8x4_bf16(uint32_t w, uint32_t& lo, uint32_t& hi
 // from 0 (the products are exact). The words go through a plain array: this
 // compiler turned a bit cast of a vector element access (v.y) into a read of
 // element 0.
-__device__ __forceinline__ float piece_sum(const u32x4& v) {
+__device__ __forceinline__ float piece_sum(const u32x4& v, float s) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   const bf16x2 one2 = __builtin_bit_cast(bf16x2, 0x3F803F80u);
-  float s = 0.0f;
 #pragma unroll
   for (int q = 0; q < 4; q++) s = __builtin_amdgcn_fdot2_f32_bf16(one2, __builtin_bit_cast(bf16x2, w[q]), s, false);
   return s;
 }
 
-// total of s over each group of 8 consecutive lanes, in the group's first
-// lane (DPP: swap within pairs, then within quads, then the other quad of the
-// 8 through the half-row mirror; the other lanes hold partial totals)
-__device__ __forceinline__ float row8_sum(float s) {
-  s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, false));
-  s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x4E, 0xF, 0xF, false));
-  s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x141, 0xF, 0xF, false));
-  return s;
-}
-
 // f32 -> bf16 by truncation (used only where the value is exact in bf16)
 __device__ __forceinline__ uint32_t bf16_trunc(float v) { return __float_as_uint(v) >> 16; }
+
+// The group sum of an activation row: thread t takes row t / 2, pieces
+// 4 (t % 2) .. 4 (t % 2) + 3 (piece_sum in piece order), and the two halves
+// meet by one DPP swap of neighbouring lanes. Thread t % 2 == 0 splits the sum
+// exactly into three bf16 values x1 + x2 + x3 and stores them for the bias
+// MFMA: x1 | x2 << 16, x3.
+__device__ __forceinline__ void store_group_sum(float s, uint32_t (*xs)[2], int r, bool first) {
+  s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, true));
+  if (first) {
+    const float x1 = bf16_to_f32(f32_to_bf16(s));
+    const float r1 = s - x1;  // exact
+    const float x2 = bf16_to_f32(f32_to_bf16(r1));
+    const float x3 = r1 - x2;  // exact, and exact in bf16 (at most 8 significant bits left)
+    xs[r][0] = bf16_trunc(x1) | (bf16_trunc(x2) << 16);
+    xs[r][1] = bf16_trunc(x3);
+  }
+}
+
 
 // two waves per SIMD: the compiler keeps the 128 accumulators and the
 // fragments in 216 VGPRs (without the bound: 324 VGPRs and 128 AGPRs, one wave)
@@ -102,33 +109,25 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
   const int n = nt * kA8N + wave * 32 + l32;  // this lane's output row (MFMA column)
   const int nc = n < N ? n : N - 1;
   const uint8_t* crow = codes + (size_t)nc * K + 32 * h;
-  // activation pieces of this thread: p = tid + 256 i, row p / 8, piece p % 8
+  // activation pieces of this thread: row tid / 2, pieces 4 (tid % 2) + i
+  const int ar = tid >> 1, ah = tid & 1;
   u32x4 av[4];
   auto load_a = [&](int g) {
+    const int t = m0 + ar;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int p = tid + kA8Threads * i, r = p >> 3, j = p & 7;
-      const int t = m0 + r;
-      av[i] = t < T ? *reinterpret_cast<const u32x4*>(x + (size_t)t * K + 64 * g + 8 * j) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < 4; i++)
+      av[i] = t < T ? *reinterpret_cast<const u32x4*>(x + (size_t)t * K + 64 * g + 8 * (4 * ah + i))
+                    : u32x4{0u, 0u, 0u, 0u};
   };
-  // the pieces into LDS, and the group sums of the 128 rows (8 threads per
-  // row: consecutive lanes) split into three bf16 values
+  // the pieces into LDS, and the row's group sum
   auto store_a = [&](int buf) {
+    float s = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const int p = tid + kA8Threads * i, r = p >> 3, j = p & 7;
-      *reinterpret_cast<u32x4*>(&As[buf][r * 128 + 16 * a8_slot(r, j)]) = av[i];
-      const float s = row8_sum(piece_sum(av[i]));
-      if (j == 0) {
-        const float x1 = bf16_to_f32(f32_to_bf16(s));
-        const float r1 = s - x1;  // exact
-        const float x2 = bf16_to_f32(f32_to_bf16(r1));
-        const float x3 = r1 - x2;  // exact, and exact in bf16 (at most 8 significant bits left)
-        Xs[buf][r][0] = bf16_trunc(x1) | (bf16_trunc(x2) << 16);
-        Xs[buf][r][1] = bf16_trunc(x3);
-      }
+      *reinterpret_cast<u32x4*>(&As[buf][ar * 128 + 16 * a8_slot(ar, 4 * ah + i)]) = av[i];
+      s = piece_sum(av[i], s);
     }
+    store_group_sum(s, Xs[buf], ar, ah == 0);
   };
   u32x4 bc[2], bn[2];
   float sc = 0.0f, scn = 0.0f, bi = 0.0f, bin = 0.0f;
@@ -180,6 +179,10 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
         }
       }
     }
+#pragma unroll
+    for (int mb = 0; mb < 4; mb++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) acc[mb][e] = fmaf(sc, tmp[mb][e], acc[mb][e]);
     // bias: inputs 0..2 of a k-slice carry (x1, x2, x3) against (b, b, b)
     {
       const uint32_t bb = bf16_trunc(bi);
@@ -193,10 +196,6 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
         acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, bbf, acc[mb], 0, 0, 0);
       }
     }
-#pragma unroll
-    for (int mb = 0; mb < 4; mb++)
-#pragma unroll
-      for (int e = 0; e < 16; e++) acc[mb][e] = fmaf(sc, tmp[mb][e], acc[mb][e]);
     if (g + 1 < G) {
       store_a(buf ^ 1);
       bc[0] = bn[0];
@@ -234,10 +233,12 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
 //     (wave w loads 64 rows of one of the two arrays), double-buffered.
 // Per group g: wait for group g's loads (the only loads issued later are the
 // activations of group g + 1: vmcnt(4)), barrier, issue the next loads, then
-// the group sums from LDS, the group's MFMAs into tmp, a second barrier (the
-// group sums are complete), the bias MFMA and the scale fold: the same
-// operations in the same order as the kernel above, so the output is the
-// same bit for bit.
+// group g's sums from LDS into a double-buffered Xs, the bias MFMA of group
+// g - 1 (whose sums the barrier has completed), group g's MFMAs into tmp and
+// its scale fold; the last group's bias follows a barrier after the loop.
+// The accumulator sees the same operations in the same order as in the
+// kernel above (fold g, bias g, fold g + 1, ...), so the output is the same
+// bit for bit, with one barrier per group.
 constexpr int kA8DStages = 3;  // activation stages
 
 __device__ __forceinline__ int a8_cslot(int r, int p) { return p ^ ((r >> 2) & 3); }
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
   __shared__ __attribute__((aligned(16))) uint8_t As[kA8DStages][kA8M * 128];
   __shared__ __attribute__((aligned(16))) uint8_t Cs[2][kA8N * 64];            // [row][64 codes], swizzled
   __shared__ __attribute__((aligned(16))) uint16_t Ss[2][2][kA8N][8];          // [block][scale|bias][row][group]
-  __shared__ __attribute__((aligned(16))) uint32_t Xs[kA8M][2];               // group sums of x as bf16
+  __shared__ __attribute__((aligned(16))) uint32_t Xs[2][kA8M][2];            // group sums of x as bf16
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
@@ -309,6 +310,21 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
     for (int r = 0; r < 16; r++) acc[mb][r] = 0.0f;
 
+  // the bias of group gb for this lane's row cr (its sums in Xs[gb % 2],
+  // its bias in the scale block of gb)
+  auto bias_mfma = [&](int gb, int cr) {
+    const uint32_t bb = Ss[(gb >> 3) & 1][1][cr][gb & 7];
+    const bf16x8 bbf =
+        __builtin_bit_cast(bf16x8, h == 0 ? u32x4{bb | (bb << 16), bb, 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+    for (int mb = 0; mb < 4; mb++) {
+      const int r = 32 * mb + l32;
+      const bf16x8 xf = __builtin_bit_cast(
+          bf16x8, h == 0 ? u32x4{Xs[gb & 1][r][0], Xs[gb & 1][r][1], 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
+      acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, bbf, acc[mb], 0, 0, 0);
+    }
+  };
+
   issue_c(0);
   issue_a(0);
   if (G > 1) issue_a(1);
@@ -325,25 +341,21 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
     if (g + 1 < G) issue_c(g + 1);
     if (g + 2 < G) issue_a(g + 2);
     const uint8_t* A = As[g % kA8DStages];
-    // group sums of group g: thread t sums pieces (row p / 8, piece p % 8) for
-    // p = t + 256 i (piece_sum), the 8 pieces of a row added in the row's
-    // first lane (row8_sum); split exactly into three bf16 values
+    // group sums of group g (store_group_sum), used by group g's bias in the
+    // next step, after its barrier
+    {
+      const int ar = tid >> 1, ah = tid & 1;
+      float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int p = tid + kA8Threads * i, r = p >> 3, j = p & 7;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(A + r * 128 + 16 * a8_slot(r, j));
-      const float s = row8_sum(piece_sum(v));
-      if (j == 0) {
-        const float x1 = bf16_to_f32(f32_to_bf16(s));
-        const float r1 = s - x1;  // exact
-        const float x2 = bf16_to_f32(f32_to_bf16(r1));
-        const float x3 = r1 - x2;  // exact, and exact in bf16 (at most 8 significant bits left)
-        Xs[r][0] = bf16_trunc(x1) | (bf16_trunc(x2) << 16);
-        Xs[r][1] = bf16_trunc(x3);
-      }
+      for (int i = 0; i < 4; i++)
+        s = piece_sum(*reinterpret_cast<const u32x4*>(A + ar * 128 + 16 * a8_slot(ar, 4 * ah + i)), s);
+      store_group_sum(s, Xs[g & 1], ar, ah == 0);
     }
-    // B: this lane's 32 codes (row 32 w + l32, bytes 32 h .. 32 h + 31)
     const int cr = 32 * wave + l32;
+    // bias of group g - 1: inputs 0..2 of a k-slice carry (x1, x2, x3)
+    // against (b, b, b)
+    if (g > 0) bias_mfma(g - 1, cr);
+    // B: this lane's 32 codes (row 32 w + l32, bytes 32 h .. 32 h + 31)
     const uint8_t* crow = Cs[g & 1] + cr * 64;
     const u32x4 bc0 = *reinterpret_cast<const u32x4*>(crow + 16 * a8_cslot(cr, 2 * h));
     const u32x4 bc1 = *reinterpret_cast<const u32x4*>(crow + 16 * a8_cslot(cr, 2 * h + 1));
@@ -371,27 +383,14 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
         }
       }
     }
-    step_barrier();  // the group sums are complete
-    const uint16_t sc = Ss[(g >> 3) & 1][0][cr][g & 7], bi = Ss[(g >> 3) & 1][1][cr][g & 7];
-    // bias: inputs 0..2 of a k-slice carry (x1, x2, x3) against (b, b, b)
-    {
-      const uint32_t bb = bi;
-      const bf16x8 bbf = __builtin_bit_cast(
-          bf16x8, h == 0 ? u32x4{bb | (bb << 16), bb, 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
-#pragma unroll
-      for (int mb = 0; mb < 4; mb++) {
-        const int r = 32 * mb + l32;
-        const bf16x8 xf =
-            __builtin_bit_cast(bf16x8, h == 0 ? u32x4{Xs[r][0], Xs[r][1], 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, bbf, acc[mb], 0, 0, 0);
-      }
-    }
-    const float scf = bf16_to_f32(sc);
+    const float scf = bf16_to_f32(Ss[(g >> 3) & 1][0][cr][g & 7]);
 #pragma unroll
     for (int mb = 0; mb < 4; mb++)
 #pragma unroll
       for (int e = 0; e < 16; e++) acc[mb][e] = fmaf(scf, tmp[mb][e], acc[mb][e]);
   }
+  step_barrier();  // the last group's sums are complete
+  bias_mfma(G - 1, 32 * wave + l32);
   // element e of lane l: token 8 (e / 4) + 4 h + e % 4 of block mb, row n
   if (n < N) {
 #pragma unroll
