@@ -309,19 +309,28 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
   for (int mb = 0; mb < 4; mb++)
 #pragma unroll
     for (int r = 0; r < 16; r++) acc[mb][r] = 0.0f;
+  const int cr = 32 * wave + l32;         // this lane's code row in the tile
+  const int ar = tid >> 1, ah = tid & 1;  // group sums: row tid / 2, pieces 4 (tid % 2) ..
 
-  // the bias of group gb for this lane's row cr (its sums in Xs[gb % 2],
-  // its bias in the scale block of gb)
-  auto bias_mfma = [&](int gb, int cr) {
-    const uint32_t bb = Ss[(gb >> 3) & 1][1][cr][gb & 7];
+  // a group's bias: inputs 0..2 of a k-slice carry the sums (x1, x2, x3) of
+  // row 32 mb + l32 (xv[mb]) against (b, b, b), b this lane's bias bits
+  auto bias_mfma = [&](const uint32_t (&xv)[4][2], uint32_t bb) {
     const bf16x8 bbf =
         __builtin_bit_cast(bf16x8, h == 0 ? u32x4{bb | (bb << 16), bb, 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
     for (int mb = 0; mb < 4; mb++) {
-      const int r = 32 * mb + l32;
-      const bf16x8 xf = __builtin_bit_cast(
-          bf16x8, h == 0 ? u32x4{Xs[gb & 1][r][0], Xs[gb & 1][r][1], 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
+      const bf16x8 xf =
+          __builtin_bit_cast(bf16x8, h == 0 ? u32x4{xv[mb][0], xv[mb][1], 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
       acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, bbf, acc[mb], 0, 0, 0);
+    }
+  };
+  // group gb's sums and this lane's bias, from LDS
+  auto read_bias = [&](int gb, uint32_t (&xv)[4][2], uint32_t& bb) {
+    bb = Ss[(gb >> 3) & 1][1][cr][gb & 7];
+#pragma unroll
+    for (int mb = 0; mb < 4; mb++) {
+      xv[mb][0] = Xs[gb & 1][32 * mb + l32][0];
+      xv[mb][1] = Xs[gb & 1][32 * mb + l32][1];
     }
   };
 
@@ -341,56 +350,83 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
     if (g + 1 < G) issue_c(g + 1);
     if (g + 2 < G) issue_a(g + 2);
     const uint8_t* A = As[g % kA8DStages];
-    // group sums of group g (store_group_sum), used by group g's bias in the
-    // next step, after its barrier
-    {
-      const int ar = tid >> 1, ah = tid & 1;
-      float s = 0.0f;
+    // the step's small LDS reads, all issued before the MFMAs: this thread's
+    // pieces for group g's sums, the lane's 32 codes (row cr, bytes 32 h ..
+    // 32 h + 31), group g - 1's sums and bias, group g's scale
+    u32x4 pv[4];
 #pragma unroll
-      for (int i = 0; i < 4; i++)
-        s = piece_sum(*reinterpret_cast<const u32x4*>(A + ar * 128 + 16 * a8_slot(ar, 4 * ah + i)), s);
-      store_group_sum(s, Xs[g & 1], ar, ah == 0);
-    }
-    const int cr = 32 * wave + l32;
-    // bias of group g - 1: inputs 0..2 of a k-slice carry (x1, x2, x3)
-    // against (b, b, b)
-    if (g > 0) bias_mfma(g - 1, cr);
-    // B: this lane's 32 codes (row 32 w + l32, bytes 32 h .. 32 h + 31)
+    for (int i = 0; i < 4; i++) pv[i] = *reinterpret_cast<const u32x4*>(A + ar * 128 + 16 * a8_slot(ar, 4 * ah + i));
     const uint8_t* crow = Cs[g & 1] + cr * 64;
     const u32x4 bc0 = *reinterpret_cast<const u32x4*>(crow + 16 * a8_cslot(cr, 2 * h));
     const u32x4 bc1 = *reinterpret_cast<const u32x4*>(crow + 16 * a8_cslot(cr, 2 * h + 1));
-    f32x16 tmp[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; kk++) {
-      // slice kk: bytes 8 kk .. 8 kk + 7 of the lane's 32
+    uint32_t xv[4][2] = {}, bb = 0;
+    if (g > 0) read_bias(g - 1, xv, bb);
+    const uint32_t scb = Ss[(g >> 3) & 1][0][cr][g & 7];
+    __builtin_amdgcn_sched_barrier(0);
+    // slice kk: inputs 8 kk .. 8 kk + 7 of each lane half's 32; its A
+    // fragments and dequantized codes are read and prepared while the MFMAs
+    // of slice kk - 1 run (scheduling barriers keep the reads ahead)
+    auto codes_of = [&](int kk) {
       const uint32_t w0 = kk < 2 ? (kk == 0 ? bc0.x : bc0.z) : (kk == 2 ? bc1.x : bc1.z);
       const uint32_t w1 = kk < 2 ? (kk == 0 ? bc0.y : bc0.w) : (kk == 2 ? bc1.y : bc1.w);
       uint32_t q0, q1, q2, q3;
       u8x4_bf16(w0, q0, q1);
       u8x4_bf16(w1, q2, q3);
-      const bf16x8 bfr = __builtin_bit_cast(bf16x8, u32x4{q0, q1, q2, q3});
+      return __builtin_bit_cast(bf16x8, u32x4{q0, q1, q2, q3});
+    };
+    auto a_frag = [&](int mb, int kk) {
+      const int r = 32 * mb + l32;
+      return *reinterpret_cast<const bf16x8*>(A + r * 128 + 16 * a8_slot(r, 4 * h + kk));
+    };
+    f32x16 tmp[4];
+    float gsum = 0.0f;  // group g's sum over this thread's four pieces, one per slice
+    bf16x8 af[4], bfr = codes_of(0);
+#pragma unroll
+    for (int mb = 0; mb < 4; mb++) af[mb] = a_frag(mb, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) {
+      bf16x8 an[4], bn;
+      if (kk < 3) {
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++) an[mb] = a_frag(mb, kk + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk < 3) bn = codes_of(kk + 1);
 #pragma unroll
       for (int mb = 0; mb < 4; mb++) {
-        const int r = 32 * mb + l32;
-        const bf16x8 af = *reinterpret_cast<const bf16x8*>(A + r * 128 + 16 * a8_slot(r, 4 * h + kk));
         if (kk == 0) {
           f32x16 z;
 #pragma unroll
           for (int e = 0; e < 16; e++) z[e] = 0.0f;
-          tmp[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, z, 0, 0, 0);
+          tmp[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr, z, 0, 0, 0);
         } else {
-          tmp[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, tmp[mb], 0, 0, 0);
+          tmp[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr, tmp[mb], 0, 0, 0);
         }
       }
+      gsum = piece_sum(pv[kk], gsum);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk < 3) {
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++) af[mb] = an[mb];
+        bfr = bn;
+      }
     }
-    const float scf = bf16_to_f32(Ss[(g >> 3) & 1][0][cr][g & 7]);
+    // group g's sums (store_group_sum), for its bias in the next step
+    store_group_sum(gsum, Xs[g & 1], ar, ah == 0);
+    // group g - 1's bias, then group g's scale fold
+    if (g > 0) bias_mfma(xv, bb);
+    const float scf = bf16_to_f32(scb);
 #pragma unroll
     for (int mb = 0; mb < 4; mb++)
 #pragma unroll
       for (int e = 0; e < 16; e++) acc[mb][e] = fmaf(scf, tmp[mb][e], acc[mb][e]);
   }
   step_barrier();  // the last group's sums are complete
-  bias_mfma(G - 1, 32 * wave + l32);
+  {
+    uint32_t xv[4][2], bb;
+    read_bias(G - 1, xv, bb);
+    bias_mfma(xv, bb);
+  }
   // element e of lane l: token 8 (e / 4) + 4 h + e % 4 of block mb, row n
   if (n < N) {
 #pragma unroll
