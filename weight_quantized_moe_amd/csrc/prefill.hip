@@ -399,31 +399,61 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a)
   }
   wait_vmcnt<0>();  // the loads past the last step
 
-  // epilogue; accumulator element r of lane l is (row 8(r/4) + 4(l/32) + r%4,
-  // column l%32) of its 32 x 32 block
+  // Epilogue. Accumulator element r of lane l is (row 8(r/4) + 4(l/32) + r%4,
+  // column l%32) of its 32 x 32 block, so a lane's values lie in 16 rows of
+  // one column. Each 32-row block goes through the wave's own code stages
+  // (free once the k loop's loads have landed) and comes back as 16-byte
+  // row pieces, so each store writes whole row segments: 8 stores per wave
+  // for the bf16 mids instead of 64, 32 for the f32 rows instead of 128
+  // (down 1.88 -> 1.77 ms on the T = 8192 workload). 16-byte groups are
+  // XOR-swizzled by row bit 2, so the two lane halves' writes (rows 4 apart)
+  // fall in different banks.
+  if (NPROJ == 2) {
+    uint16_t* const tb = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(B0));  // [32 rows][32 mids]
 #pragma unroll
-  for (int ms = 0; ms < 4; ms++)
+    for (int ms = 0; ms < 4; ms++) {
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const int row = 32 * ms + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (row >= rows) continue;
-      if (NPROJ == 2) {
-        const int n = n0 + 32 * wave + (lane & 31);
-        if (n < N) {
-          const float g = t_p[0] * acc[ms][0][r];
-          const float u = t_p[NPROJ - 1] * acc[ms][1][r];
-          a.mid[(size_t)(row0 + row) * N + n] = f32_to_bf16(silu_mul(g, u));
+      for (int r = 0; r < 16; r++) {
+        const int rb = 8 * (r >> 2) + 4 * h + (r & 3), col = lane & 31;
+        const float g = t_p[0] * acc[ms][0][r];
+        const float u = t_p[NPROJ - 1] * acc[ms][1][r];
+        tb[rb * 32 + 8 * ((col >> 3) ^ (2 * ((rb >> 2) & 1))) + (col & 7)] = f32_to_bf16(silu_mul(g, u));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const int rb = (lane >> 2) + 16 * j, cg = lane & 3, row = 32 * ms + rb;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(tb + rb * 32 + 8 * (cg ^ (2 * ((rb >> 2) & 1))));
+        const int n = n0 + 32 * wave + 8 * cg;  // N % 8 == 0: n < N covers all 8
+        if (row < rows && n < N) *reinterpret_cast<u32x4*>(a.mid + (size_t)(row0 + row) * N + n) = v;
+      }
+    }
+  } else {
+    float* const tb[2] = {reinterpret_cast<float*>(const_cast<uint8_t*>(B0)),
+                          reinterpret_cast<float*>(const_cast<uint8_t*>(B1))};  // [32 rows][32 columns] per f
+#pragma unroll
+    for (int ms = 0; ms < 4; ms++) {
+#pragma unroll
+      for (int f = 0; f < 2; f++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int rb = 8 * (r >> 2) + 4 * h + (r & 3), col = lane & 31;
+          tb[f][rb * 32 + 4 * ((col >> 2) ^ (4 * ((rb >> 2) & 1))) + (col & 3)] = acc[ms][f][r];
         }
-      } else {
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int rb = (lane >> 3) + 8 * j, cg = lane & 7, row = 32 * ms + rb;
         const int pair = out_pair[row];
         const float wp = out_w[row] * t_p[0];
 #pragma unroll
         for (int f = 0; f < 2; f++) {
-          const int n = n0 + kWR * wave + 32 * f + (lane & 31);
-          if (n < N) a.part[(size_t)pair * N + n] = wp * acc[ms][f][r];
+          const f32x4 v = *reinterpret_cast<const f32x4*>(tb[f] + rb * 32 + 4 * (cg ^ (4 * ((rb >> 2) & 1))));
+          const int n = n0 + kWR * wave + 32 * f + 4 * cg;  // N % 4 == 0: n < N covers all 4
+          if (row < rows && n < N)
+            *reinterpret_cast<f32x4*>(a.part + (size_t)pair * N + n) = f32x4{wp * v.x, wp * v.y, wp * v.z, wp * v.w};
         }
       }
     }
+  }
 }
 
 static PrefillArgs make_args(const BankView& b, int k, const RouteTables& rt) {
