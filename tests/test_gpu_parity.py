@@ -553,6 +553,27 @@ def test_forward_tiny_ragged_and_residual(tiny_bank):
         check_bf16_of(yb, yf, "tiny ragged bf16")
 
 
+def test_forward_partial_output_tiles():
+    # H = 320, I = 192: the grouped GEMM's last n-tile is partial in both
+    # launches (gate/up 128 output columns a tile, down 256), so the
+    # epilogues' column masks and their row-piece stores meet a tile edge;
+    # K of 5 and 3 k-steps (odd) and ragged row tiles
+    H, I, E, T, k = 320, 192, 8, 150, 2
+    say(f"partial output tiles H={H} I={I} E={E} T={T}")
+    bank, _ = W.build_bank(3, H, I, E)
+    recs = host_records(3, range(E), H, I)
+    x = synth.activations(91, T, H)
+    res = synth.activations(92, T, H)
+    lg = np.random.default_rng(9).normal(size=(T, E)).astype(np.float32)
+    lg[:, 5] += 2.0
+    idx, w = oracle.route_topk(lg, k)
+    ref_f, _ = oracle.moe_forward(recs, E, H, I, x, idx, w, residual=res)
+    for flags in (2, 4):
+        yf, yb = gpu_forward(bank, x, idx, w, k, flags, residual=res)
+        check_f32(yf, ref_f, f"partial tiles flags={flags}")
+        check_bf16_of(yb, yf, "partial tiles bf16")
+
+
 def test_forward_single_token_paths(tiny_bank):
     # one token takes the flat kernels (k <= 16); k = 16 is their largest case,
     # the residual is folded into their combine; flags=2 forces the same path
