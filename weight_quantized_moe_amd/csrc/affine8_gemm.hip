@@ -232,13 +232,17 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
 //   - scales and biases: 16 bytes (8 groups) of each row, a block ahead
 //     (wave w loads 64 rows of one of the two arrays), double-buffered.
 // Per group g: wait for group g's loads (the only loads issued later are the
-// activations of group g + 1: vmcnt(4)), barrier, issue the next loads, then
-// group g's sums from LDS into a double-buffered Xs, the bias MFMA of group
-// g - 1 (whose sums the barrier has completed), group g's MFMAs into tmp and
-// its scale fold; the last group's bias follows a barrier after the loop.
-// The accumulator sees the same operations in the same order as in the
-// kernel above (fold g, bias g, fold g + 1, ...), so the output is the same
-// bit for bit, with one barrier per group.
+// activations of group g + 1: vmcnt(4)), barrier, issue the next loads; read
+// the step's small LDS operands together (the pieces of group g's sums, the
+// lane's codes, group g - 1's sums and bias, group g's scale); then group g's
+// MFMAs into tmp, each slice's A fragments and codes prepared while the
+// previous slice's MFMAs run and one piece of the sums added per slice; store
+// group g's sums into a double-buffered Xs; the bias MFMA of group g - 1
+// (whose sums the barrier has completed); group g's scale fold. The last
+// group's bias follows a barrier after the loop. The accumulator sees the
+// same operations in the same order as in the kernel above (fold g, bias g,
+// fold g + 1, ...), so the output is the same bit for bit, with one barrier
+// per group.
 constexpr int kA8DStages = 3;  // activation stages
 
 __device__ __forceinline__ int a8_cslot(int r, int p) { return p ^ ((r >> 2) & 3); }
