@@ -477,26 +477,33 @@ __global__ __launch_bounds__(64 * kFlatDecodeMaxK) void flat_down_kernel(FlatArg
                    : static_cast<void*>(static_cast<uint16_t*>(a0.y) + (size_t)tok * a0.H);
   constexpr int G = 8, R = 64 / G, QB = 5;
   extern __shared__ __attribute__((aligned(16))) uint32_t ms[];  // [k][I/2]
-  __shared__ int s_idx[kFlatDecodeMaxK];
-  __shared__ float s_w[kFlatDecodeMaxK];
   __shared__ float s_d[kFlatDecodeMaxK][R];
   const int H = a.H, I = a.I, k = a.k, nquads = I / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rsub = lane / G, sub = lane % G;
   const int r = blockIdx.x * R + rsub;
   const bool row_ok = r < H;
-  if (threadIdx.x < k) {
-    const int e = a.idx[threadIdx.x];
-    s_idx[threadIdx.x] = (e >= 0 && e < a.E) ? e : -1;
-    s_w[threadIdx.x] = a.w[threadIdx.x];
-  }
-  // the k waves copy the mids, all chunks at once, into the swizzled layout
-  dma_copy_lds_swz(a.mid, ms, (uint32_t)(k * I * 2), k);
-  wait_vmcnt<0>();
-  __syncthreads();
   {
     const int j = wave;  // one wave per pair
-    const int e = s_idx[j];
+    int e = a.idx[j];
+    e = (e >= 0 && e < a.E) ? e : -1;
+    const float wj = a.w[j];
+    // this pair's mids (I * 2 bytes, whole KiB chunks) into its part of the
+    // swizzled buffer, by this wave alone
+    {
+      const uint8_t* base = uniform_ptr(a.mid);
+      const uint32_t l0 = lds_addr(ms);
+      // whole 64-chunk loads covering the pair's chunks [8 q0, 8 q0 + 8 nquads);
+      // a load that straddles two pairs is made by both waves (the same
+      // bytes to the same places)
+      const int p0 = 8 * j * nquads, p1 = 8 * (j + 1) * nquads, ptot = 8 * k * nquads;
+      for (int c = p0 / 64; 64 * c < p1; c++) {
+        const uint32_t pos = c * 64 + lane;
+        const uint32_t q = pos >> 3;
+        const uint32_t off = 16u * (8u * q + ((pos & 7u) ^ (q & 7u)));
+        if ((int)pos < ptot) dma16(base, off, __builtin_amdgcn_readfirstlane(l0 + c * 1024));
+      }
+    }
     float ad = 0.0f;
     if (e >= 0) {
       const uint8_t* rec = a.bank + (size_t)e * a.stride;
@@ -511,6 +518,10 @@ __global__ __launch_bounds__(64 * kFlatDecodeMaxK) void flat_down_kernel(FlatArg
           const int qd = qb + sub + G * i;
           if (row_ok && qd < nquads) vd[i] = load_quad(cd, sd, qd);
         }
+        // the mids copy and the weights have landed (the copy was issued first)
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<0>();
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < QB; i++) {
           const int qd = qb + sub + G * i;
@@ -526,8 +537,9 @@ __global__ __launch_bounds__(64 * kFlatDecodeMaxK) void flat_down_kernel(FlatArg
         }
       }
     }
+    wait_vmcnt<0>();  // (no expert: the copy still lands before the workgroup ends)
     const float d = group_sum_last<G>(ad);
-    if (sub == G - 1) s_d[j][rsub] = (e >= 0) ? s_w[j] * d : 0.0f;
+    if (sub == G - 1) s_d[j][rsub] = (e >= 0) ? wj * d : 0.0f;
   }
   __syncthreads();
   if (threadIdx.x < R) {
