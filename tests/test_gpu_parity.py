@@ -1005,10 +1005,11 @@ def test_affine8_and_rmsnorm_unaligned_rows():
         check_bf16(to_np_bits(yr), oracle.bf16_to_f32(oracle.rmsnorm(xr, 1e-6)), f"rmsnorm unaligned H={H}")
 
 
-@pytest.mark.parametrize("T,K,N", [(300, 256, 200), (64, 128, 64), (129, 512, 130)])
+@pytest.mark.parametrize("T,K,N", [(300, 256, 200), (64, 128, 64), (129, 512, 130), (96, 1088, 200)])
 def test_affine8_gemm_ragged(T, K, N):
     # from 64 tokens the linear runs as the MFMA GEMM: ragged token and row
-    # tiles, K of 2 to 8 groups
+    # tiles, K of 2 to 8 groups; 96 x 1088 x 200 (two tiles, 17 groups) splits
+    # K into three ranges of whole 8-group blocks, the last holding one group
     v = synth.resident_weights(14, N, K)
     codes, scales, biases = oracle.q8_quantize(v)
     x = synth.activations(15, T, K)
@@ -1048,10 +1049,12 @@ def test_affine8_gemm_dma_form_matches_register_form(T, K, N):
     assert np.array_equal(to_np_bits(y), to_np_bits(y2)), "HBM -> LDS and register forms differ"
 
 
-def test_affine8_gemm_full_shape_sampled():
-    # a 5120 x 5120 resident over 1,024 tokens (8 token tiles x 40 row tiles);
-    # the oracle on 24 sampled tokens, every output row
-    T, K, N = 1024, 5120, 5120
+@pytest.mark.parametrize("T", [256, 1024])
+def test_affine8_gemm_full_shape_sampled(T):
+    # a 5120 x 5120 resident over 1,024 tokens (8 token tiles x 40 row tiles)
+    # and over 256 (2 x 40 tiles: K split into five ranges, partial sums added
+    # in range order); the oracle on sampled tokens, every output row
+    K, N = 5120, 5120
     v = synth.resident_weights(16, N, K)
     codes, scales, biases = oracle.q8_quantize(v)
     x = synth.activations(17, T, K)
@@ -1059,9 +1062,9 @@ def test_affine8_gemm_full_shape_sampled():
     wq.affine8_g64_linear(bf16_tensor(x), torch.from_numpy(codes.view(np.int32)).to(DEV),
                           bf16_tensor(scales), bf16_tensor(biases), T, K, N, y)
     torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, 511, 1023], np.random.default_rng(18).integers(0, T, 18)]))
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, T // 2 - 1, T - 1], np.random.default_rng(18).integers(0, T, 18)]))
     ref_f, _ = oracle.affine8_linear(x[rows], codes, scales, biases)
-    check_bf16(to_np_bits(y)[rows], ref_f, "affine8 gemm 1024x5120x5120 sampled")
+    check_bf16(to_np_bits(y)[rows], ref_f, f"affine8 gemm {T}x5120x5120 sampled")
 
 
 # ---- the stacked decode workload: 12 chained layers ------------------------------------

@@ -61,7 +61,7 @@ def test_affine8_gemm_dma_kernel_waits_are_its_own():
     kernel must be one of its own HBM -> LDS loads, and every vmcnt wait one
     of its own."""
     asm = _device_asm(os.path.join(B.SRC, "affine8_gemm.hip"))
-    body = _function(asm, "_ZN3moe23affine8_gemm_dma_kernelEPKtPKhS1_S1_iiiiPt")
+    body = _function(asm, "_ZN3moe23affine8_gemm_dma_kernelEPKtPKhS1_S1_iiiiiPtPf")
     lines = body.splitlines()
     assert sum("global_load_lds_dwordx4" in l for l in lines) >= 7
     assert not any(re.search(r"global_load_(?!lds)|buffer_load|scratch_|flat_load", l) for l in lines)
@@ -76,7 +76,7 @@ def test_affine8_gemm_group_sums_read_all_four_words():
     Every run of four accumulating v_dot2 into one register must read four
     different source registers."""
     asm = _device_asm(os.path.join(B.SRC, "affine8_gemm.hip"))
-    for name in ("_ZN3moe19affine8_gemm_kernelEPKtPKhS1_S1_iiiiPt", "_ZN3moe23affine8_gemm_dma_kernelEPKtPKhS1_S1_iiiiPt"):
+    for name in ("_ZN3moe19affine8_gemm_kernelEPKtPKhS1_S1_iiiiiPtPf", "_ZN3moe23affine8_gemm_dma_kernelEPKtPKhS1_S1_iiiiiPtPf"):
         dots = [m.groups() for l in _function(asm, name).splitlines()
                 for m in [re.search(r"v_dot2c_f32_bf16_e32 (v\d+), 0x3f803f80, (v\d+)", l)] if m]
         assert len(dots) >= 8 and len(dots) % 4 == 0, (name, len(dots))

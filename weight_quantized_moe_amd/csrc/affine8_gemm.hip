@@ -89,13 +89,14 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
                                                                   const uint8_t* __restrict__ codes,
                                                                   const uint16_t* __restrict__ scales,
                                                                   const uint16_t* __restrict__ biases, int T,
-                                                                  int K, int N, int n_tiles,
-                                                                  uint16_t* __restrict__ y) {
+                                                                  int K, int N, int n_tiles, int gps,
+                                                                  uint16_t* __restrict__ y, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint8_t As[2][kA8M * 128];
   __shared__ __attribute__((aligned(16))) uint32_t Xs[2][kA8M][2];  // group sums of x as bf16 (x1, x2 | x3, 0)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int G = K / 64;
+  const int g0 = (int)blockIdx.y * gps, g1 = min(G, g0 + gps);  // this split's groups
   int mt, nt;
   if (n_tiles % 8 == 0) {
     const int per = n_tiles / 8, i = blockIdx.x / 8;
@@ -144,13 +145,13 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
     for (int r = 0; r < 16; r++) acc[mb][r] = 0.0f;
 
-  load_a(0);
-  load_b(0, bc, sc, bi);
-  store_a(0);
+  load_a(g0);
+  load_b(g0, bc, sc, bi);
+  store_a(g0 & 1);
   __syncthreads();
-  for (int g = 0; g < G; g++) {
+  for (int g = g0; g < g1; g++) {
     const int buf = g & 1;
-    if (g + 1 < G) {
+    if (g + 1 < g1) {
       load_a(g + 1);
       load_b(g + 1, bn, scn, bin);
     }
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
         acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, bbf, acc[mb], 0, 0, 0);
       }
     }
-    if (g + 1 < G) {
+    if (g + 1 < g1) {
       store_a(buf ^ 1);
       bc[0] = bn[0];
       bc[1] = bn[1];
@@ -212,7 +213,12 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
       for (int e = 0; e < 16; e++) {
         const int t = m0 + 32 * mb + 8 * (e / 4) + 4 * h + (e % 4);
-        if (t < T) y[(size_t)t * N + n] = f32_to_bf16(acc[mb][e]);
+        if (t < T) {
+          if (part)
+            part[((size_t)blockIdx.y * T + t) * N + n] = acc[mb][e];
+          else
+            y[(size_t)t * N + n] = f32_to_bf16(acc[mb][e]);
+        }
       }
   }
 }
@@ -249,7 +255,7 @@ __device__ __forceinline__ int a8_cslot(int r, int p) { return p ^ ((r >> 2) & 3
 
 __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2))) void affine8_gemm_dma_kernel(
     const uint16_t* __restrict__ x, const uint8_t* codes, const uint16_t* scales, const uint16_t* biases, int T,
-    int K, int N, int n_tiles, uint16_t* __restrict__ y) {
+    int K, int N, int n_tiles, int gps, uint16_t* __restrict__ y, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint8_t As[kA8DStages][kA8M * 128];
   __shared__ __attribute__((aligned(16))) uint8_t Cs[2][kA8N * 64];            // [row][64 codes], swizzled
   __shared__ __attribute__((aligned(16))) uint16_t Ss[2][2][kA8N][8];          // [block][scale|bias][row][group]
@@ -269,6 +275,7 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
   }
   const int m0 = mt * kA8M, n0 = nt * kA8N;
   const int n = n0 + wave * 32 + l32;  // this lane's output row (MFMA column)
+  const int g0 = (int)blockIdx.y * gps, g1 = min(G, g0 + gps);  // this split's groups (whole blocks of 8)
 
   // load sources: uniform bases and per-lane 32-bit offsets
   const uint8_t* xb = uniform_ptr(x + (size_t)m0 * K);
@@ -338,21 +345,21 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
     }
   };
 
-  issue_c(0);
-  issue_a(0);
-  if (G > 1) issue_a(1);
-  for (int g = 0; g < G; g++) {
+  issue_c(g0);
+  issue_a(g0);
+  if (g0 + 1 < g1) issue_a(g0 + 1);
+  for (int g = g0; g < g1; g++) {
     // group g's codes, scales and activations have landed for this wave: the
     // loads issued after them are group g + 1's activations
-    if (g + 1 < G)
+    if (g + 1 < g1)
       wait_vmcnt<4>();
     else
       wait_vmcnt<0>();
     // every wave's loads of group g have landed, and every wave is done with
     // group g - 1 (codes buffer (g + 1) % 2, activation stage (g + 2) % 3)
     step_barrier();
-    if (g + 1 < G) issue_c(g + 1);
-    if (g + 2 < G) issue_a(g + 2);
+    if (g + 1 < g1) issue_c(g + 1);
+    if (g + 2 < g1) issue_a(g + 2);
     const uint8_t* A = As[g % kA8DStages];
     // the step's small LDS reads, all issued before the MFMAs: this thread's
     // pieces for group g's sums, the lane's 32 codes (row cr, bytes 32 h ..
@@ -364,7 +371,7 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
     const u32x4 bc0 = *reinterpret_cast<const u32x4*>(crow + 16 * a8_cslot(cr, 2 * h));
     const u32x4 bc1 = *reinterpret_cast<const u32x4*>(crow + 16 * a8_cslot(cr, 2 * h + 1));
     uint32_t xv[4][2] = {}, bb = 0;
-    if (g > 0) read_bias(g - 1, xv, bb);
+    if (g > g0) read_bias(g - 1, xv, bb);
     const uint32_t scb = Ss[(g >> 3) & 1][0][cr][g & 7];
     __builtin_amdgcn_sched_barrier(0);
     // slice kk: inputs 8 kk .. 8 kk + 7 of each lane half's 32; its A
@@ -423,7 +430,7 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
     // group g's sums (store_group_sum), for its bias in the next step
     store_group_sum(gsum, Xs[g & 1], ar, ah == 0);
     // group g - 1's bias, then group g's scale fold
-    if (g > 0) bias_mfma(xv, bb);
+    if (g > g0) bias_mfma(xv, bb);
     const float scf = bf16_to_f32(scb);
 #pragma unroll
     for (int mb = 0; mb < 4; mb++)
@@ -433,7 +440,7 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
   step_barrier();  // the last group's sums are complete
   {
     uint32_t xv[4][2], bb;
-    read_bias(G - 1, xv, bb);
+    read_bias(g1 - 1, xv, bb);
     bias_mfma(xv, bb);
   }
   // element e of lane l: token 8 (e / 4) + 4 h + e % 4 of block mb, row n
@@ -443,25 +450,84 @@ __global__ __launch_bounds__(kA8Threads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
       for (int e = 0; e < 16; e++) {
         const int t = m0 + 32 * mb + 8 * (e / 4) + 4 * h + (e % 4);
-        if (t < T) y[(size_t)t * N + n] = f32_to_bf16(acc[mb][e]);
+        if (t < T) {
+          if (part)
+            part[((size_t)blockIdx.y * T + t) * N + n] = acc[mb][e];
+          else
+            y[(size_t)t * N + n] = f32_to_bf16(acc[mb][e]);
+        }
       }
   }
 }
 
+// y = bf16 of the splits' f32 partial sums, added in split order
+__global__ __launch_bounds__(256) void affine8_split_sum_kernel(const float* __restrict__ part, int S, size_t tn,
+                                                               uint16_t* __restrict__ y) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < tn; i += (size_t)gridDim.x * 256) {
+    float v = part[i];
+    for (int sp = 1; sp < S; sp++) v += part[(size_t)sp * tn + i];
+    y[i] = f32_to_bf16(v);
+  }
+}
+
+// workgroups of this GEMM resident at once on the current device (two per CU)
+static int gemm_slots() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return 2 * cus;
+}
+
 hipError_t launch_affine8_gemm(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
                                const uint16_t* biases, int T, int K, int N, uint16_t* y, hipStream_t s) {
-  const int n_tiles = (N + kA8N - 1) / kA8N, m_tiles = (T + kA8M - 1) / kA8M;
+  const int n_tiles = (N + kA8N - 1) / kA8N, m_tiles = (T + kA8M - 1) / kA8M, tiles = n_tiles * m_tiles;
+  const int G = K / 64;
+  // Few tiles (fewer than the CUs: a prefill of a few hundred tokens) leave
+  // most of the chip idle while each walks all G groups. Then K is split into
+  // S ranges of whole 8-group blocks (the largest even split whose
+  // workgroups still all fit at once); each range's sum, fold and bias go to
+  // f32 partials (stream-ordered scratch), added in range order into y.
+  int S = 1, gps = G;
+  const int slots = gemm_slots();
+  if (slots > 0 && 2 * tiles <= slots && G >= 16) {
+    const int nb = (G + 7) / 8;
+    for (int d = nb; d >= 2; d--)
+      if (nb % d == 0 && tiles * d <= slots) {
+        S = d;
+        break;
+      }
+    gps = (nb / S) * 8;
+  }
+  float* part = nullptr;
+  if (S > 1 && hipMallocAsync(reinterpret_cast<void**>(&part), (size_t)S * T * N * sizeof(float), s) != hipSuccess) {
+    (void)hipGetLastError();  // no scratch: the single-range form
+    S = 1;
+    gps = G;
+    part = nullptr;
+  }
   // the HBM -> LDS form: K a multiple of 512 (blocks of 8 groups), 16-byte
   // aligned scale and bias rows, and 32-bit load offsets within a tile
   const bool dma = K % 512 == 0 && ((uintptr_t)scales & 15) == 0 && ((uintptr_t)biases & 15) == 0 &&
                    (uint64_t)kA8M * K * 2 < (1ull << 31);
+  const dim3 grid(tiles, S);
   if (dma)
-    launch_kernel("affine8_gemm", affine8_gemm_dma_kernel, dim3(n_tiles * m_tiles), dim3(kA8Threads), 0, s, x,
-                  reinterpret_cast<const uint8_t*>(codes), scales, biases, T, K, N, n_tiles, y);
+    launch_kernel("affine8_gemm", affine8_gemm_dma_kernel, grid, dim3(kA8Threads), 0, s, x,
+                  reinterpret_cast<const uint8_t*>(codes), scales, biases, T, K, N, n_tiles, gps, y, part);
   else
-    launch_kernel("affine8_gemm", affine8_gemm_kernel, dim3(n_tiles * m_tiles), dim3(kA8Threads), 0, s, x,
-                  reinterpret_cast<const uint8_t*>(codes), scales, biases, T, K, N, n_tiles, y);
-  return hipGetLastError();
+    launch_kernel("affine8_gemm", affine8_gemm_kernel, grid, dim3(kA8Threads), 0, s, x,
+                  reinterpret_cast<const uint8_t*>(codes), scales, biases, T, K, N, n_tiles, gps, y, part);
+  hipError_t e = hipGetLastError();
+  if (S > 1) {
+    if (e == hipSuccess) {
+      const size_t tn = (size_t)T * N;
+      const unsigned blocks = (unsigned)std::min<size_t>((tn + 255) / 256, 4096);
+      launch_kernel("affine8_split_sum", affine8_split_sum_kernel, dim3(blocks), dim3(256), 0, s, part, S, tn, y);
+      e = hipGetLastError();
+    }
+    const hipError_t ef = hipFreeAsync(part, s);
+    if (e == hipSuccess) e = ef;
+  }
+  return e;
 }
 
 }  // namespace moe
