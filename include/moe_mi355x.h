@@ -267,9 +267,10 @@ int moe_status_clear(void* workspace, void* stream);
  * tiles number fewer than the device's CUs (a few hundred tokens), K is
  * split into ranges of whole 64 x 8 blocks whose f32 partial outputs are
  * added in range order: the call then takes S * T * N * 4 bytes of scratch
- * from the stream-ordered pool (hipMallocAsync / hipFreeAsync on `stream`,
- * so calls on different streams do not share it), and without it runs
- * unsplit. Errors: MOE_ESHAPE, MOE_EINVAL (null), MOE_EALIGN, MOE_EHIP. */
+ * from a stream-ordered memory pool the library keeps per device
+ * (hipMallocFromPoolAsync / hipFreeAsync on `stream`, so calls on different
+ * streams do not share it; the pool keeps its memory for reuse until the
+ * process ends), and without it runs unsplit. Errors: MOE_ESHAPE, MOE_EINVAL (null), MOE_EALIGN, MOE_EHIP. */
 int affine8_g64_linear(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
                        const uint16_t* biases, int T, int K, int N, uint16_t* y, void* stream);
 
