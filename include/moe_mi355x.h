@@ -267,7 +267,8 @@ int moe_status_clear(void* workspace, void* stream);
  * tiles number fewer than the device's CUs (a few hundred tokens), K is
  * split into ranges of whole 64 x 8 blocks whose f32 partial outputs are
  * added in range order: the call then takes S * T * N * 4 bytes of scratch
- * (at most 32 MiB: S times the tiles stays within two workgroups per CU)
+ * (at most 32 MiB on a 256-CU device: S times the tiles stays within two
+ * workgroups per CU)
  * from a stream-ordered memory pool the library keeps per device
  * (hipMallocFromPoolAsync / hipFreeAsync on `stream`, so calls on different
  * streams do not share it; the pool keeps its memory for reuse until the
