@@ -260,7 +260,7 @@ int moe_status_clear(void* workspace, void* stream);
  * x bf16 [T][K]; codes U32 [N][K/4] (4 codes per word, first in the low
  * byte); scales, biases bf16 [N][K/64]; y bf16 [T][N].
  * Rules: K % 64 == 0, N >= 1, T >= 0; codes 16-byte aligned, x 4-byte
- * aligned (MOE_EALIGN otherwise). From 64 tokens (env
+ * aligned (MOE_EALIGN otherwise). From 33 tokens (env
  * MOE_AFFINE8_GEMM_MIN_T) with x 16-byte aligned the call runs as a tiled
  * MFMA GEMM, below that as a bandwidth-bound pass that reads the weights
  * once per 16 tokens; both accumulate in f32. When the GEMM's 128 x 128

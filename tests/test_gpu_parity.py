@@ -1005,11 +1005,13 @@ def test_affine8_and_rmsnorm_unaligned_rows():
         check_bf16(to_np_bits(yr), oracle.bf16_to_f32(oracle.rmsnorm(xr, 1e-6)), f"rmsnorm unaligned H={H}")
 
 
-@pytest.mark.parametrize("T,K,N", [(300, 256, 200), (64, 128, 64), (129, 512, 130), (96, 1088, 200)])
+@pytest.mark.parametrize("T,K,N", [(300, 256, 200), (64, 128, 64), (129, 512, 130), (96, 1088, 200),
+                                   (40, 5120, 256)])
 def test_affine8_gemm_ragged(T, K, N):
-    # from 64 tokens the linear runs as the MFMA GEMM: ragged token and row
+    # from 33 tokens the linear runs as the MFMA GEMM: ragged token and row
     # tiles, K of 2 to 8 groups; 96 x 1088 x 200 (two tiles, 17 groups) splits
-    # K into three ranges of whole 8-group blocks, the last holding one group
+    # K into three ranges of whole 8-group blocks, the last holding one group;
+    # 40 tokens (one tile of 128 rows, 40 real) over 80 groups in ten ranges
     v = synth.resident_weights(14, N, K)
     codes, scales, biases = oracle.q8_quantize(v)
     x = synth.activations(15, T, K)

@@ -811,7 +811,10 @@ static int affine8_gemm_min_t() {
   static int v = -1;
   if (v < 0) {
     const char* s = std::getenv("MOE_AFFINE8_GEMM_MIN_T");
-    v = (s && *s) ? std::atoi(s) : 64;
+    // from 33 tokens: with K split over the chip the GEMM takes 25-27 us at
+    // any T up to 128 (K = N = 5120), the bandwidth-bound pass 25 us at
+    // T = 32 and 37-48 us at 48-63
+    v = (s && *s) ? std::atoi(s) : 33;
     if (v < 1) v = 1;
   }
   return v;
