@@ -687,6 +687,30 @@ def test_layer_call_tiny(tiny_bank):
                              ws if kk <= 8 else None)
 
 
+def test_many_experts_all_paths():
+    # E = 600 (above 512: the one-token selection holds 16 keys per lane;
+    # not a power of two), H = 128, I = 64, k = 4: the one-call layer on one
+    # token against route + forward, and the forward through each path
+    # (few-token kernels, routed GEMV, grouped GEMM) against the oracle
+    H, I, E, k = 128, 64, 600, 4
+    say(f"many experts: E={E}")
+    bank, _ = W.build_bank(5, H, I, E)
+    Wr = synth.router_weights(6, H, E)
+    x1 = synth.activations(61, 1, H)
+    idx1, _, _ = check_layer_call(bank, "E=600 one token", x1, Wr, k)
+    assert np.all((idx1 >= 0) & (idx1 < E))
+    for T, flags in ((4, 0), (40, 0), (300, 0), (300, 2)):
+        x = synth.activations(62 + T, T, H)
+        lg = np.random.default_rng(T).normal(size=(T, E)).astype(np.float32)
+        lg[:, 17] += 2.5  # one expert in most tokens: a long group
+        idx, w = oracle.route_topk(lg, k)
+        recs = host_records(5, np.unique(idx), H, I)
+        ref_f, _ = oracle.moe_forward(recs, E, H, I, x, idx, w)
+        yf, yb = gpu_forward(bank, x, idx, w, k, flags)
+        check_f32(yf, ref_f, f"E={E} T={T} flags={flags}")
+        check_bf16_of(yb, yf, f"E={E} T={T} bf16")
+
+
 def test_layer_call_decode_full_shape(big_bank):
     bank, _ = big_bank
     c = W.CONFIGS["decode"]
