@@ -226,6 +226,29 @@ def test_vq_forward_full_shape(vq_big, T):
     check_bf16_of(yb, yf, f"vq T={T} bf16")
 
 
+def test_vq_forward_odd_k_two_passes_dropped_slot():
+    # k = 3: the gate/up workgroups take slots in twos, the last alone; H and
+    # I one group past a lane's five (81 and 41 groups): a second pass over
+    # each row; a slot with id -1 contributes nothing (the oracle gets a valid
+    # id with routing weight 0 there)
+    H, I, E, k, T = 5184, 2624, 6, 3, 4
+    say(f"vq H={H} I={I} k={k}")
+    bank, base, cb = W.build_vq_bank(37, H, I, E)
+    x = synth.activations(38, T, H)
+    lg = np.random.default_rng(38).normal(size=(T, E)).astype(np.float32)
+    idx, w = oracle.route_topk(lg, k)
+    recs = vq_host_records(37, np.unique(idx), H, I)
+    res = synth.activations(39, T, H)
+    idx_gpu = idx.copy()
+    idx_gpu[1, 2] = -1
+    w_ref = w.copy()
+    w_ref[1, 2] = 0.0
+    yf, yb = gpu_vq_forward(bank, x, idx_gpu, w, k, res)
+    rf, _ = oracle.vq_moe_forward(recs, cb.cpu().numpy(), E, H, I, x, idx, w_ref, residual=res)
+    check_f32(yf, rf, "vq odd k")
+    check_bf16_of(yb, yf, "vq odd k bf16")
+
+
 # ---- pack side: record digests and the manifest --------------------------------------
 def device_digests(bank, e0, n):
     d = torch.empty((n, 32), dtype=torch.uint8, device=DEV)

@@ -86,3 +86,24 @@ def test_affine8_gemm_group_sums_read_all_four_words():
         for dst, srcs in by_dst.items():
             for i in range(0, len(srcs) - 3, 4):
                 assert len(set(srcs[i:i + 4])) == 4, (name, dst, srcs)
+
+
+def test_vq_kernels_index_loads_precede_the_lds_wait():
+    """The VQ gate/up and down kernels copy the codebook and their inputs HBM
+    -> LDS from inline asm, then load their index groups into registers (the
+    same number in every lane), then wait with vmcnt(number of index loads)
+    before the barrier: the wait covers the copies only if every index load
+    of the first pass sits between them and it, and no other vector-memory
+    load shares the counter there."""
+    asm = _device_asm(os.path.join(B.SRC, "vq.hip"))
+    for name, n in (("_ZN3moe16vq_gateup_kernelENS_6VqArgsE", 20), ("_ZN3moe14vq_down_kernelENS_6VqArgsE", 5)):
+        lines = _function(asm, name).splitlines()
+        first_wait = next(i for i, l in enumerate(lines) if re.search(r"s_waitcnt\s+vmcnt", l))
+        assert re.search(rf"vmcnt\({n}\)", lines[first_wait]), (name, lines[first_wait])
+        assert "s_barrier" in "".join(lines[first_wait:first_wait + 4]), name
+        before = lines[:first_wait]
+        loads = [i for i, l in enumerate(before) if "global_load_dwordx3" in l]
+        assert len(loads) == n, (name, len(loads))
+        lds = [i for i, l in enumerate(before) if "global_load_lds" in l]
+        assert lds and max(lds) < min(loads), name
+        assert not any(re.search(r"global_load_(?!lds|dwordx3)|buffer_load|scratch_|flat_load", l) for l in before), name

@@ -48,18 +48,6 @@ __device__ __forceinline__ bf16x2 e4m3x2_bf16(uint32_t word) {
   return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, HI);
 }
 
-// sum over the 8 weights of codeword c (LDS) times 8 inputs (4 packed bf16
-// pairs at xp, LDS)
-__device__ __forceinline__ float cw_dot8(const uint8_t* cb, uint32_t c, const uint32_t* xp, float s) {
-  const u32x2 cw = *reinterpret_cast<const u32x2*>(cb + 8 * c);
-  const u32x4 xv = *reinterpret_cast<const u32x4*>(xp);
-  s = dot2(e4m3x2_bf16<false>(cw.x), xv.x, s);
-  s = dot2(e4m3x2_bf16<true>(cw.x), xv.y, s);
-  s = dot2(e4m3x2_bf16<false>(cw.y), xv.z, s);
-  s = dot2(e4m3x2_bf16<true>(cw.y), xv.w, s);
-  return s;
-}
-
 struct Grp {
   uint32_t w0, w1, w2;
 };
@@ -69,92 +57,146 @@ __device__ __forceinline__ Grp load_grp(const uint8_t* row, int g) {
   return Grp{p[0], p[1], p[2]};
 }
 
-// sum over group g of an input buffer: 8 indices against its inputs 64 g ..
-// 64 g + 63 (xbuf: packed bf16 pairs in LDS in the swizzled chunk layout of
-// gemv_util.h, a group being a quad there; g counted from the buffer's
-// start). The swizzle keeps the 16-byte input reads of a wave's lanes, which
-// take different groups, off each other's banks: 24.4 -> 19.7 us for the
-// one-token gate/up launch, 15.3 -> 12.5 us for down.
-__device__ __forceinline__ float grp_dot(const uint8_t* cb, const Grp& q, const uint32_t* xbuf, int g, float s) {
+// The LDS reads of one group (8 indices): the 8 codewords (cb: the codebook in
+// LDS) and the group's 64 inputs as 8 chunks of 4 packed bf16 pairs (xbuf:
+// LDS, in the swizzled chunk layout of gemv_util.h, a group being a quad
+// there; g counted from the buffer's start). The swizzle keeps the 16-byte
+// input reads of a wave's lanes, which take different groups, off each
+// other's banks: 24.4 -> 19.7 us for the one-token gate/up launch, 15.3 ->
+// 12.5 us for down. The reads of a group are issued together, so a group
+// waits for LDS once, not once per index.
+__device__ __forceinline__ void read_codewords(const uint8_t* cb, const Grp& q, u32x2 (&cw)[8]) {
   uint32_t c[8];
   unpack8(q.w0, q.w1, q.w2, c);
 #pragma unroll
-  for (int i = 0; i < 8; i++) s = cw_dot8(cb, c[i], xbuf + 4 * xchunk(g, i), s);
+  for (int i = 0; i < 8; i++) cw[i] = *reinterpret_cast<const u32x2*>(cb + 8 * c[i]);
+}
+
+__device__ __forceinline__ void read_inputs(const uint32_t* xbuf, int g, u32x4 (&xv)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; i++) xv[i] = *reinterpret_cast<const u32x4*>(xbuf + 4 * xchunk(g, i));
+}
+
+// s plus the sum over one group's 64 weights times its inputs, index by
+// index, each codeword's E4M3 pairs as exact bf16 pairs against v_dot2
+__device__ __forceinline__ float group_dot(const u32x2 (&cw)[8], const u32x4 (&xv)[8], float s) {
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    s = dot2(e4m3x2_bf16<false>(cw[i].x), xv[i].x, s);
+    s = dot2(e4m3x2_bf16<true>(cw[i].x), xv[i].y, s);
+    s = dot2(e4m3x2_bf16<false>(cw[i].y), xv[i].z, s);
+    s = dot2(e4m3x2_bf16<true>(cw[i].y), xv[i].w, s);
+  }
   return s;
 }
 
-// Gate/up + SwiGLU. Workgroup (blockIdx.x, pair p = blockIdx.y): wave w takes
-// rows 16 blockIdx.x + 4 w .. + 3 of gate and up; 16 lanes share a row, lane
-// sub taking the groups sub, sub + 16, ... (all its loads issued before any
-// arithmetic). LDS: codebook | x of the pair's token.
+// Gate/up + SwiGLU. Workgroup (blockIdx.x, blockIdx.y = token t × pair group):
+// rows 16 blockIdx.x .. + 15 of gate and up for kVqGuPairs pairs of token t
+// (slots j0, j0 + 1, ...), which share t's inputs and one staged codebook.
+// Wave w takes 4 of the rows; 16 lanes share a row, lane sub taking the
+// groups sub, sub + 16, ... of each pair's gate and up rows. Every load of a
+// pass is issued first: codebook and inputs HBM -> LDS, then the index groups
+// into registers, group i of every row before group i + 1, each lane the same
+// number (past the row's last group: group 0, not summed; a slot past k or
+// with an invalid id: expert 0's rows, not stored). The wait for the LDS
+// copies counts on those index loads; the
+// groups are then summed in the order their loads return, each group's LDS
+// reads (codewords of both projections, the shared inputs) issued together.
+constexpr int kVqGuPairs = 2;
+
 __global__ __launch_bounds__(kVqThreads) void vq_gateup_kernel(VqArgs a) {
-  constexpr int G = 16, R = 64 / G, QB = 5;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint8_t* cb = lds;
-  uint32_t* xs = reinterpret_cast<uint32_t*>(lds + kVqCodebookBytes);
-  const int H = a.H, I = a.I, ngrp = H / 64;
-  const int p = blockIdx.y, t = p / a.k;
-  const int e = a.idx[p];
-  if (e < 0 || e >= a.E) return;
+  constexpr int G = 16, R = 64 / G, QB = 5, NP = kVqGuPairs;
+  __shared__ __attribute__((aligned(16))) uint8_t cb[kVqCodebookBytes];
+  extern __shared__ __attribute__((aligned(16))) uint32_t xs[];
+  const int H = a.H, I = a.I, k = a.k, ngrp = H / 64;
+  const int npg = (k + NP - 1) / NP;
+  const int t = blockIdx.y / npg, j0 = (blockIdx.y % npg) * NP;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rsub = lane / G, sub = lane % G;
-  dma_copy_lds(a.codebook, cb, kVqCodebookBytes, kVqThreads / 64);
   const int r = (blockIdx.x * (kVqThreads / 64) + wave) * R + rsub;
   const bool row_ok = r < I;
-  const uint8_t* rec = a.bank + (size_t)e * a.stride;
   const size_t row_bytes = (size_t)H * 3 / 16;
-  const uint8_t* rg = rec + a.idx_off[0] + (size_t)(row_ok ? r : 0) * row_bytes;
-  const uint8_t* ru = rec + a.idx_off[1] + (size_t)(row_ok ? r : 0) * row_bytes;
-  Grp qg[QB], qu[QB];
-  float acc_g = 0.0f, acc_u = 0.0f;
-  // x of token t -> LDS, while the first index loads are in flight
-  const u32x4* xsrc = reinterpret_cast<const u32x4*>(a.x + (size_t)t * H);
+  const uint8_t* rows[NP][2];
+  int ev[NP];
+  bool pv[NP];
+#pragma unroll
+  for (int q = 0; q < NP; q++) {
+    const int e = j0 + q < k ? a.idx[t * k + j0 + q] : -1;
+    ev[q] = e;
+    pv[q] = e >= 0 && e < a.E;
+    const uint8_t* rec = a.bank + (size_t)(pv[q] ? e : 0) * a.stride;
+    rows[q][0] = rec + a.idx_off[0] + (size_t)(row_ok ? r : 0) * row_bytes;
+    rows[q][1] = rec + a.idx_off[1] + (size_t)(row_ok ? r : 0) * row_bytes;
+  }
+  dma_copy_lds(a.codebook, cb, kVqCodebookBytes, kVqThreads / 64);
+  dma_copy_lds_swz(a.x + (size_t)t * H, xs, (uint32_t)(H * 2), kVqThreads / 64);
+  float acc[NP][2] = {};
+  Grp qv[QB][NP][2];
   for (int qb = 0; qb < ngrp; qb += G * QB) {
 #pragma unroll
     for (int i = 0; i < QB; i++) {
       const int g = qb + sub + G * i;
-      if (row_ok && g < ngrp) {
-        qg[i] = load_grp(rg, g);
-        qu[i] = load_grp(ru, g);
+      const int gl = row_ok && g < ngrp ? g : 0;
+#pragma unroll
+      for (int q = 0; q < NP; q++) {
+        qv[i][q][0] = load_grp(rows[q][0], gl);
+        qv[i][q][1] = load_grp(rows[q][1], gl);
       }
     }
     if (qb == 0) {
-      for (int i = threadIdx.x; i < H / 8; i += kVqThreads) reinterpret_cast<u32x4*>(xs)[xchunk(i >> 3, i & 7)] = xsrc[i];
-      wait_vmcnt<0>();
-      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<QB * NP * 2>();
+      step_barrier();
     }
 #pragma unroll
     for (int i = 0; i < QB; i++) {
       const int g = qb + sub + G * i;
-      if (row_ok && g < ngrp) {
-        acc_g = grp_dot(cb, qg[i], xs, g, acc_g);
-        acc_u = grp_dot(cb, qu[i], xs, g, acc_u);
+      const bool ok = row_ok && g < ngrp;
+      u32x4 xv[8];
+      read_inputs(xs, ok ? g : 0, xv);
+#pragma unroll
+      for (int q = 0; q < NP; q++) {
+        u32x2 cg[8], cu[8];
+        read_codewords(cb, qv[i][q][0], cg);
+        read_codewords(cb, qv[i][q][1], cu);
+        if (ok) {
+          acc[q][0] = group_dot(cg, xv, acc[q][0]);
+          acc[q][1] = group_dot(cu, xv, acc[q][1]);
+        }
       }
     }
   }
-  const float sg = group_sum_last<G>(acc_g), su = group_sum_last<G>(acc_u);
-  if (sub == G - 1 && row_ok) {
-    const uint16_t* gains_g = reinterpret_cast<const uint16_t*>(rec + a.gain_off[0]);
-    const uint16_t* gains_u = reinterpret_cast<const uint16_t*>(rec + a.gain_off[1]);
-    const float gv = sg * f16_to_f32(gains_g[r]);
-    const float uv = su * f16_to_f32(gains_u[r]);
-    a.mid[(size_t)p * I + r] = f32_to_bf16(silu_mul(gv, uv));
+#pragma unroll
+  for (int q = 0; q < NP; q++) {
+    const float sg = group_sum_last<G>(acc[q][0]), su = group_sum_last<G>(acc[q][1]);
+    if (sub == G - 1 && row_ok && pv[q]) {
+      const uint8_t* rec = a.bank + (size_t)ev[q] * a.stride;
+      const uint16_t* gains_g = reinterpret_cast<const uint16_t*>(rec + a.gain_off[0]);
+      const uint16_t* gains_u = reinterpret_cast<const uint16_t*>(rec + a.gain_off[1]);
+      const float gv = sg * f16_to_f32(gains_g[r]);
+      const float uv = su * f16_to_f32(gains_u[r]);
+      a.mid[(size_t)(t * k + j0 + q) * I + r] = f32_to_bf16(silu_mul(gv, uv));
+    }
   }
 }
 
 // Down + weighted combine. Workgroup (8 output rows from 8 blockIdx.x, token
 // t = blockIdx.y), one wave per pair j < k; 8 lanes share a row. LDS:
-// codebook | the token's k rows of mids. The k routing-weighted row sums meet
-// in LDS and are added in slot order onto the residual.
+// codebook | the token's k rows of mids, copied HBM -> LDS; each lane's index
+// groups are loaded after those copies (the same number in every lane, a
+// lane past the last row or of an unused slot loading row 0 of expert 0), so
+// the wait for the copies counts on them. The k routing-weighted row sums
+// meet in LDS and are added in slot order onto the residual.
 __global__ __launch_bounds__(64 * kFlatDecodeMaxK) void vq_down_kernel(VqArgs a) {
   constexpr int G = 8, R = 64 / G, QB = 5;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ __attribute__((aligned(16))) uint8_t cb[kVqCodebookBytes];
   __shared__ float s_d[kFlatDecodeMaxK][R];
-  uint8_t* cb = lds;
-  uint32_t* ms = reinterpret_cast<uint32_t*>(lds + kVqCodebookBytes);
+  extern __shared__ __attribute__((aligned(16))) uint32_t ms[];
   const int H = a.H, I = a.I, k = a.k, ngrp = I / 64;
   const int t = blockIdx.y;
-  const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
+  // the wave's slot, uniform: its expert id is a scalar load, which the
+  // copies below need not wait for
+  const int lane = threadIdx.x & 63, j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rsub = lane / G, sub = lane % G;
   const int r = blockIdx.x * R + rsub;
   const bool row_ok = r < H;
@@ -166,32 +208,29 @@ __global__ __launch_bounds__(64 * kFlatDecodeMaxK) void vq_down_kernel(VqArgs a)
   const uint8_t* rd = rec + a.idx_off[2] + (size_t)(row_ok ? r : 0) * row_bytes;
   dma_copy_lds(a.codebook, cb, kVqCodebookBytes, k);
   dma_copy_lds_swz(a.mid + (size_t)t * k * I, ms, (uint32_t)(k * I * 2), k);
+  float acc = 0.0f;
+  const int g0 = j * ngrp;  // the pair's mids start at this group of the buffer
   Grp q[QB];
-  if (valid) {
+  for (int qb = 0; qb < ngrp; qb += G * QB) {
 #pragma unroll
     for (int i = 0; i < QB; i++) {
-      const int g = sub + G * i;
-      if (row_ok && g < ngrp) q[i] = load_grp(rd, g);
+      const int g = qb + sub + G * i;
+      q[i] = load_grp(rd, row_ok && g < ngrp ? g : 0);
     }
-  }
-  wait_vmcnt<0>();
-  __syncthreads();
-  float acc = 0.0f;
-  if (valid) {
-    const int g0 = j * ngrp;  // the pair's mids start at this group of the buffer
-    for (int qb = 0; qb < ngrp; qb += G * QB) {
-      if (qb > 0) {
+    if (qb == 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<QB>();
+      step_barrier();
+    }
 #pragma unroll
-        for (int i = 0; i < QB; i++) {
-          const int g = qb + sub + G * i;
-          if (row_ok && g < ngrp) q[i] = load_grp(rd, g);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < QB; i++) {
-        const int g = qb + sub + G * i;
-        if (row_ok && g < ngrp) acc = grp_dot(cb, q[i], ms, g0 + g, acc);
-      }
+    for (int i = 0; i < QB; i++) {
+      const int g = qb + sub + G * i;
+      const bool ok = valid && row_ok && g < ngrp;
+      u32x2 cw[8];
+      u32x4 mv[8];
+      read_codewords(cb, q[i], cw);
+      read_inputs(ms, g0 + (ok ? g : 0), mv);
+      if (ok) acc = group_dot(cw, mv, acc);
     }
   }
   const float d = group_sum_last<G>(acc);
@@ -246,12 +285,12 @@ __global__ __launch_bounds__(256) void vq_dequant_kernel(VqArgs a, int expert, i
 hipError_t launch_vq_forward(const VqArgs& a, hipStream_t s) {
   const int P = a.T * a.k;
   if (P == 0) return hipSuccess;
-  launch_kernel("vq_gateup", vq_gateup_kernel, dim3((a.I + 15) / 16, P), dim3(kVqThreads),
-                (uint32_t)(kVqCodebookBytes + a.H * 2), s, a);
+  launch_kernel("vq_gateup", vq_gateup_kernel, dim3((a.I + 15) / 16, a.T * ((a.k + kVqGuPairs - 1) / kVqGuPairs)),
+                dim3(kVqThreads), (uint32_t)(a.H * 2), s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  launch_kernel("vq_down", vq_down_kernel, dim3((a.H + 7) / 8, a.T), dim3(64 * a.k),
-                (uint32_t)(kVqCodebookBytes + a.k * a.I * 2), s, a);
+  launch_kernel("vq_down", vq_down_kernel, dim3((a.H + 7) / 8, a.T), dim3(64 * a.k), (uint32_t)(a.k * a.I * 2), s,
+                a);
   return hipGetLastError();
 }
 
