@@ -247,3 +247,42 @@ def test_status_word_calls_validate():
     assert L.moe_status_clear(None, None) == wq.MOE_EINVAL
     assert L.moe_status_clear(C.c_void_p((1 << 26) + 8), None) == wq.MOE_EALIGN
     assert wq.MOE_STATUS_OFFSET == 8 and (wq.MOE_STATUS_ROUTE_TIMEOUT, wq.MOE_STATUS_BAD_IDX) == (1, 2)
+
+
+def test_binding_rejects_short_buffers_before_the_call():
+    """The binding checks every tensor against the bytes the call's sizes
+    imply (the library takes plain pointers and would access past a short
+    buffer's end). Host tensors serve: the check raises before any library
+    call."""
+    import torch
+
+    b = wq.moe_nvfp4_bank()
+    b.H, b.I, b.E = 128, 64, 16
+    T, k, H = 8, 4, 128
+
+    def t(n, dtype=torch.int16):
+        return torch.empty(n, dtype=dtype)
+
+    ok = dict(x=t(T * H), idx=t(T * k, torch.int32), w=t(T * k, torch.float32), y=t(T * H))
+    cases = [("x", t(T * H - 1)), ("idx", t(T * k - 1, torch.int32)), ("w", t(T * k - 1, torch.float32)),
+             ("y", t(T * H - 1))]
+    for name, short in cases:
+        a = dict(ok, **{name: short})
+        with pytest.raises(wq.MoeError) as e:
+            wq.moe_nvfp4_forward(b, a["x"], T, a["idx"], a["w"], k, None, a["y"], 0, t(256, torch.uint8))
+        assert e.value.code == wq.MOE_ESHAPE and name in str(e.value), (name, e.value)
+    # an f32 output needs 4 bytes per value; a residual as many bytes as x
+    with pytest.raises(wq.MoeError, match="y"):
+        wq.moe_nvfp4_forward(b, ok["x"], T, ok["idx"], ok["w"], k, None, t(T * H), wq.MOE_F32_OUT, t(256, torch.uint8))
+    with pytest.raises(wq.MoeError, match="residual"):
+        wq.moe_nvfp4_forward(b, ok["x"], T, ok["idx"], ok["w"], k, t(T * H // 2), ok["y"], 0, t(256, torch.uint8))
+    # the one-call layer also checks the router weights and the logits
+    with pytest.raises(wq.MoeError, match="w_router"):
+        wq.moe_nvfp4_layer(b, ok["x"], t(b.E * H - 1, torch.float32), T, k, None, t(T * b.E, torch.float32),
+                           ok["idx"], ok["w"], ok["y"], 0, t(256, torch.uint8))
+    with pytest.raises(wq.MoeError, match="logits"):
+        wq.moe_route_topk(None, None, t(T * b.E - 1, torch.float32), T, H, b.E, k, ok["idx"], ok["w"])
+    with pytest.raises(wq.MoeError, match="codes"):
+        wq.affine8_g64_linear(t(T * H), t(H * H - 1, torch.uint8), t(H * 2), t(H * 2), T, H, H, t(T * H))
+    with pytest.raises(wq.MoeError, match="y"):
+        wq.moe_rmsnorm(t(T * H), T, H, 1e-6, t(T * H - 8))

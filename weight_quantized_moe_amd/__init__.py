@@ -149,6 +149,30 @@ def _ptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
 
 
+def _need(what, t, nbytes):
+    """Raises MOE_ESHAPE when the tensor t (if given) spans fewer than nbytes:
+    the library takes plain pointers and reads or writes exactly the bytes
+    its sizes imply, so a short buffer would be accessed past its end."""
+    if t is None or nbytes <= 0:
+        return
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise MoeError(MOE_ESHAPE, f"{what}: {have} bytes, the call needs {int(nbytes)}")
+
+
+def _need_tokens(T, H, E, k, flags=0, x=None, residual=None, y=None, idx=None, w=None, logits=None,
+                 w_router=None):
+    if T <= 0:
+        return
+    _need("x", x, T * H * 2)
+    _need("residual", residual, T * H * 2)
+    _need("y", y, T * H * (4 if flags & MOE_F32_OUT else 2))
+    _need("idx", idx, T * k * 4)
+    _need("w", w, T * k * 4)
+    _need("logits", logits, T * E * 4)
+    _need("w_router", w_router, E * H * 4)
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -195,11 +219,16 @@ def moe_pack_nvfp4_bank(bank, codes, scales, g, stream=None):
 
 # ---- routing ------------------------------------------------------------------------
 def moe_route_topk(x, w_router, logits, T, H, E, k, idx, w, stream=None):
+    _need_tokens(T, H, E, k, x=x, w_router=None if x is None else w_router, logits=logits, idx=idx, w=w)
     _check(lib().moe_route_topk(_ptr(x), _ptr(w_router), _ptr(logits), T, H, E, k, _ptr(idx), _ptr(w),
                                 _stream(stream)))
 
 
 def moe_sort_pairs(idx, T, k, E, offsets, sorted_, stream=None):
+    if T > 0:
+        _need("idx", idx, T * k * 4)
+        _need("sorted", sorted_, T * k * 4)
+        _need("offsets", offsets, (E + 1) * 4)
     _check(lib().moe_sort_pairs(_ptr(idx), T, k, E, _ptr(offsets), _ptr(sorted_), _stream(stream)))
 
 
@@ -208,6 +237,10 @@ def moe_sort_workspace_bytes(T, k, E):
 
 
 def moe_sort_pairs_ws(idx, T, k, E, offsets, sorted_, workspace, stream=None):
+    if T > 0:
+        _need("idx", idx, T * k * 4)
+        _need("sorted", sorted_, T * k * 4)
+        _need("offsets", offsets, (E + 1) * 4)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().moe_sort_pairs_ws(_ptr(idx), T, k, E, _ptr(offsets), _ptr(sorted_), _ptr(workspace), ws_bytes,
                                    _stream(stream)))
@@ -219,32 +252,47 @@ def moe_nvfp4_workspace_bytes(T, k, H, I, E):
 
 
 def moe_nvfp4_forward(bank, x, T, idx, w, k, residual, y, flags, workspace, stream=None):
+    _need_tokens(T, bank.H, bank.E, k, flags, x=x, residual=residual, y=y, idx=idx, w=w)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().moe_nvfp4_forward(C.byref(bank), _ptr(x), T, _ptr(idx), _ptr(w), k, _ptr(residual), _ptr(y),
                                    flags, _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def moe_nvfp4_forward_noalloc(bank, x, T, idx, w, k, residual, y, flags, status=None, stream=None):
+    _need_tokens(T, bank.H, bank.E, k, flags, x=x, residual=residual, y=y, idx=idx, w=w)
     _check(lib().moe_nvfp4_forward_noalloc(C.byref(bank), _ptr(x), T, _ptr(idx), _ptr(w), k, _ptr(residual), _ptr(y),
                                            flags, _ptr(status), _stream(stream)))
 
 
 def moe_nvfp4_layer(bank, x, w_router, T, k, residual, logits, idx, w, y, flags, workspace, stream=None):
+    _need_tokens(T, bank.H, bank.E, k, flags, x=x, residual=residual, y=y, idx=idx, w=w, logits=logits,
+                 w_router=w_router)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().moe_nvfp4_layer(C.byref(bank), _ptr(x), _ptr(w_router), T, k, _ptr(residual), _ptr(logits),
                                  _ptr(idx), _ptr(w), _ptr(y), flags, _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def affine8_g64_linear(x, codes, scales, biases, T, K, N, y, stream=None):
+    if T > 0 and K > 0 and N > 0:
+        _need("x", x, T * K * 2)
+        _need("codes", codes, N * K)
+        _need("scales", scales, N * (K // 64) * 2)
+        _need("biases", biases, N * (K // 64) * 2)
+        _need("y", y, T * N * 2)
     _check(lib().affine8_g64_linear(_ptr(x), _ptr(codes), _ptr(scales), _ptr(biases), T, K, N, _ptr(y),
                                     _stream(stream)))
 
 
 def moe_rmsnorm(x, T, H, eps, y, stream=None):
+    if T > 0 and H > 0:
+        _need("x", x, T * H * 2)
+        _need("y", y, T * H * 2)
     _check(lib().moe_rmsnorm(_ptr(x), T, H, float(eps), _ptr(y), _stream(stream)))
 
 
 def moe_nvfp4_dequant(bank, expert, proj, out_f32, out_unit, stream=None):
+    _need("out_f32", out_f32, bank.H * bank.I * 4)
+    _need("out_unit", out_unit, bank.H * bank.I * 2)
     _check(lib().moe_nvfp4_dequant(C.byref(bank), expert, proj, _ptr(out_f32), _ptr(out_unit), _stream(stream)))
 
 
@@ -261,6 +309,7 @@ def moe_nvfp4_global_from_ws2(ws2):
 
 def moe_nvfp4_record_sha256(bank, e0, n, digests, stream=None):
     """digests: device uint8 [n][32]."""
+    _need("digests", digests, n * 32)
     _check(lib().moe_nvfp4_record_sha256(C.byref(bank), e0, n, _ptr(digests), _stream(stream)))
 
 
@@ -333,6 +382,7 @@ def moe_vq_pack_bank(bank, idx, gains, stream=None):
 
 
 def moe_vq_dequant(bank, expert, proj, out_f32, stream=None):
+    _need("out_f32", out_f32, bank.H * bank.I * 4)
     _check(lib().moe_vq_dequant(C.byref(bank), expert, proj, _ptr(out_f32), _stream(stream)))
 
 
@@ -341,6 +391,7 @@ def moe_vq_workspace_bytes(T, k, H, I):
 
 
 def moe_vq_forward(bank, x, T, idx, w, k, residual, y, flags, ws, stream=None):
+    _need_tokens(T, bank.H, bank.E, k, flags, x=x, residual=residual, y=y, idx=idx, w=w)
     _check(lib().moe_vq_forward(C.byref(bank), _ptr(x), T, _ptr(idx), _ptr(w), k, _ptr(residual), _ptr(y), flags,
                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 

@@ -133,8 +133,13 @@ __global__ __launch_bounds__(kDecThreads) void gemv_kernel(DecodeArgs a) {
   while (np < a.passes && r0 + (np * kDecWaves + wave) * R < r1) np++;
   const int nsteps = np * nqb;
 
-  Quad v[NPROJ][kQB];
-  auto load_step = [&](int st) {
+  // One-quad steps over token chunks (gate/up's default) request the next
+  // step's weights before this step's arithmetic, into a second register
+  // set; wider steps already have all their quads in flight, and in the
+  // one-token form the set would cost occupancy.
+  constexpr bool kAhead = kQB == 1 && MT > 1;
+  Quad v[NPROJ][kQB], vn[kAhead ? NPROJ : 1][kQB];
+  auto load_step = [&](int st, Quad (&dst)[NPROJ][kQB]) {
     const int p = st / nqb, qb = (st % nqb) * G * kQB;
     const int r = r0 + (p * kDecWaves + wave) * R + rsub;
     if (r < r1) {
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(kDecThreads) void gemv_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < kQB; i++) {
           const int qd = qb + sub + G * i;
-          if (qd < nquads) v[q][i] = load_quad(rc, rs, qd);
+          if (qd < nquads) dst[q][i] = load_quad(rc, rs, qd);
         }
       }
     }
@@ -156,14 +161,15 @@ __global__ __launch_bounds__(kDecThreads) void gemv_kernel(DecodeArgs a) {
 
   // The chunk's input rows go HBM -> LDS with no registers (one wave-wide
   // load per 1 KiB of a row). With one load step per wave (every row's quads
-  // in one batch: down by default; gate/up loads one quad per step and so
-  // re-reads its rows, from the L2, for every chunk) the weights are loaded
-  // once, before the first chunk's rows, and stay in registers for every
-  // chunk: the rows and
-  // the weights are in flight together and one wait covers both. Loads
+  // in one batch: down by default) the weights are loaded once, before the
+  // first chunk's rows, and stay in registers for every chunk. Gate/up loads
+  // one quad per step and so re-reads its rows, from the L2, for every chunk:
+  // its first step's weights are requested with the chunk's rows, and each
+  // later step's while the step before is summed. Either way the rows and
+  // the first weights are in flight together and one wait covers both. Loads
   // complete in issue order, so nothing waited for between the weights and
-  // the rows may be a load: the first chunk's row numbers are read before
-  // the weights, and the barriers wait for LDS only (step_barrier).
+  // the rows may be a load: the chunk's row numbers are read before the
+  // weights, and the barriers wait for LDS only (step_barrier).
   const int per_row = K / 8, ipr = (per_row + 63) / 64;  // 16-byte pieces and wave loads per row
   int prow[MT];  // input rows of the chunk (wave-uniform)
   auto chunk_rows = [&](int m0, int mt) {
@@ -174,11 +180,14 @@ __global__ __launch_bounds__(kDecThreads) void gemv_kernel(DecodeArgs a) {
     }
   };
   chunk_rows(0, min(MT, M));
-  if (nsteps == 1) load_step(0);
+  if (nsteps == 1) load_step(0, v);
   for (int m0 = 0; m0 < M; m0 += MT) {
     const int mt = min(MT, M - m0);
     step_barrier();  // the previous chunk's rows are read
     if (m0 > 0) chunk_rows(m0, mt);
+    if constexpr (kAhead) {
+      if (nsteps > 1) load_step(0, v);  // in flight together with the chunk's rows
+    }
     for (int jj = wave; jj < mt * ipr; jj += kDecWaves) {
       const int m = jj / ipr, blk = jj - m * ipr, pin = 64 * blk + lane;
       int row = prow[0];
@@ -205,7 +214,11 @@ __global__ __launch_bounds__(kDecThreads) void gemv_kernel(DecodeArgs a) {
 #pragma unroll
       for (int m = 0; m < MT; m++) acc[q][m] = 0.0f;
     for (int st = 0; st < nsteps; st++) {
-      if (nsteps > 1) load_step(st);
+      if constexpr (kAhead) {
+        if (st + 1 < nsteps) load_step(st + 1, vn);
+      } else {
+        if (nsteps > 1) load_step(st, v);
+      }
       const int p = st / nqb, qb = (st % nqb) * G * kQB;
       const int r = r0 + (p * kDecWaves + wave) * R + rsub;
       const bool row_ok = r < r1;
@@ -249,6 +262,14 @@ __global__ __launch_bounds__(kDecThreads) void gemv_kernel(DecodeArgs a) {
           for (int q = 0; q < NPROJ; q++) acc[q][m] = 0.0f;
         }
       }
+      if constexpr (kAhead) {
+        if (nsteps > 1) {  // one step: its weights stay in v for every chunk
+#pragma unroll
+          for (int q = 0; q < NPROJ; q++)
+#pragma unroll
+            for (int i = 0; i < kQB; i++) v[q][i] = vn[q][i];
+        }
+      }
     }
   }
 }
@@ -270,7 +291,10 @@ static void launch_gemv_g(const DecodeArgs& b, dim3 grid, size_t lds, bool one, 
 // Tuning knobs (environment, read at each launch): MOE_GEMV_QB_{GATEUP,DOWN}
 // quads per lane per load step (1, 2 or 5; defaults 1 and 5: gate/up with one
 // quad per step measured 5-9 % faster from 24 to 127 tokens, e.g. 1,350
-// against 1,480 us at 64); MOE_GEMV_PASSES_{GATEUP,DOWN} wave passes per block.
+// against 1,480 us at 64); MOE_GEMV_PASSES_{GATEUP,DOWN} wave passes per block
+// (defaults 2 and 1: two passes of gate/up rows per block, each step's weights
+// requested one step ahead, 734 -> 673 us at T = 32 and 1,144 -> 1,055 us at
+// T = 64 against one pass loading each step where it is summed).
 template <int NPROJ>
 static hipError_t launch_gemv(const DecodeArgs& a, int slots, int max_m, hipStream_t s) {
   const int K = (NPROJ == 2) ? a.H : a.I;
@@ -280,7 +304,7 @@ static hipError_t launch_gemv(const DecodeArgs& a, int slots, int max_m, hipStre
   const int R = 64 / G;
   const int qb = NPROJ == 2 ? env_int("MOE_GEMV_QB_GATEUP", 1) : env_int("MOE_GEMV_QB_DOWN", 5);
   DecodeArgs b = a;
-  b.passes = env_int(NPROJ == 2 ? "MOE_GEMV_PASSES_GATEUP" : "MOE_GEMV_PASSES_DOWN", 1);
+  b.passes = NPROJ == 2 ? env_int("MOE_GEMV_PASSES_GATEUP", 2) : env_int("MOE_GEMV_PASSES_DOWN", 1);
   if (b.passes < 1) b.passes = 1;
   const int rows_per_block = b.passes * kDecWaves * R;
   dim3 grid((N + rows_per_block - 1) / rows_per_block, slots);
