@@ -171,13 +171,19 @@ __global__ __launch_bounds__(kDecThreads) void gemv_kernel(DecodeArgs a) {
   // the rows may be a load: the chunk's row numbers are read before the
   // weights, and the barriers wait for LDS only (step_barrier).
   const int per_row = K / 8, ipr = (per_row + 63) / 64;  // 16-byte pieces and wave loads per row
-  int prow[MT];  // input rows of the chunk (wave-uniform)
+  // the chunk's pair ids, their input rows and (down) routing weights, all
+  // wave-uniform; read once per chunk, ahead of its weights and rows, so the
+  // arithmetic waits on none of them
+  int pid[MT], prow[MT];
+  float wt[MT];
   auto chunk_rows = [&](int m0, int mt) {
 #pragma unroll
     for (int m = 0; m < MT; m++) {
-      const int p = pairs[m0 + min(m, mt - 1)];
-      prow[m] = __builtin_amdgcn_readfirstlane((NPROJ == 2) ? p / a.k : p);
+      pid[m] = __builtin_amdgcn_readfirstlane(pairs[m0 + min(m, mt - 1)]);
+      prow[m] = (NPROJ == 2) ? pid[m] / a.k : pid[m];
     }
+#pragma unroll
+    for (int m = 0; m < MT; m++) wt[m] = (NPROJ == 1 && m < mt) ? a.w[pid[m]] : 0.0f;
   };
   chunk_rows(0, min(MT, M));
   if (nsteps == 1) load_step(0, v);
@@ -201,13 +207,6 @@ __global__ __launch_bounds__(kDecThreads) void gemv_kernel(DecodeArgs a) {
     }
     wait_vmcnt<0>();
     step_barrier();
-    float wt[MT];
-    int pr[MT];
-#pragma unroll
-    for (int m = 0; m < MT; m++) {
-      pr[m] = (m < mt) ? pairs[m0 + m] : 0;
-      wt[m] = (NPROJ == 1 && m < mt) ? a.w[pr[m]] : 0.0f;
-    }
     float acc[NPROJ][MT];
 #pragma unroll
     for (int q = 0; q < NPROJ; q++)
@@ -253,9 +252,9 @@ __global__ __launch_bounds__(kDecThreads) void gemv_kernel(DecodeArgs a) {
             for (int q = 0; q < NPROJ; q++) sm[q] = group_sum<G>(acc[q][m]);
             if (sub == 0 && row_ok) {
               if (NPROJ == 2)
-                a.mid[(size_t)pr[m] * N + r] = f32_to_bf16(silu_mul(sm[0], sm[NPROJ - 1]));
+                a.mid[(size_t)pid[m] * N + r] = f32_to_bf16(silu_mul(sm[0], sm[NPROJ - 1]));
               else
-                a.part[(size_t)pr[m] * N + r] = wt[m] * sm[0];
+                a.part[(size_t)pid[m] * N + r] = wt[m] * sm[0];
             }
           }
 #pragma unroll
