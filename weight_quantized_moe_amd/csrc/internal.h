@@ -101,12 +101,12 @@ hipError_t launch_decode_down(const BankView& b, const uint16_t* mid, const floa
 // mids in LDS, I % 16 == 0): gate/up then down with the combine folded in;
 // mid [T*k][I] is scratch, y [T][H] the layer output
 constexpr int kFlatDecodeMaxK = 16;
-// tokens the one-item-per-wave decode kernels take: they stream every pair's
-// record at about 6 TB/s, the routed GEMV reads each distinct record once
-// but more slowly; on skewed routing the two cross between 12 and 16 tokens
-// (392 against 402 us at 12, 477-490 against 470 us at 16, 574-584 against
-// 557 us at 20)
-constexpr int kFlatDecodeMaxT = 14;
+// tokens the one-item-per-wave decode kernels take by default: they stream
+// every pair's record at about 6 TB/s, the routed GEMV reads each distinct
+// record once; on skewed routing the two cross between 8 and 10 tokens
+// (226-228 against 226-253 us at 8, 278 against 271 us at 10, 328 against
+// 311 us at 12, 381 against 351 us at 14)
+constexpr int kFlatDecodeMaxT = 9;
 hipError_t launch_flat_decode(const BankView& b, const uint16_t* x, int T, const int32_t* idx,
                               const float* w, int k, const uint16_t* residual, uint16_t* mid,
                               void* y, bool f32_out, uint32_t* status, hipStream_t s);
