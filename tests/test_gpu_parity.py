@@ -962,6 +962,22 @@ def test_layer_route_giveup_contract(tiny_bank, monkeypatch):
     check_layer_call(bank, "tiny after a give-up", x1, Wr, 2, residual=res, ws=ws)
 
 
+def test_layer_call_token_counts():
+    # the one-call layer for 2..16 tokens (few-token kernels up to 9, the
+    # routed GEMV above; 16 keys per lane in the top-k at E = 600), one
+    # workspace over calls of several T, each call against route + forward
+    H, I = 128, 64
+    for E, k, Ts in ((256, 8, (2, 5, 9, 16)), (600, 4, (3, 16))):
+        say(f"layer call: E={E}, T in {Ts}")
+        bank, _ = W.build_bank(7, H, I, E)
+        Wr = synth.router_weights(8, H, E)
+        ws = wq.workspace(wq.moe_nvfp4_workspace_bytes(16, k, H, I, E))
+        for T in Ts:
+            x = synth.activations(90 + T, T, H)
+            res = synth.activations(190 + T, T, H) if T % 2 else None
+            check_layer_call(bank, f"layer call E={E} T={T}", x, Wr, k, residual=res, ws=ws)
+
+
 def test_forward_deterministic(big_bank):
     bank, _ = big_bank
     c = W.CONFIGS["batched"]
